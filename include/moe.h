@@ -1,0 +1,215 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) decode-step mixture-of-experts FFN.
+ *
+ * The layer (colibri pull request 1992, "What it is": router logits, the
+ * routing, the routed experts plus the shared expert and its gate, the MoE
+ * output joining the residual; GB10 blueprint for Qwen3.6-35B-A3B-FP8,
+ * "Kernels" table: dense_gemv_bf16 router, moe_topk_softmax,
+ * moe_expert_gate_up_shared_fp8, moe_expert_silu_down_shared_fp8,
+ * moe_weighted_sum_blend) computes, for each activation row r:
+ *
+ *   logits[r,e] = x[r,:] . Wr[e,:] (+ bias[e])            bf16 x bf16 -> f32
+ *   p = softmax over all E; ids = the k largest (ties: lower index first),
+ *       in descending order; w_j = p[id_j] / sum_j p[id_j]          f32, i32
+ *   s[r] = sigmoid(x[r,:] . w_sg)                      shared-expert gate
+ *   for each routed slot j and the shared expert:
+ *       [g ; u] = W_gu x    (gate rows 0..I-1, then up rows I..2I-1)
+ *       h = silu(g) * u     (f32)
+ *       d = W_dn h
+ *   y = sum_j w_j d_j + s d_shared
+ *   out = bf16_rne(residual + y), or bf16_rne(y) without a residual.
+ *
+ * Conventions
+ *  - Every pointer argument marked "device" is a device address on the ctx's
+ *    GPU; "host" pointers are read during the call only.  The caller owns
+ *    every buffer.  The library allocates no device memory during a call: it
+ *    uses the caller's workspace and a few KB of synchronisation words the ctx
+ *    allocates at creation.
+ *  - Calls are asynchronous: success (MOE_OK) means the work is enqueued on
+ *    `stream` (an opaque hipStream_t; NULL = the device's null stream).  No
+ *    call synchronises with the host.
+ *  - Every argument is validated before anything is enqueued: a call that
+ *    returns an error other than MOE_ERR_HIP / MOE_ERR_DEVICE_LOST has
+ *    enqueued nothing and written nothing.
+ *  - 0 is success and errors are negative (HIP style).  A HIP launch error
+ *    marks the ctx lost (sticky, as a CUDA error marks the device lost in the
+ *    colibri chain, "What it is"); every later call on it returns
+ *    MOE_ERR_DEVICE_LOST without launching until the ctx is destroyed.
+ *  - One ctx may be used from one thread, with its calls stream-ordered: the
+ *    ctx's synchronisation words are shared by its launches.  Distinct ctxs
+ *    are independent.  No exception crosses the ABI.
+ *
+ * Shape limits (MOE_ERR_UNSUPPORTED_SHAPE otherwise): hidden and every
+ * intermediate size a multiple of 128, hidden <= 8192, inter <= 4096;
+ * 1 <= top_k <= 16, top_k <= n_experts <= 1024; 0 <= rows <= 1024; grouping
+ * for rows >= 2 also needs n_experts * ceil(rows/32) <= 8192.
+ * Alignment (MOE_ERR_MISALIGNED otherwise): weight codes (and their byte
+ * strides), the router matrix, the gate vector and x 16-byte aligned, ldx a
+ * multiple of 8 elements; fp8 scales 4-byte and nvfp4 scales 2-byte aligned;
+ * routing arrays and logits 4-byte, outputs 2-byte aligned.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_API __attribute__((visibility("default")))
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,       /* NULL where required, negative size, bad enum */
+    MOE_ERR_UNSUPPORTED_SHAPE = -2, /* outside the shape limits above */
+    MOE_ERR_MISALIGNED = -3,        /* pointer or leading dimension misaligned */
+    MOE_ERR_WORKSPACE_TOO_SMALL = -4,
+    MOE_ERR_HIP = -5,               /* a HIP call failed; the ctx is now lost */
+    MOE_ERR_DEVICE_LOST = -6,       /* sticky: an earlier HIP error or injected fault */
+};
+
+enum moe_weight_format {
+    /* OCP e4m3 codes, row-major [out][in], one f32 scale per 128x128 block,
+     * scale array [out/128][in/128]; w = code * scale (GB10 blueprint,
+     * "Precision": fp8/block128x128). */
+    MOE_WFMT_FP8_E4M3_B128 = 0,
+    /* e2m1 codes two per byte (even column in the low nibble), row-major
+     * [out][in/2] bytes; one e4m3 scale byte per 16 consecutive input columns,
+     * array [out][in/16]; one f32 global scale per matrix; w = code * scale *
+     * global ("Inspecting Qwen3.5-397B-A17B-NVFP4", "The Architectural
+     * Revelations": NVFP4 weights). */
+    MOE_WFMT_NVFP4 = 1,
+};
+
+typedef struct moe_ctx moe_ctx;
+
+/* One family of experts (the routed ones, or the single shared expert) stored
+ * as per-expert slabs at a fixed byte stride.  Device pointers. */
+typedef struct moe_expert_weights {
+    const void *gate_up;        /* [2I][H] codes (fp8: 1 B each; nvfp4: H/2 B per row) */
+    const void *gate_up_scale;  /* fp8: f32 [2I/128][H/128]; nvfp4: e4m3 [2I][H/16] */
+    const float *gate_up_global;/* nvfp4: f32 per expert (stride 1 float); fp8: NULL */
+    const void *down;           /* [H][I] codes (fp8) or [H][I/2] bytes (nvfp4) */
+    const void *down_scale;     /* fp8: f32 [H/128][I/128]; nvfp4: e4m3 [H][I/16] */
+    const float *down_global;   /* nvfp4: f32 per expert; fp8: NULL */
+    int64_t gate_up_stride;     /* bytes from one expert's gate_up to the next */
+    int64_t gate_up_scale_stride;
+    int64_t down_stride;
+    int64_t down_scale_stride;
+} moe_expert_weights;
+
+typedef struct moe_layer_weights {
+    size_t struct_size;         /* sizeof(moe_layer_weights), for versioning */
+    int hidden;                 /* H */
+    int n_experts;              /* E */
+    int top_k;                  /* k */
+    int inter;                  /* I of a routed expert */
+    int shared_inter;           /* I of the shared expert; 0 = no shared expert */
+    int weight_format;          /* enum moe_weight_format */
+    const void *router_w;       /* device bf16 [E][H]; may be NULL if logits are always given */
+    const float *router_bias;   /* device f32 [E] or NULL */
+    const void *shared_gate_w;  /* device bf16 [H]; NULL = ungated shared expert (s = 1) */
+    moe_expert_weights routed;  /* E slabs */
+    moe_expert_weights shared;  /* one slab (strides unused) */
+} moe_layer_weights;
+
+/* Routing results: caller-owned device arrays. */
+typedef struct moe_routing {
+    size_t struct_size;         /* sizeof(moe_routing) */
+    int32_t *topk_ids;          /* [R][k], descending weight */
+    float *topk_w;              /* [R][k], renormalised, sums to 1 per row */
+    float *shared_gate;         /* [R], s = sigmoid(x . w_sg) (1 when ungated) */
+    int32_t *expert_count;      /* [E]   rows routed to each expert (R >= 2; may be NULL at R == 1) */
+    int32_t *expert_offset;     /* [E+1] exclusive scan of expert_count */
+    int32_t *perm;              /* [R*k] perm[offset[e] + n] = r*k + j, rows ascending per expert */
+    float *logits;              /* [R][E] router logits out; may be NULL */
+} moe_routing;
+
+/* Kernel kinds, for moe_ctx_kernel_stats. */
+enum moe_kernel_id {
+    MOE_K_ROUTER = 0,   /* router GEMV (+ shared gate, + top-k for small R) */
+    MOE_K_TOPK = 1,     /* top-k softmax from logits (+ shared gate) */
+    MOE_K_GROUP = 2,    /* histogram, scan, ranks, permutation */
+    MOE_K_GATE_UP = 3,  /* gate/up GEMV + silu*mul (routed and shared) */
+    MOE_K_DOWN = 4,     /* down GEMV (R == 1: fused with the blend) */
+    MOE_K_BLEND = 5,    /* weighted blend + residual (R >= 2) */
+    MOE_K_MFMA_GATE_UP = 6,
+    MOE_K_MFMA_DOWN = 7,
+    MOE_K_COUNT = 8
+};
+
+MOE_API int moe_abi_version(void);
+MOE_API const char *moe_strerror(int status);
+
+/* Create a ctx on HIP device `device`.  Allocates the ctx's synchronisation
+ * words (a few KB) on that device.  Reads MOE_FAULT_AT (see
+ * moe_ctx_set_fault_at), MOE_FORCE_ARM ("gemv" or "mfma") and
+ * MOE_MFMA_MIN_ROWS from the environment. */
+MOE_API int moe_ctx_create(int device, moe_ctx **out);
+MOE_API int moe_ctx_destroy(moe_ctx *ctx);
+/* The ctx's sticky status: MOE_OK, or the error that marked it lost. */
+MOE_API int moe_ctx_status(const moe_ctx *ctx);
+/* Fault injection: the n-th kernel launch from now on (n >= 1) is not made;
+ * the ctx becomes lost and the call returns MOE_ERR_DEVICE_LOST.  n <= 0
+ * disables it. */
+MOE_API int moe_ctx_set_fault_at(moe_ctx *ctx, int64_t n);
+/* Rows per expert at and above which (with a step of at least 32 rows) an
+ * expert takes the MFMA grouped-GEMM arm; 0 restores the default. */
+MOE_API int moe_ctx_set_mfma_min_rows(moe_ctx *ctx, int rows);
+/* Force the arm: 0 = automatic, 1 = GEMV arm only, 2 = MFMA arm for every
+ * expert with at least one row (steps of >= 2 rows). */
+MOE_API int moe_ctx_set_force_arm(moe_ctx *ctx, int arm);
+/* Device-side error word: kernels that meet an expert id outside [0, E)
+ * skip it and set bit 0.  Synchronises the ctx's device; clears the word
+ * when `clear` is non-zero. */
+MOE_API int moe_ctx_device_errors(moe_ctx *ctx, uint32_t *flags, int clear);
+/* Per-kernel timing with HIP events on the launch stream (diagnostics;
+ * adds an event pair around every launch while enabled).  enable != 0
+ * starts (and resets) it; stats synchronise on the recorded events. */
+MOE_API int moe_ctx_set_timing(moe_ctx *ctx, int enable);
+MOE_API int moe_ctx_kernel_stats(moe_ctx *ctx, int kernel_id, double *total_ms,
+                                 int64_t *launches);
+
+/* Workspace bytes a call with `rows` rows needs (moe_layer_forward with a
+ * NULL routing argument included).  0 on invalid arguments. */
+MOE_API size_t moe_workspace_bytes(const moe_layer_weights *w, int rows);
+
+/* Routing (GB10 blueprint, "Kernels": dense_gemv_bf16 as the router,
+ * moe_topk_softmax; "Plan arms": multi-row decode steps).
+ *   x         device bf16 [rows][ldx] activations
+ *   logits_in device f32 [rows][E] or NULL; when given it replaces the router
+ *             GEMV (the router matrix is then not read)
+ *   out       routing arrays to fill; expert_count/offset/perm are filled when
+ *             rows >= 2 (and must then be non-NULL)
+ *   ws        device workspace of at least moe_workspace_bytes(w, rows) */
+MOE_API int moe_route(moe_ctx *ctx, const moe_layer_weights *w, const void *x, int rows,
+                      int64_t ldx, const float *logits_in, const moe_routing *out,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Experts and blend for already-routed rows (GB10 blueprint, "Kernels":
+ * moe_expert_gate_up_shared_fp8, moe_expert_silu_down_shared_fp8,
+ * moe_weighted_sum_blend).
+ *   in        routing of these rows (as moe_route fills it; the grouping
+ *             arrays are read when rows >= 2); ids outside [0, E) are skipped
+ *             and flagged in the ctx's device error word
+ *   y         device bf16 [rows][ldy] or NULL: receives bf16_rne(y)
+ *   residual  device bf16 [rows][ldy] or NULL, in-out: residual <- bf16_rne(residual + y)
+ *   At least one of y and residual must be given. */
+MOE_API int moe_expert_ffn(moe_ctx *ctx, const moe_layer_weights *w, const void *x, int rows,
+                           int64_t ldx, const moe_routing *in, void *y, void *residual,
+                           int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer: moe_route then moe_expert_ffn.  `routing` may be NULL,
+ * in which case the routing arrays live in the workspace. */
+MOE_API int moe_layer_forward(moe_ctx *ctx, const moe_layer_weights *w, const void *x, int rows,
+                              int64_t ldx, const float *logits_in, const moe_routing *routing,
+                              void *y, void *residual, int64_t ldy, void *ws, size_t ws_bytes,
+                              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,589 @@
+// api.cpp -- the C ABI (include/moe.h): argument validation before any
+// enqueue, the ctx (sticky lost state, fault injection, arm options, event
+// timing), the workspace layout and the launch sequence of a layer.
+//
+// Conventions follow colibri pull request 1992, "What it is": ops declined on
+// bad arguments, a HIP error marks the device lost to the ctx, one stream per
+// call; 0 is success here (HIP style) rather than the page's 0 = declined.
+#include "moe.h"
+#include "moe_debug.h"
+#include "kernels.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+namespace {
+
+enum SyncWord : int { kWordRouterTicket = 0, kWordError = 1, kSyncWords = 64 };
+constexpr int kDefaultMfmaMinRows = 0;   // MFMA arm off until enabled
+constexpr int kMaxRows = 1024;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxHidden = 8192;
+constexpr int kMaxInter = 4096;
+constexpr int kFusedTopkMaxRows = 16;
+constexpr size_t kMaxGroupWords = 8192;   // grouping bitmap: 32 KB of LDS
+constexpr size_t kMaxTimingRecords = 1 << 16;
+
+struct TimingRecord {
+    hipEvent_t a, b;
+    int kind;
+};
+
+}  // namespace
+
+struct moe_ctx {
+    int device = 0;
+    int status = MOE_OK;
+    int64_t fault_countdown = 0;
+    int mfma_min_rows = kDefaultMfmaMinRows;
+    int force_arm = 0;
+    uint32_t *words = nullptr;   // device: kSyncWords words
+    bool timing = false;
+    std::vector<TimingRecord> recs;
+    std::vector<hipEvent_t> spare;
+};
+
+namespace {
+
+// Makes the ctx's device current for the call and restores the caller's.
+class DeviceGuard {
+  public:
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev_) != hipSuccess) {
+            ok_ = false;
+            return;
+        }
+        if (prev_ != dev) {
+            ok_ = hipSetDevice(dev) == hipSuccess;
+            changed_ = ok_;
+        }
+    }
+    ~DeviceGuard() {
+        if (changed_) (void)hipSetDevice(prev_);
+    }
+    bool ok() const { return ok_; }
+
+  private:
+    int prev_ = -1;
+    bool ok_ = true;
+    bool changed_ = false;
+};
+
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t group_words(int E, int R) { return (size_t)E * (size_t)((R + 31) / 32); }
+
+int validate_family(const moe_expert_weights &f, int fmt, bool many) {
+    if (!f.gate_up || !f.gate_up_scale || !f.down || !f.down_scale) return MOE_ERR_INVALID_ARG;
+    if (fmt == MOE_WFMT_NVFP4 && (!f.gate_up_global || !f.down_global)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(f.gate_up, 16) || !aligned(f.down, 16)) return MOE_ERR_MISALIGNED;
+    const size_t salign = fmt == MOE_WFMT_FP8_E4M3_B128 ? 4 : 2;
+    if (!aligned(f.gate_up_scale, salign) || !aligned(f.down_scale, salign)) return MOE_ERR_MISALIGNED;
+    if (fmt == MOE_WFMT_NVFP4 && (!aligned(f.gate_up_global, 4) || !aligned(f.down_global, 4)))
+        return MOE_ERR_MISALIGNED;
+    if (many) {
+        if (f.gate_up_stride < 0 || f.gate_up_scale_stride < 0 || f.down_stride < 0 || f.down_scale_stride < 0)
+            return MOE_ERR_INVALID_ARG;
+        if (f.gate_up_stride % 16 || f.down_stride % 16) return MOE_ERR_MISALIGNED;
+        if (f.gate_up_scale_stride % (int64_t)salign || f.down_scale_stride % (int64_t)salign)
+            return MOE_ERR_MISALIGNED;
+    }
+    return MOE_OK;
+}
+
+// Down-projection lane shape (must match the kernels' launcher): lanes per
+// row from the routed intermediate size, chunks per lane for the longer of
+// routed and shared; at most 4 chunks per lane.
+bool down_shape_ok(const moe_layer_weights *w) {
+    const int fmt = w->weight_format;
+    const int nch = (fmt == MOE_WFMT_FP8_E4M3_B128 ? w->inter : w->inter / 2) / 16;
+    const int ie = std::max(w->inter, w->shared_inter);
+    const int nchmax = (fmt == MOE_WFMT_FP8_E4M3_B128 ? ie : ie / 2) / 16;
+    const int lpr = nch >= 64 ? 64 : nch >= 32 ? 32 : nch >= 16 ? 16 : 8;
+    return (nchmax + lpr - 1) / lpr <= 4;
+}
+
+int validate_weights(const moe_layer_weights *w) {
+    if (!w) return MOE_ERR_INVALID_ARG;
+    if (w->struct_size != sizeof(moe_layer_weights)) return MOE_ERR_INVALID_ARG;
+    if (w->weight_format != MOE_WFMT_FP8_E4M3_B128 && w->weight_format != MOE_WFMT_NVFP4)
+        return MOE_ERR_INVALID_ARG;
+    const int H = w->hidden, E = w->n_experts, k = w->top_k, I = w->inter, Is = w->shared_inter;
+    if (H <= 0 || E <= 0 || k <= 0 || I <= 0 || Is < 0) return MOE_ERR_INVALID_ARG;
+    if (H % 128 || H > kMaxHidden || I % 128 || I > kMaxInter || Is % 128 || Is > kMaxInter)
+        return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (k > kMaxTopK || k > E || E > kMaxExperts) return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (!down_shape_ok(w)) return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (w->router_w && !aligned(w->router_w, 16)) return MOE_ERR_MISALIGNED;
+    if (w->router_bias && !aligned(w->router_bias, 4)) return MOE_ERR_MISALIGNED;
+    if (w->shared_gate_w && !aligned(w->shared_gate_w, 16)) return MOE_ERR_MISALIGNED;
+    int rc = validate_family(w->routed, w->weight_format, true);
+    if (rc) return rc;
+    if (Is > 0) {
+        rc = validate_family(w->shared, w->weight_format, false);
+        if (rc) return rc;
+    }
+    return MOE_OK;
+}
+
+int validate_rows(const moe_layer_weights *w, int R) {
+    if (R < 0) return MOE_ERR_INVALID_ARG;
+    if (R > kMaxRows) return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (R >= 2 && group_words(w->n_experts, R) > kMaxGroupWords) return MOE_ERR_UNSUPPORTED_SHAPE;
+    return MOE_OK;
+}
+
+struct Layout {
+    size_t logits, ids, w, s, counts, offsets, perm, meta, gemv, mfma, tiles, h, dbuf, total;
+};
+
+Layout make_layout(const moe_layer_weights *w, int R) {
+    Layout L{};
+    const size_t E = w->n_experts, k = w->top_k, H = w->hidden;
+    const size_t ne = (size_t)R * k + (w->shared_inter > 0 ? (size_t)R : 0);
+    const size_t hs = (size_t)std::max(w->inter, w->shared_inter);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = round_up(off + bytes, 256);
+        return at;
+    };
+    L.logits = take((size_t)R * E * 4);
+    L.ids = take((size_t)R * k * 4);
+    L.w = take((size_t)R * k * 4);
+    L.s = take((size_t)R * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.perm = take((size_t)R * k * 4);
+    L.meta = take(moe::kMetaWords * 4);
+    L.gemv = take(E * 4);
+    L.mfma = take(E * 4);
+    L.tiles = take((E + 1) * 4);
+    L.h = take(ne * hs * 4);
+    L.dbuf = take(R >= 2 ? ne * H * 4 : 0);
+    L.total = off;
+    return L;
+}
+
+template <class T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+int fail(moe_ctx *c, int status) {
+    c->status = status;
+    return status;
+}
+
+hipEvent_t take_event(moe_ctx *c) {
+    if (!c->spare.empty()) {
+        hipEvent_t e = c->spare.back();
+        c->spare.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// One kernel launch under the ctx's rules: the injected fault, optional
+// event timing, and the sticky lost state on a launch error.
+template <class F>
+int launch(moe_ctx *c, int kind, hipStream_t st, F &&f) {
+    if (c->fault_countdown > 0 && --c->fault_countdown == 0) return fail(c, MOE_ERR_DEVICE_LOST);
+    hipEvent_t a = nullptr, b = nullptr;
+    if (kind >= 0 && c->timing && c->recs.size() < kMaxTimingRecords) {
+        a = take_event(c);
+        b = take_event(c);
+        if (a && b) (void)hipEventRecord(a, st);
+    }
+    const hipError_t e = f();
+    if (a && b) {
+        (void)hipEventRecord(b, st);
+        c->recs.push_back({a, b, kind});
+    }
+    if (e != hipSuccess) return fail(c, MOE_ERR_HIP);
+    return MOE_OK;
+}
+
+struct RoutingPtrs {
+    int32_t *ids;
+    float *w, *s;
+    int32_t *counts, *offsets, *perm;
+    float *logits;
+};
+
+int check_routing(const moe_routing *r, int R, bool need_group) {
+    if (!r || r->struct_size != sizeof(moe_routing)) return MOE_ERR_INVALID_ARG;
+    if (R == 0) return MOE_OK;
+    if (!r->topk_ids || !r->topk_w || !r->shared_gate) return MOE_ERR_INVALID_ARG;
+    if (need_group && R >= 2 && (!r->expert_count || !r->expert_offset || !r->perm)) return MOE_ERR_INVALID_ARG;
+    const void *ps[] = {r->topk_ids, r->topk_w, r->shared_gate, r->expert_count, r->expert_offset, r->perm, r->logits};
+    for (const void *p : ps)
+        if (p && !aligned(p, 4)) return MOE_ERR_MISALIGNED;
+    return MOE_OK;
+}
+
+int check_x(const moe_layer_weights *w, const void *x, int R, int64_t ldx) {
+    if (R == 0) return MOE_OK;
+    if (!x) return MOE_ERR_INVALID_ARG;
+    if (ldx < w->hidden) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || ldx % 8) return MOE_ERR_MISALIGNED;
+    return MOE_OK;
+}
+
+int check_out(const moe_layer_weights *w, const void *y, const void *res, int R, int64_t ldy) {
+    if (R == 0) return MOE_OK;
+    if (!y && !res) return MOE_ERR_INVALID_ARG;
+    if (ldy < w->hidden) return MOE_ERR_INVALID_ARG;
+    if ((y && !aligned(y, 2)) || (res && !aligned(res, 2))) return MOE_ERR_MISALIGNED;
+    return MOE_OK;
+}
+
+int check_ws(const moe_layer_weights *w, int R, const void *ws, size_t ws_bytes) {
+    if (R == 0) return MOE_OK;
+    if (!ws) return MOE_ERR_INVALID_ARG;
+    if (!aligned(ws, 16)) return MOE_ERR_MISALIGNED;
+    if (ws_bytes < make_layout(w, R).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return MOE_OK;
+}
+
+bool mfma_enabled(const moe_ctx *c, int R) {
+    if (c->force_arm == 1) return false;
+    if (c->force_arm == 2) return R >= 2;
+    return R >= 32 && c->mfma_min_rows > 0;
+}
+int mfma_threshold(const moe_ctx *c, int R) {
+    if (!mfma_enabled(c, R)) return 0;
+    return c->force_arm == 2 ? 1 : c->mfma_min_rows;
+}
+
+moe::RouteArgs route_args(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
+                          const float *logits_in, const RoutingPtrs &rp, void *ws, const Layout &L) {
+    moe::RouteArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.ldx = ldx;
+    a.R = R;
+    a.wr = static_cast<const uint16_t *>(w->router_w);
+    a.bias = w->router_bias;
+    a.wsg = static_cast<const uint16_t *>(w->shared_gate_w);
+    a.H = w->hidden;
+    a.E = w->n_experts;
+    a.k = w->top_k;
+    a.logits_in = logits_in;
+    a.logits = rp.logits ? rp.logits : at<float>(ws, L.logits);
+    a.ids = rp.ids;
+    a.w = rp.w;
+    a.s = rp.s;
+    a.counts = rp.counts;
+    a.offsets = rp.offsets;
+    a.perm = rp.perm;
+    a.meta = at<int32_t>(ws, L.meta);
+    a.gemv_list = at<int32_t>(ws, L.gemv);
+    a.mfma_list = at<int32_t>(ws, L.mfma);
+    a.mfma_tiles = at<int32_t>(ws, L.tiles);
+    a.mfma_min_rows = mfma_threshold(c, R);
+    a.counter = c->words + kWordRouterTicket;
+    a.err = c->words + kWordError;
+    return a;
+}
+
+int do_route(moe_ctx *c, const moe::RouteArgs &a, bool plan, hipStream_t st) {
+    int rc;
+    if (!a.logits_in) {
+        const bool fuse = a.R <= kFusedTopkMaxRows;
+        rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_router(a, fuse, st); });
+        if (rc) return rc;
+        if (!fuse) {
+            rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, false, st); });
+            if (rc) return rc;
+        }
+    } else {
+        rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, true, st); });
+        if (rc) return rc;
+    }
+    if (a.R >= 2) {
+        rc = launch(c, MOE_K_GROUP, st, [&] { return moe::launch_group(a, plan, st); });
+        if (rc) return rc;
+    }
+    return MOE_OK;
+}
+
+moe::ExpertSet expert_set(const moe_expert_weights &f, int inter) {
+    moe::ExpertSet s{};
+    s.gu = static_cast<const uint8_t *>(f.gate_up);
+    s.gu_s = static_cast<const uint8_t *>(f.gate_up_scale);
+    s.dn = static_cast<const uint8_t *>(f.down);
+    s.dn_s = static_cast<const uint8_t *>(f.down_scale);
+    s.gu_g = f.gate_up_global;
+    s.dn_g = f.down_global;
+    s.gu_stride = f.gate_up_stride;
+    s.gu_s_stride = f.gate_up_scale_stride;
+    s.dn_stride = f.down_stride;
+    s.dn_s_stride = f.down_scale_stride;
+    s.inter = inter;
+    return s;
+}
+
+int do_ffn(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx, const RoutingPtrs &rp,
+           void *y, void *res, int64_t ldy, void *ws, const Layout &L, hipStream_t st) {
+    moe::FfnArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.ldx = ldx;
+    a.R = R;
+    a.H = w->hidden;
+    a.E = w->n_experts;
+    a.k = w->top_k;
+    a.fmt = w->weight_format;
+    a.routed = expert_set(w->routed, w->inter);
+    if (w->shared_inter > 0) a.shared = expert_set(w->shared, w->shared_inter);
+    a.ids = rp.ids;
+    a.w = rp.w;
+    a.s = rp.s;
+    a.counts = rp.counts;
+    a.offsets = rp.offsets;
+    a.perm = rp.perm;
+    a.meta = at<int32_t>(ws, L.meta);
+    a.gemv_list = at<int32_t>(ws, L.gemv);
+    a.mfma_list = at<int32_t>(ws, L.mfma);
+    a.mfma_tiles = at<int32_t>(ws, L.tiles);
+    a.h = at<float>(ws, L.h);
+    a.hstride = std::max(w->inter, w->shared_inter);
+    a.dbuf = at<float>(ws, L.dbuf);
+    a.y = static_cast<uint16_t *>(y);
+    a.res = static_cast<uint16_t *>(res);
+    a.ldy = ldy;
+    a.err = c->words + kWordError;
+    a.max_routed_tasks = std::min(w->n_experts, R * w->top_k);
+    a.mfma_max_tiles = 0;
+    int rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up(a, st); });
+    if (rc) return rc;
+    if (R == 1) return launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
+    rc = launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_grouped(a, st); });
+    if (rc) return rc;
+    return launch(c, MOE_K_BLEND, st, [&] { return moe::launch_blend(a, st); });
+}
+
+RoutingPtrs routing_ptrs(const moe_routing *r, void *ws, const Layout &L) {
+    RoutingPtrs p{};
+    if (r) {
+        p = {r->topk_ids, r->topk_w, r->shared_gate, r->expert_count, r->expert_offset, r->perm, r->logits};
+    } else {
+        p = {at<int32_t>(ws, L.ids), at<float>(ws, L.w),      at<float>(ws, L.s),      at<int32_t>(ws, L.counts),
+             at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm), nullptr};
+    }
+    return p;
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+
+extern "C" {
+
+MOE_API int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_API const char *moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case MOE_ERR_MISALIGNED: return "misaligned pointer or leading dimension";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP error (ctx lost)";
+        case MOE_ERR_DEVICE_LOST: return "device lost (sticky)";
+        default: return "unknown status";
+    }
+}
+
+MOE_API int moe_ctx_create(int device, moe_ctx **out) {
+    if (!out) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess) return MOE_ERR_HIP;
+    if (device < 0 || device >= n) return MOE_ERR_INVALID_ARG;
+    moe_ctx *c = new (std::nothrow) moe_ctx();
+    if (!c) return MOE_ERR_INVALID_ARG;
+    c->device = device;
+    DeviceGuard g(device);
+    if (!g.ok() || hipMalloc(&c->words, kSyncWords * sizeof(uint32_t)) != hipSuccess ||
+        hipMemset(c->words, 0, kSyncWords * sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        if (c->words) (void)hipFree(c->words);
+        delete c;
+        return MOE_ERR_HIP;
+    }
+    if (const char *v = getenv("MOE_FAULT_AT")) c->fault_countdown = std::max<long long>(0, atoll(v));
+    if (const char *v = getenv("MOE_MFMA_MIN_ROWS")) c->mfma_min_rows = std::max(0, atoi(v));
+    if (const char *v = getenv("MOE_FORCE_ARM")) {
+        if (!strcmp(v, "gemv")) c->force_arm = 1;
+        if (!strcmp(v, "mfma")) c->force_arm = 2;
+    }
+    *out = c;
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_destroy(moe_ctx *c) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    DeviceGuard g(c->device);
+    for (auto &r : c->recs) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (auto e : c->spare) (void)hipEventDestroy(e);
+    if (c->words) (void)hipFree(c->words);
+    delete c;
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_status(const moe_ctx *c) { return c ? c->status : MOE_ERR_INVALID_ARG; }
+
+MOE_API int moe_ctx_set_fault_at(moe_ctx *c, int64_t n) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    c->fault_countdown = n > 0 ? n : 0;
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_set_mfma_min_rows(moe_ctx *c, int rows) {
+    if (!c || rows < 0) return MOE_ERR_INVALID_ARG;
+    c->mfma_min_rows = rows == 0 ? kDefaultMfmaMinRows : rows;
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_set_force_arm(moe_ctx *c, int arm) {
+    if (!c || arm < 0 || arm > 2) return MOE_ERR_INVALID_ARG;
+    c->force_arm = arm;
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_device_errors(moe_ctx *c, uint32_t *flags, int clear) {
+    if (!c || !flags) return MOE_ERR_INVALID_ARG;
+    if (c->status) return MOE_ERR_DEVICE_LOST;
+    DeviceGuard g(c->device);
+    if (hipDeviceSynchronize() != hipSuccess) return fail(c, MOE_ERR_HIP);
+    if (hipMemcpy(flags, c->words + kWordError, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(c, MOE_ERR_HIP);
+    if (clear && hipMemset(c->words + kWordError, 0, sizeof(uint32_t)) != hipSuccess) return fail(c, MOE_ERR_HIP);
+    if (clear && hipDeviceSynchronize() != hipSuccess) return fail(c, MOE_ERR_HIP);
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_set_timing(moe_ctx *c, int enable) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    DeviceGuard g(c->device);
+    for (auto &r : c->recs) {
+        c->spare.push_back(r.a);
+        c->spare.push_back(r.b);
+    }
+    c->recs.clear();
+    c->timing = enable != 0;
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_kernel_stats(moe_ctx *c, int kind, double *total_ms, int64_t *launches) {
+    if (!c || !total_ms || !launches || kind < 0 || kind >= MOE_K_COUNT) return MOE_ERR_INVALID_ARG;
+    DeviceGuard g(c->device);
+    double t = 0.0;
+    int64_t n = 0;
+    for (auto &r : c->recs) {
+        if (r.kind != kind) continue;
+        if (hipEventSynchronize(r.b) != hipSuccess) return fail(c, MOE_ERR_HIP);
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(c, MOE_ERR_HIP);
+        t += ms;
+        ++n;
+    }
+    *total_ms = t;
+    *launches = n;
+    return MOE_OK;
+}
+
+MOE_API size_t moe_workspace_bytes(const moe_layer_weights *w, int rows) {
+    if (validate_weights(w) || validate_rows(w, rows)) return 0;
+    return make_layout(w, rows).total;
+}
+
+MOE_API int moe_route(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
+                      const float *logits_in, const moe_routing *out, void *ws, size_t ws_bytes, void *stream) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->status) return MOE_ERR_DEVICE_LOST;
+    int rc;
+    if ((rc = validate_weights(w)) || (rc = validate_rows(w, R)) || (rc = check_x(w, x, R, ldx)) ||
+        (rc = check_routing(out, R, true)) || (rc = check_ws(w, R, ws, ws_bytes)))
+        return rc;
+    if (!logits_in && !w->router_w) return MOE_ERR_INVALID_ARG;
+    if (logits_in && !aligned(logits_in, 4)) return MOE_ERR_MISALIGNED;
+    if (R == 0) return MOE_OK;
+    DeviceGuard g(c->device);
+    if (!g.ok()) return fail(c, MOE_ERR_HIP);
+    const Layout L = make_layout(w, R);
+    const RoutingPtrs rp = routing_ptrs(out, ws, L);
+    return do_route(c, route_args(c, w, x, R, ldx, logits_in, rp, ws, L), false, (hipStream_t)stream);
+}
+
+MOE_API int moe_expert_ffn(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
+                           const moe_routing *in, void *y, void *res, int64_t ldy, void *ws, size_t ws_bytes,
+                           void *stream) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->status) return MOE_ERR_DEVICE_LOST;
+    int rc;
+    if ((rc = validate_weights(w)) || (rc = validate_rows(w, R)) || (rc = check_x(w, x, R, ldx)) ||
+        (rc = check_routing(in, R, true)) || (rc = check_out(w, y, res, R, ldy)) ||
+        (rc = check_ws(w, R, ws, ws_bytes)))
+        return rc;
+    if (R == 0) return MOE_OK;
+    DeviceGuard g(c->device);
+    if (!g.ok()) return fail(c, MOE_ERR_HIP);
+    const hipStream_t st = (hipStream_t)stream;
+    const Layout L = make_layout(w, R);
+    const RoutingPtrs rp = routing_ptrs(in, ws, L);
+    if (R >= 2) {
+        const moe::RouteArgs a = route_args(c, w, x, R, ldx, nullptr, rp, ws, L);
+        rc = launch(c, MOE_K_GROUP, st, [&] { return moe::launch_plan(a, st); });
+        if (rc) return rc;
+    }
+    return do_ffn(c, w, x, R, ldx, rp, y, res, ldy, ws, L, st);
+}
+
+MOE_API int moe_layer_forward(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
+                              const float *logits_in, const moe_routing *routing, void *y, void *res, int64_t ldy,
+                              void *ws, size_t ws_bytes, void *stream) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->status) return MOE_ERR_DEVICE_LOST;
+    int rc;
+    if ((rc = validate_weights(w)) || (rc = validate_rows(w, R)) || (rc = check_x(w, x, R, ldx)) ||
+        (routing && (rc = check_routing(routing, R, true))) || (rc = check_out(w, y, res, R, ldy)) ||
+        (rc = check_ws(w, R, ws, ws_bytes)))
+        return rc;
+    if (!logits_in && !w->router_w) return MOE_ERR_INVALID_ARG;
+    if (logits_in && !aligned(logits_in, 4)) return MOE_ERR_MISALIGNED;
+    if (R == 0) return MOE_OK;
+    DeviceGuard g(c->device);
+    if (!g.ok()) return fail(c, MOE_ERR_HIP);
+    const hipStream_t st = (hipStream_t)stream;
+    const Layout L = make_layout(w, R);
+    const RoutingPtrs rp = routing_ptrs(routing, ws, L);
+    rc = do_route(c, route_args(c, w, x, R, ldx, logits_in, rp, ws, L), true, st);
+    if (rc) return rc;
+    return do_ffn(c, w, x, R, ldx, rp, y, res, ldy, ws, L, st);
+}
+
+MOE_API int moe_debug_decode(moe_ctx *c, int fmt, const void *codes, float *out, int n, void *stream) {
+    if (!c || !codes || !out || n < 0 || n % 4 || (fmt != 0 && fmt != 1)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(codes, 4) || !aligned(out, 4)) return MOE_ERR_MISALIGNED;
+    if (c->status) return MOE_ERR_DEVICE_LOST;
+    if (n == 0) return MOE_OK;
+    DeviceGuard g(c->device);
+    const hipStream_t st = (hipStream_t)stream;
+    return launch(c, -1, st, [&] {
+        return moe::launch_decode_probe(fmt, static_cast<const uint8_t *>(codes), out, n, st);
+    });
+}
+
+}  // extern "C"

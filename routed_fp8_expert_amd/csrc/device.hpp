@@ -1,0 +1,166 @@
+// device.hpp -- device helpers shared by the gfx950 kernels: vector loads,
+// the stored number formats, wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ loads
+
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+// Weights are read once per step: stream them past the caches.
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// ------------------------------------------------------------------ formats
+
+// bf16 is the top half of a binary32, so widening is a shift.
+__device__ __forceinline__ float bf16lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest bf16, ties to even; NaN kept quiet.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// Two OCP e4m3 codes (byte pair 0-1 or 2-3 of `w`) to two bf16.  Every e4m3
+// value is exact in bf16 (3 mantissa bits, exponents 2^-9 .. 2^8).
+template <bool HI>
+__device__ __forceinline__ bf16x2 e4m3x2_bf16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+// Two OCP e4m3 codes to two f32.
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3x2_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+// One e4m3 code (byte `b` of `w`) to f32.
+__device__ __forceinline__ float e4m3_f32(uint32_t w, int b) {
+    f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(w >> (16 * (b >> 1)), false);
+    return (b & 1) ? v.y : v.x;
+}
+// Two e2m1 codes (byte `B` of `w`, the low nibble first) to two bf16.
+template <int B>
+__device__ __forceinline__ bf16x2 e2m1x2_bf16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B);
+}
+// Two e2m1 codes to two f32.
+template <int B>
+__device__ __forceinline__ f32x2 e2m1x2_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+}
+
+__device__ __forceinline__ float dot2(bf16x2 a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, as_bf16x2(b), c, false);
+}
+
+// 16 e4m3 codes (one 16-byte chunk) . 16 bf16 activations (two 16-byte chunks).
+__device__ __forceinline__ float dot16_e4m3_bf16(u32x4 w, u32x4 xa, u32x4 xb) {
+    float a = 0.0f;
+    a = dot2(e4m3x2_bf16<false>(w.x), xa.x, a);
+    a = dot2(e4m3x2_bf16<true>(w.x), xa.y, a);
+    a = dot2(e4m3x2_bf16<false>(w.y), xa.z, a);
+    a = dot2(e4m3x2_bf16<true>(w.y), xa.w, a);
+    a = dot2(e4m3x2_bf16<false>(w.z), xb.x, a);
+    a = dot2(e4m3x2_bf16<true>(w.z), xb.y, a);
+    a = dot2(e4m3x2_bf16<false>(w.w), xb.z, a);
+    a = dot2(e4m3x2_bf16<true>(w.w), xb.w, a);
+    return a;
+}
+
+// 8 e2m1 codes (one dword) . 8 bf16 activations (one 16-byte chunk).
+__device__ __forceinline__ float dot8_e2m1_bf16(uint32_t w, u32x4 x, float a) {
+    a = dot2(e2m1x2_bf16<0>(w), x.x, a);
+    a = dot2(e2m1x2_bf16<1>(w), x.y, a);
+    a = dot2(e2m1x2_bf16<2>(w), x.z, a);
+    a = dot2(e2m1x2_bf16<3>(w), x.w, a);
+    return a;
+}
+
+// 16 e4m3 codes . 16 f32 activations (four 16-byte chunks).
+__device__ __forceinline__ float dot16_e4m3_f32(u32x4 w, const f32x4 *h) {
+    float a = 0.0f;
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f32x2 lo = e4m3x2_f32<false>(ws[q]), hi = e4m3x2_f32<true>(ws[q]);
+        a = fmaf(lo.x, h[q].x, a);
+        a = fmaf(lo.y, h[q].y, a);
+        a = fmaf(hi.x, h[q].z, a);
+        a = fmaf(hi.y, h[q].w, a);
+    }
+    return a;
+}
+
+// 8 e2m1 codes (one dword) . 8 f32 activations (two 16-byte chunks).
+__device__ __forceinline__ float dot8_e2m1_f32(uint32_t w, f32x4 h0, f32x4 h1, float a) {
+    f32x2 v0 = e2m1x2_f32<0>(w), v1 = e2m1x2_f32<1>(w), v2 = e2m1x2_f32<2>(w),
+          v3 = e2m1x2_f32<3>(w);
+    a = fmaf(v0.x, h0.x, a);
+    a = fmaf(v0.y, h0.y, a);
+    a = fmaf(v1.x, h0.z, a);
+    a = fmaf(v1.y, h0.w, a);
+    a = fmaf(v2.x, h1.x, a);
+    a = fmaf(v2.y, h1.y, a);
+    a = fmaf(v3.x, h1.z, a);
+    a = fmaf(v3.y, h1.w, a);
+    return a;
+}
+
+// 8 bf16 weights . 8 bf16 activations (one 16-byte chunk each).
+__device__ __forceinline__ float dot8_bf16(u32x4 w, u32x4 x, float a) {
+    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), a, false);
+    return a;
+}
+
+// ------------------------------------------------------------------ reductions
+
+// Butterfly sum over aligned groups of W lanes; every lane of the group ends
+// with the same value (the same tree in every kernel, so a dot product comes
+// out bit-identical wherever it is computed).
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g / (1.0f + expf(-g)) * u;
+}
+
+// Device-side error word bits.
+enum : uint32_t { kErrBadExpertId = 1u };
+
+__device__ __forceinline__ void flag_error(uint32_t *err, uint32_t bit) {
+    if (err) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace moe

@@ -1,0 +1,72 @@
+// kernels.hpp -- host-side launch interface between the C ABI (api.cpp) and
+// the gfx950 kernels (route.hip, ffn.hip).  Plain structs of device pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct ExpertSet {
+    const uint8_t *gu, *gu_s, *dn, *dn_s;     // codes and scales (bytes)
+    const float *gu_g, *dn_g;                 // nvfp4 globals (per expert), else null
+    int64_t gu_stride, gu_s_stride, dn_stride, dn_s_stride;
+    int inter;                                 // I of this family (0 = absent)
+};
+
+// Per-step bookkeeping written by the grouping kernel, read by the expert
+// kernels (int32 words in the workspace).
+enum MetaWord : int {
+    kMetaGemvCount = 0,   // routed experts on the GEMV arm
+    kMetaMfmaCount = 1,   // routed experts on the MFMA arm
+    kMetaMfmaTiles = 2,   // MFMA row tiles (routed)
+    kMetaWords = 16
+};
+
+struct RouteArgs {
+    const uint16_t *x; int64_t ldx; int R;
+    const uint16_t *wr; const float *bias; const uint16_t *wsg;
+    int H, E, k;
+    const float *logits_in;     // when non-null the router GEMV is skipped
+    float *logits;              // [R][E] (router output or scratch)
+    int32_t *ids; float *w; float *s;
+    int32_t *counts, *offsets, *perm;   // grouping (R >= 2)
+    int32_t *meta, *gemv_list, *mfma_list, *mfma_tiles;
+    int mfma_min_rows;          // experts with count >= this go to the MFMA arm (0 = never)
+    unsigned *counter;          // ctx word for the router's last-block top-k
+    uint32_t *err;
+};
+
+struct FfnArgs {
+    const uint16_t *x; int64_t ldx; int R; int H; int E; int k; int fmt;
+    ExpertSet routed, shared;
+    const int32_t *ids; const float *w; const float *s;
+    const int32_t *counts, *offsets, *perm;
+    const int32_t *meta, *gemv_list, *mfma_list, *mfma_tiles;
+    float *h;        // [NE][hstride] silu*mul products, NE = R*k (+ R shared)
+    int hstride;     // max(I, Is)
+    float *dbuf;     // [NE][H] per-entry down outputs (R >= 2)
+    uint16_t *y; uint16_t *res; int64_t ldy;
+    uint32_t *err;
+    int max_routed_tasks;       // grid bound on routed experts for R >= 2
+    int mfma_max_tiles;         // grid bound on MFMA row tiles
+};
+
+// Each launcher returns the hipError_t of its launch (hipGetLastError).
+hipError_t launch_router(const RouteArgs &a, bool fuse_topk, hipStream_t st);
+hipError_t launch_topk(const RouteArgs &a, bool compute_s, hipStream_t st);
+hipError_t launch_group(const RouteArgs &a, bool plan, hipStream_t st);
+hipError_t launch_plan(const RouteArgs &a, hipStream_t st);
+size_t group_lds_bytes(int E, int R);
+
+hipError_t launch_gate_up(const FfnArgs &a, hipStream_t st);
+hipError_t launch_down_blend_r1(const FfnArgs &a, hipStream_t st);
+hipError_t launch_down_grouped(const FfnArgs &a, hipStream_t st);
+hipError_t launch_blend(const FfnArgs &a, hipStream_t st);
+hipError_t launch_mfma_gate_up(const FfnArgs &a, hipStream_t st);
+hipError_t launch_mfma_down(const FfnArgs &a, hipStream_t st);
+
+// Diagnostics: decode n codes with the kernels' own converters.
+hipError_t launch_decode_probe(int fmt, const uint8_t *codes, float *out, int n, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,272 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, for every workload, plus the kernels' own format
+converters, determinism and batch invariance."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as syn
+from gpu_helpers import check_layer, make_tie_free, need_gpu, oracle_threads
+from helpers import bits, host, tie_free_x
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    need_gpu()
+    import routed_fp8_expert_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def ctx(moe):
+    c = moe.Ctx(0)
+    yield c
+    c.close()
+
+
+@pytest.fixture(autouse=True)
+def _threads(orc):
+    orc.set_threads(oracle_threads())
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ formats
+
+def test_decode_probe_e4m3(moe, ctx, orc):
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(512, dtype=torch.float32, device="cuda")
+    moe.moe_debug_decode(ctx, 0, codes, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().reshape(256, 2)
+    ref = orc.e4m3_to_f32(np.arange(256, dtype=np.uint8))
+    ok = ~np.isnan(ref)
+    for path in range(2):
+        assert np.array_equal(o[ok, path].view(np.uint32), ref[ok].view(np.uint32)), f"path {path}"
+
+
+def test_decode_probe_e2m1(moe, ctx, orc):
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(1024, dtype=torch.float32, device="cuda")
+    moe.moe_debug_decode(ctx, 1, codes, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().reshape(256, 4)
+    b = np.arange(256, dtype=np.uint8)
+    lo, hi = orc.e2m1_to_f32(b & 15), orc.e2m1_to_f32(b >> 4)
+    for path in (0, 2):
+        assert np.array_equal(o[:, path], lo), f"low nibble path {path}"
+        assert np.array_equal(o[:, path + 1], hi), f"high nibble path {path}"
+
+
+# ------------------------------------------------------------------ helpers
+
+def _run(moe, ctx, wl, W, x, logits_in=None, residual0=None, rows_routing=True, layer=0):
+    from routed_fp8_expert_amd.workload import layer_weights
+    R = x.shape[0]
+    lw = layer_weights(wl, W)
+    rt = moe.Routing(R, wl.n_experts, wl.top_k, "cuda", logits=True)
+    ws = moe.workspace(lw, R, "cuda")
+    y = torch.full((R, wl.hidden), float("nan"), dtype=torch.bfloat16, device="cuda")
+    if residual0 is None:
+        residual0 = syn.make_residual(wl, layer, R, "cuda")
+    res = residual0.clone()
+    moe.moe_layer_forward(ctx, lw, x, y, res, ws, logits_in=logits_in, routing=rt)
+    torch.cuda.synchronize()
+    return y, res, rt, residual0
+
+
+def _layer(moe, ctx, orc, wl, layer, rows, sample_rows=None, W=None):
+    W = W if W is not None else syn.make_layer_weights(wl, layer, "cuda")
+    if wl.router == "gemv":
+        x, _ = tie_free_x(orc, wl, W, layer, rows, device="cuda")
+    else:
+        x = syn.make_x(wl, layer, rows, 0, "cuda")
+    li = syn.make_logits_in(wl, layer, rows, "cuda")
+    _say(f"{wl.name}: layer {layer}, rows {rows}")
+    y, res, rt, res0 = _run(moe, ctx, wl, W, x, li, layer=layer)
+    assert moe.moe_ctx_status(ctx) == 0
+    stats = check_layer(orc, wl, W, x, li, res0, y, res, rt, rows=sample_rows,
+                        what=f"{wl.name} L{layer} R{rows}")
+    _say(f"  max|err|/rms {stats[0]:.2e}, mean rel {stats[1]:.2e}")
+    return stats
+
+
+# ------------------------------------------------------------------ workloads
+
+def test_tiny_one_row(moe, ctx, orc):
+    _layer(moe, ctx, orc, syn.WORKLOADS["tiny"], 0, 1)
+
+
+@pytest.mark.parametrize("rows", [2, 3, 5, 17, 64])
+def test_tiny_multi_row_gemv_router(moe, ctx, orc, rows):
+    _layer(moe, ctx, orc, syn.WORKLOADS["tiny"], 0, rows)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 39])
+def test_a3b_one_row(moe, ctx, orc, layer):
+    _layer(moe, ctx, orc, syn.WORKLOADS["a3b"], layer, 1)
+
+
+@pytest.mark.parametrize("rows", [2, 4, 8, 16, 32, 64])
+def test_a3b_multi_row(moe, ctx, orc, rows):
+    wl = syn.WORKLOADS["a3b_multi"]
+    for layer in (0, 1):
+        _layer(moe, ctx, orc, wl, layer, rows)
+
+
+@pytest.mark.parametrize("rows", [1, 8])
+def test_a17b_nvfp4(moe, ctx, orc, rows):
+    _layer(moe, ctx, orc, syn.WORKLOADS["a17b"], 0, rows)
+
+
+def test_a3b_zipf_64(moe, ctx, orc):
+    _layer(moe, ctx, orc, syn.WORKLOADS["a3b_zipf"], 0, 64)
+
+
+def test_a3b_zipf_512_sampled(moe, ctx, orc):
+    wl = syn.WORKLOADS["a3b_zipf"]
+    li = syn.make_logits_in(wl, 0, 512, "cpu")
+    ids = li.topk(wl.top_k, dim=1).indices
+    hot = int(torch.bincount(ids.flatten(), minlength=wl.n_experts).argmax())
+    hot_rows = torch.where((ids == hot).any(1))[0][:8].tolist()
+    sample = sorted(set(hot_rows + [0, 1, 255, 256, 510, 511] + list(range(100, 108))))
+    _layer(moe, ctx, orc, wl, 0, 512, sample_rows=sample)
+
+
+def test_a3b_forty_layers_as_benchmarked(moe, ctx, orc):
+    """The benchmark's configuration: 40 resident layers, one row, run back to
+    back on one stream; every layer checked."""
+    from routed_fp8_expert_amd.workload import Resident
+    wl = syn.WORKLOADS["a3b"]
+    _say("a3b: building 40 resident layers")
+    res = Resident(wl, 1, device="cuda")
+    make_tie_free(orc, res)
+    res.run(ctx)
+    torch.cuda.synchronize()
+    assert moe.moe_ctx_status(ctx) == 0
+    worst = 0.0
+    for n, l in enumerate(res.layer_ids):
+        st = check_layer(orc, wl, res.W[n], res.x[n], None, res.residual0[n], res.y[n],
+                         res.residual[n], res.routing[n], what=f"a3b L{l}")
+        worst = max(worst, st[0])
+    _say(f"  40 layers ok, worst max|err|/rms {worst:.2e}")
+
+
+# ------------------------------------------------------------------ variants
+
+def _tiny_with(**changes):
+    wl = syn.WORKLOADS["tiny"]
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    for k, v in changes.items():
+        W[k] = v
+    return wl, W
+
+
+def test_no_residual_no_bias_ungated_shared(moe, ctx, orc):
+    import dataclasses
+    wl, W = _tiny_with(router_bias=None, shared_gate_w=None)
+    x, _ = tie_free_x(orc, wl, W, 0, 3, device="cuda")
+    y, res, rt, res0 = _run(moe, ctx, wl, W, x)
+    assert torch.all(rt.shared_gate == 1.0)
+    check_layer(orc, wl, W, x, None, res0, y, res, rt, what="ungated")
+
+
+def test_without_shared_expert(moe, ctx, orc):
+    import dataclasses
+    wl0 = syn.WORKLOADS["tiny"]
+    wl = dataclasses.replace(wl0, shared_inter=0)
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    x, _ = tie_free_x(orc, wl, W, 0, 2, device="cuda")
+    y, res, rt, res0 = _run(moe, ctx, wl, W, x)
+    check_layer(orc, wl, W, x, None, res0, y, res, rt, what="no shared")
+
+
+@pytest.mark.parametrize("k", [1, 16])
+def test_top_k_extremes(moe, ctx, orc, k):
+    import dataclasses
+    wl = dataclasses.replace(syn.WORKLOADS["tiny"], top_k=k)
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    x, _ = tie_free_x(orc, wl, W, 0, 4, device="cuda")
+    y, res, rt, res0 = _run(moe, ctx, wl, W, x)
+    check_layer(orc, wl, W, x, None, res0, y, res, rt, what=f"k={k}")
+    if k == 1:
+        assert torch.all(rt.topk_w == 1.0)
+
+
+def test_padded_leading_dimensions(moe, ctx, orc):
+    from routed_fp8_expert_amd.workload import layer_weights
+    wl = syn.WORKLOADS["tiny"]
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    x, _ = tie_free_x(orc, wl, W, 0, 3, device="cuda")
+    xp = torch.zeros((3, wl.hidden + 64), dtype=torch.bfloat16, device="cuda")
+    xp[:, : wl.hidden] = x
+    res0 = syn.make_residual(wl, 0, 3, "cuda")
+    yp = torch.zeros((3, wl.hidden + 32), dtype=torch.bfloat16, device="cuda")
+    rp = torch.zeros((3, wl.hidden + 32), dtype=torch.bfloat16, device="cuda")
+    rp[:, : wl.hidden] = res0
+    lw = layer_weights(wl, W)
+    rt = moe.Routing(3, wl.n_experts, wl.top_k, "cuda")
+    ws = moe.workspace(lw, 3, "cuda")
+    moe.moe_layer_forward(ctx, lw, xp[:, : wl.hidden], yp[:, : wl.hidden], rp[:, : wl.hidden], ws,
+                          routing=rt)
+    torch.cuda.synchronize()
+    assert torch.all(yp[:, wl.hidden:] == 0) and torch.all(rp[:, wl.hidden:] == 0)
+    check_layer(orc, wl, W, x, None, res0, yp[:, : wl.hidden], rp[:, : wl.hidden], rt, what="padded")
+
+
+def test_zero_rows_is_a_no_op(moe, ctx):
+    from routed_fp8_expert_amd.workload import layer_weights
+    wl = syn.WORKLOADS["tiny"]
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    lw = layer_weights(wl, W)
+    x = torch.empty((0, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((0, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    moe.moe_layer_forward(ctx, lw, x, y, None, ws)
+    torch.cuda.synchronize()
+    assert moe.moe_ctx_status(ctx) == 0
+
+
+def test_max_rows_with_given_logits(moe, ctx, orc):
+    wl = syn.WORKLOADS["a3b_multi"]
+    _layer(moe, ctx, orc, wl, 0, 1024, sample_rows=[0, 1, 511, 512, 1022, 1023])
+
+
+# ------------------------------------------------------------------ properties
+
+def test_determinism(moe, ctx, orc):
+    wl = syn.WORKLOADS["a3b_multi"]
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    x = syn.make_x(wl, 0, 16, 0, "cuda")
+    li = syn.make_logits_in(wl, 0, 16, "cuda")
+    r0 = syn.make_residual(wl, 0, 16, "cuda")
+    a = _run(moe, ctx, wl, W, x, li, r0)
+    b = _run(moe, ctx, wl, W, x, li, r0)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+    assert torch.equal(a[2].topk_ids, b[2].topk_ids) and torch.equal(a[2].perm, b[2].perm)
+
+
+def test_batch_invariance_gemv_arm(moe, ctx, orc):
+    """Three rows in one call give the bits of three one-row calls (the
+    colibri pull request's decode GEMV convention)."""
+    wl = syn.WORKLOADS["a3b"]
+    W = syn.make_layer_weights(wl, 2, "cuda")
+    x, _ = tie_free_x(orc, wl, W, 2, 3, device="cuda")
+    r0 = syn.make_residual(wl, 2, 3, "cuda")
+    moe.moe_ctx_set_force_arm(ctx, 1)
+    try:
+        y3, res3, rt3, _ = _run(moe, ctx, wl, W, x, None, r0)
+        for r in range(3):
+            y1, res1, rt1, _ = _run(moe, ctx, wl, W, x[r:r + 1].contiguous(), None,
+                                    r0[r:r + 1].contiguous())
+            assert torch.equal(rt1.topk_ids[0], rt3.topk_ids[r])
+            assert torch.equal(rt1.topk_w[0], rt3.topk_w[r])
+            assert torch.equal(y1[0].view(torch.int16), y3[r].view(torch.int16)), f"row {r}"
+            assert torch.equal(res1[0].view(torch.int16), res3[r].view(torch.int16)), f"row {r}"
+    finally:
+        moe.moe_ctx_set_force_arm(ctx, 0)
