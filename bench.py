@@ -1,0 +1,293 @@
+"""Benchmark of the decode-step MoE FFN on one MI355X.
+
+One step = one pass of the whole layer (routing, grouping when rows >= 2,
+gate/up + silu*mul, down + blend into the residual) over every resident
+layer of the workload, back to back on one stream, inputs already in HBM.
+Default workload: the 35B-A3B shape at one decode row (hidden 2048, 256
+experts top-8, intermediate 512, a gated shared expert, fp8 e4m3 block-128
+weights), 40 independent layers so the touched weights (~1.17 GB per step)
+exceed the on-package cache.
+
+Prints one JSON line (rank 0).  value = effective weight GB/s (each distinct
+touched expert's codes and scales once per step, the shared expert, the
+shared-gate vector and the router matrix) over the timed steps; us_per_layer
+and pct_hbm_peak are given beside it.  `roofline` is for the dominant kernel,
+timed with HIP events on the launch stream; `cpu_baseline` is the CPU oracle
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "us per MoE layer + effective weight GB/s (% of HBM peak), 35B-A3B shape, n=1"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="a3b")
+    p.add_argument("--rows", type=int, default=None)
+    p.add_argument("--layers", type=int, default=None)
+    p.add_argument("--launch", choices=["graph", "stream", "both"], default="both")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--profile-steps", type=int, default=None,
+                   help="run exactly this many steps (no warmup, no report) for profilers")
+    p.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
+                   help="run 10 device-to-device copies of MIB MiB (the counter calibration kernel)")
+    return p.parse_args()
+
+
+def distinct_routed(res) -> int:
+    """Distinct routed experts touched per step, summed over layers."""
+    import torch
+    total = 0
+    for rt in res.routing:
+        total += int(torch.unique(rt.topk_ids).numel())
+    return total
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "routed_fp8_expert_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str, rows: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel and workload, if it was taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_r{rows}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_digest") != source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, res, budget_s: float):
+    """The CPU oracle on the same layers (touched experts copied to the host
+    outside the timing), layer by layer until the time budget is spent."""
+    import numpy as np
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import bits, host, oracle_layer
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    oracle.set_threads(threads)
+    done_layers, t_total, bytes_total = 0, 0.0, 0
+    import moe_synth as syn
+    for n in range(len(res.layer_ids)):
+        ids = res.routing[n].topk_ids.cpu().numpy()
+        L = oracle_layer(oracle, wl, res.W[n], experts=np.unique(ids))
+        x = bits(res.x[n])
+        li = host(res.logits_in[n])
+        t0 = time.perf_counter()
+        oracle.layer_forward(L, x, logits_in=li)
+        t_total += time.perf_counter() - t0
+        done_layers += 1
+        bytes_total += syn.effective_weight_bytes(wl, int(np.unique(ids).size), li is None)
+        if t_total >= budget_s:
+            break
+    return {
+        "value": round(bytes_total / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "us_per_layer": round(t_total / done_layers * 1e6, 1),
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done_layers} of {len(res.layer_ids)} layers of the same workload, one pass each, "
+                  f"{threads} OpenMP threads, f64 arithmetic",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    if args.copy_calibration is not None:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 10}))
+        return
+
+    import moe_synth as syn
+    import routed_fp8_expert_amd as moe
+    from routed_fp8_expert_amd.workload import Resident
+
+    wl = syn.WORKLOADS[args.workload]
+    rows = args.rows if args.rows is not None else wl.rows[0]
+    layers = args.layers if args.layers is not None else wl.layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    res = Resident(wl, rows, layers, device=dev, keep_y=False)
+    ctx = moe.Ctx(0)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def step():
+        res.run(ctx, stream=stream, write_y=False)
+
+    if args.profile_steps is not None:
+        with torch.cuda.stream(stream):
+            for _ in range(args.profile_steps):
+                step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": wl.name, "rows": rows}))
+        return
+
+    results = {}
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+
+    def time_plain():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def time_graph():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(max(3, args.warmup // 4)):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    if args.launch in ("stream", "both"):
+        results["stream"] = time_plain()
+    if args.launch in ("graph", "both"):
+        results["graph"] = time_graph()
+    assert moe.moe_ctx_status(ctx) == 0
+    best_mode = min(results, key=results.get)
+    ms_per_step = results[best_mode]
+
+    touched = distinct_routed(res)
+    router_gemv = wl.router == "gemv"
+    eff_bytes = sum(syn.effective_weight_bytes(wl, int(torch.unique(rt.topk_ids).numel()), router_gemv)
+                    for rt in res.routing)
+    gbs = eff_bytes / (ms_per_step * 1e-3) / 1e9
+    us_layer = ms_per_step * 1e3 / layers
+
+    # per-kernel durations with HIP events around each launch (separate pass)
+    moe.moe_ctx_set_timing(ctx, True)
+    kt_steps = min(args.steps, 50)
+    for _ in range(kt_steps):
+        step()
+    torch.cuda.synchronize()
+    kernels = {}
+    for kid, name in enumerate(moe.KERNELS):
+        ms, n = moe.moe_ctx_kernel_stats(ctx, kid)
+        if n:
+            kernels[name] = {"avg_us": round(ms / n * 1e3, 3), "launches_per_step": n // kt_steps}
+    moe.moe_ctx_set_timing(ctx, False)
+
+    # algorithmic bytes per launch of each kernel (rows == 1 layout)
+    H, E, I, Is, k = wl.hidden, wl.n_experts, wl.inter, wl.shared_inter, wl.top_k
+    if wl.fmt == syn.FMT_FP8_B128:
+        gu_bytes_e = 2 * I * H + 4 * (2 * I // 128) * (H // 128)
+        dn_bytes_e = H * I + 4 * (H // 128) * (I // 128)
+    else:
+        gu_bytes_e = (2 * I * H) // 2 + (2 * I * H) // 16 + 4
+        dn_bytes_e = (H * I) // 2 + (H * I) // 16 + 4
+    u_per_layer = touched / layers
+    algo = {
+        "gate_up": (u_per_layer + (1 if Is else 0)) * gu_bytes_e + rows * H * 2 + (rows * k + rows) * I * 4,
+        "down": (u_per_layer + (1 if Is else 0)) * dn_bytes_e + (rows * k + rows) * I * 4 + 2 * rows * H * 2,
+        "router": (E * H * 2 + H * 2 + rows * H * 2) if router_gemv else 0,
+    }
+    # the dominant kernel: the largest share of the step's kernel time
+    roof_kernel = max(("gate_up", "down"),
+                      key=lambda n: kernels.get(n, {}).get("avg_us", 0) * kernels.get(n, {}).get("launches_per_step", 0))
+    kstat = kernels.get(roof_kernel)
+    roofline = None
+    if kstat:
+        achieved = algo[roof_kernel] / (kstat["avg_us"] * 1e-6) / 1e9
+        traffic = counter_traffic(roof_kernel, wl.name, rows)
+        roofline = {"bound": "hbm", "kernel": roof_kernel, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "algorithmic_bytes_per_launch": int(algo[roof_kernel])}
+    per_kernel_roof = {}
+    for name, st in kernels.items():
+        if name in algo and algo[name]:
+            per_kernel_roof[name] = round(algo[name] / (st["avg_us"] * 1e-6) / 1e9, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, res, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "us_per_layer": round(us_layer, 3),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-w/bf16-x/f32-acc" if wl.fmt == syn.FMT_FP8_B128 else "nvfp4-w/bf16-x/f32-acc",
+        "data": "synthetic (seeded; weights N(0,0.02) quantised, activations N(0,1) RMS-normalised)",
+        "config": {"workload": f"{wl.name}: hidden {H}, {E} experts top-{k}, inter {I}, shared inter {Is}, "
+                               f"{'fp8 e4m3 block-128' if wl.fmt == 0 else 'nvfp4'} weights, "
+                               f"{rows} row(s), {layers} layers back to back",
+                   "rows": rows, "layers": layers, "launch": best_mode,
+                   "router": wl.router},
+        "launch_ms_per_step": {m: round(v, 5) for m, v in results.items()},
+        "effective_bytes_per_step": int(eff_bytes),
+        "kernels": kernels,
+        "kernel_effective_gbs": per_kernel_roof,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+    ctx.close()
+
+
+if __name__ == "__main__":
+    main()

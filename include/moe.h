@@ -138,7 +138,8 @@ enum moe_kernel_id {
     MOE_K_BLEND = 5,    /* weighted blend + residual (R >= 2) */
     MOE_K_MFMA_GATE_UP = 6,
     MOE_K_MFMA_DOWN = 7,
-    MOE_K_COUNT = 8
+    MOE_K_LAYER = 8,    /* a whole one-row layer in one launch */
+    MOE_K_COUNT = 9
 };
 
 MOE_API int moe_abi_version(void);
@@ -162,8 +163,14 @@ MOE_API int moe_ctx_set_mfma_min_rows(moe_ctx *ctx, int rows);
 /* Force the arm: 0 = automatic, 1 = GEMV arm only, 2 = MFMA arm for every
  * expert with at least one row (steps of >= 2 rows). */
 MOE_API int moe_ctx_set_force_arm(moe_ctx *ctx, int arm);
+/* One-row layers: 0 = one launch per layer (router, top-k, routed and shared
+ * experts and the blend in one kernel; built for the 16-, 256- and
+ * 512-expert layer shapes, other shapes use the three launches), 1 = three
+ * launches (router and shared expert; routed gate/up; down and blend).
+ * Also MOE_ONE_ROW_PATH=split in the environment.  Both give the same bits. */
+MOE_API int moe_ctx_set_one_row_path(moe_ctx *ctx, int path);
 /* Device-side error word: kernels that meet an expert id outside [0, E)
- * skip it and set bit 0.  Synchronises the ctx's device; clears the word
+ * skip it and set bit 0; a bounded wait that timed out sets bit 1.  Synchronises the ctx's device; clears the word
  * when `clear` is non-zero. */
 MOE_API int moe_ctx_device_errors(moe_ctx *ctx, uint32_t *flags, int clear);
 /* Per-kernel timing with HIP events on the launch stream (diagnostics;

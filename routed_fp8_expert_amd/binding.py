@@ -27,7 +27,7 @@ MOE_ERR_DEVICE_LOST = -6
 MOE_WFMT_FP8_E4M3_B128 = 0
 MOE_WFMT_NVFP4 = 1
 
-KERNELS = ["router", "topk", "group", "gate_up", "down", "blend", "mfma_gate_up", "mfma_down"]
+KERNELS = ["router", "topk", "group", "gate_up", "down", "blend", "mfma_gate_up", "mfma_down", "layer"]
 
 
 class MoeError(RuntimeError):
@@ -78,6 +78,7 @@ def lib():
             "moe_ctx_set_fault_at": ([vp, i64], i32),
             "moe_ctx_set_mfma_min_rows": ([vp, i32], i32),
             "moe_ctx_set_force_arm": ([vp, i32], i32),
+            "moe_ctx_set_one_row_path": ([vp, i32], i32),
             "moe_ctx_device_errors": ([vp, C.POINTER(C.c_uint32), i32], i32),
             "moe_ctx_set_timing": ([vp, i32], i32),
             "moe_ctx_kernel_stats": ([vp, i32, C.POINTER(C.c_double), C.POINTER(i64)], i32),
@@ -172,6 +173,10 @@ def moe_ctx_set_mfma_min_rows(ctx: Ctx, rows: int) -> None:
 
 def moe_ctx_set_force_arm(ctx: Ctx, arm: int) -> None:
     _check(lib().moe_ctx_set_force_arm(ctx.handle, int(arm)), "moe_ctx_set_force_arm")
+
+
+def moe_ctx_set_one_row_path(ctx: Ctx, path: int) -> None:
+    _check(lib().moe_ctx_set_one_row_path(ctx.handle, int(path)), "moe_ctx_set_one_row_path")
 
 
 def moe_ctx_device_errors(ctx: Ctx, clear: bool = True) -> int:

@@ -19,14 +19,16 @@
 
 namespace {
 
-enum SyncWord : int { kWordRouterTicket = 0, kWordError = 1, kSyncWords = 64 };
+// ctx words: the router ticket, the error word and the warming sink on their
+// own lines, then the single-launch layer's synchronisation lines.
+enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, kWordLayerSync = 1024,
+                      kSyncWords = 1024 + 40 * 64 };
 constexpr int kDefaultMfmaMinRows = 0;   // MFMA arm off until enabled
 constexpr int kMaxRows = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxHidden = 8192;
 constexpr int kMaxInter = 4096;
-constexpr int kFusedTopkMaxRows = 16;
 constexpr size_t kMaxGroupWords = 8192;   // grouping bitmap: 32 KB of LDS
 constexpr size_t kMaxTimingRecords = 1 << 16;
 
@@ -43,6 +45,7 @@ struct moe_ctx {
     int64_t fault_countdown = 0;
     int mfma_min_rows = kDefaultMfmaMinRows;
     int force_arm = 0;
+    int one_row_path = 0;        // 0 = single launch where built, 1 = three launches
     uint32_t *words = nullptr;   // device: kSyncWords words
     bool timing = false;
     std::vector<TimingRecord> recs;
@@ -141,7 +144,7 @@ int validate_rows(const moe_layer_weights *w, int R) {
 }
 
 struct Layout {
-    size_t logits, ids, w, s, counts, offsets, perm, meta, gemv, mfma, tiles, h, dbuf, total;
+    size_t logits, ids, w, s, counts, offsets, perm, meta, gemv, mfma, tiles, h, dbuf, lrep, hrep, total;
 };
 
 Layout make_layout(const moe_layer_weights *w, int R) {
@@ -168,6 +171,9 @@ Layout make_layout(const moe_layer_weights *w, int R) {
     L.tiles = take((E + 1) * 4);
     L.h = take(ne * hs * 4);
     L.dbuf = take(R >= 2 ? ne * H * 4 : 0);
+    // replicas for the single-launch one-row layer
+    L.lrep = take(R == 1 ? (size_t)moe::kReplicas * E * 4 : 0);
+    L.hrep = take(R == 1 ? (size_t)moe::kReplicas * ne * hs * 4 : 0);
     L.total = off;
     return L;
 }
@@ -290,21 +296,18 @@ moe::RouteArgs route_args(moe_ctx *c, const moe_layer_weights *w, const void *x,
     a.mfma_list = at<int32_t>(ws, L.mfma);
     a.mfma_tiles = at<int32_t>(ws, L.tiles);
     a.mfma_min_rows = mfma_threshold(c, R);
-    a.counter = c->words + kWordRouterTicket;
     a.err = c->words + kWordError;
+    a.ticket = c->words + kWordRouterTicket;
     return a;
 }
 
 int do_route(moe_ctx *c, const moe::RouteArgs &a, bool plan, hipStream_t st) {
     int rc;
     if (!a.logits_in) {
-        const bool fuse = a.R <= kFusedTopkMaxRows;
-        rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_router(a, fuse, st); });
+        rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_router(a, st); });
         if (rc) return rc;
-        if (!fuse) {
-            rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, false, st); });
-            if (rc) return rc;
-        }
+        rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, false, st); });
+        if (rc) return rc;
     } else {
         rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, true, st); });
         if (rc) return rc;
@@ -332,8 +335,8 @@ moe::ExpertSet expert_set(const moe_expert_weights &f, int inter) {
     return s;
 }
 
-int do_ffn(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx, const RoutingPtrs &rp,
-           void *y, void *res, int64_t ldy, void *ws, const Layout &L, hipStream_t st) {
+moe::FfnArgs ffn_args(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
+                      const RoutingPtrs &rp, void *y, void *res, int64_t ldy, void *ws, const Layout &L) {
     moe::FfnArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.ldx = ldx;
@@ -361,14 +364,34 @@ int do_ffn(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t
     a.res = static_cast<uint16_t *>(res);
     a.ldy = ldy;
     a.err = c->words + kWordError;
+    a.sink = c->words + kWordSink;
+    a.logits_rep = at<float>(ws, L.lrep);
+    a.h_rep = at<float>(ws, L.hrep);
     a.max_routed_tasks = std::min(w->n_experts, R * w->top_k);
     a.mfma_max_tiles = 0;
+    return a;
+}
+
+// Experts and blend for routed rows (generic kernels).
+int do_ffn(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
     int rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up(a, st); });
     if (rc) return rc;
-    if (R == 1) return launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
+    if (a.R == 1) return launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
     rc = launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_grouped(a, st); });
     if (rc) return rc;
     return launch(c, MOE_K_BLEND, st, [&] { return moe::launch_blend(a, st); });
+}
+
+// The whole one-row layer in three launches: router rows with the shared
+// expert's gate/up; the top-k inside the routed gate/up; down with the blend.
+int do_layer_r1(moe_ctx *c, const moe::RouteArgs &r, moe::FfnArgs a, hipStream_t st) {
+    if (c->one_row_path == 0 && moe::layer_r1_supported(r, a))
+        return launch(c, MOE_K_LAYER, st, [&] { return moe::launch_layer_r1(r, a, c->words + kWordLayerSync, st); });
+    int rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_lead_r1(r, a, st); });
+    if (rc) return rc;
+    rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up_r1(a, st); });
+    if (rc) return rc;
+    return launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
 }
 
 RoutingPtrs routing_ptrs(const moe_routing *r, void *ws, const Layout &L) {
@@ -421,6 +444,7 @@ MOE_API int moe_ctx_create(int device, moe_ctx **out) {
     }
     if (const char *v = getenv("MOE_FAULT_AT")) c->fault_countdown = std::max<long long>(0, atoll(v));
     if (const char *v = getenv("MOE_MFMA_MIN_ROWS")) c->mfma_min_rows = std::max(0, atoi(v));
+    if (const char *v = getenv("MOE_ONE_ROW_PATH")) c->one_row_path = !strcmp(v, "split") ? 1 : 0;
     if (const char *v = getenv("MOE_FORCE_ARM")) {
         if (!strcmp(v, "gemv")) c->force_arm = 1;
         if (!strcmp(v, "mfma")) c->force_arm = 2;
@@ -459,6 +483,12 @@ MOE_API int moe_ctx_set_mfma_min_rows(moe_ctx *c, int rows) {
 MOE_API int moe_ctx_set_force_arm(moe_ctx *c, int arm) {
     if (!c || arm < 0 || arm > 2) return MOE_ERR_INVALID_ARG;
     c->force_arm = arm;
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_set_one_row_path(moe_ctx *c, int path) {
+    if (!c || path < 0 || path > 1) return MOE_ERR_INVALID_ARG;
+    c->one_row_path = path;
     return MOE_OK;
 }
 
@@ -548,7 +578,7 @@ MOE_API int moe_expert_ffn(moe_ctx *c, const moe_layer_weights *w, const void *x
         rc = launch(c, MOE_K_GROUP, st, [&] { return moe::launch_plan(a, st); });
         if (rc) return rc;
     }
-    return do_ffn(c, w, x, R, ldx, rp, y, res, ldy, ws, L, st);
+    return do_ffn(c, ffn_args(c, w, x, R, ldx, rp, y, res, ldy, ws, L), st);
 }
 
 MOE_API int moe_layer_forward(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
@@ -569,9 +599,12 @@ MOE_API int moe_layer_forward(moe_ctx *c, const moe_layer_weights *w, const void
     const hipStream_t st = (hipStream_t)stream;
     const Layout L = make_layout(w, R);
     const RoutingPtrs rp = routing_ptrs(routing, ws, L);
-    rc = do_route(c, route_args(c, w, x, R, ldx, logits_in, rp, ws, L), true, st);
+    const moe::RouteArgs ra = route_args(c, w, x, R, ldx, logits_in, rp, ws, L);
+    const moe::FfnArgs fa = ffn_args(c, w, x, R, ldx, rp, y, res, ldy, ws, L);
+    if (R == 1) return do_layer_r1(c, ra, fa, st);
+    rc = do_route(c, ra, true, st);
     if (rc) return rc;
-    return do_ffn(c, w, x, R, ldx, rp, y, res, ldy, ws, L, st);
+    return do_ffn(c, fa, st);
 }
 
 MOE_API int moe_debug_decode(moe_ctx *c, int fmt, const void *codes, float *out, int n, void *stream) {

@@ -135,21 +135,88 @@ __device__ __forceinline__ float dot8_bf16(u32x4 w, u32x4 x, float a) {
 }
 
 // ------------------------------------------------------------------ reductions
+//
+// Cross-lane steps use DPP (data-parallel primitives on the VALU: quad
+// permutes, half-row and row mirrors, row broadcasts) rather than
+// ds_bpermute, so a reduction is a short chain of VALU ops with no LDS round
+// trip.  All lanes of the wave must be active.
 
-// Butterfly sum over aligned groups of W lanes; every lane of the group ends
-// with the same value (the same tree in every kernel, so a dot product comes
-// out bit-identical wherever it is computed).
+enum : int {
+    kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+    kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+    kDppHalfMirror = 0x141, // lane i <- lane 7-i within each 8-lane half-row
+    kDppMirror = 0x140,     // lane i <- lane 15-i within each 16-lane row
+    kDppBcast15 = 0x142,    // row r <- lane 15 of row r-1 (rows selected by the row mask)
+    kDppBcast31 = 0x143,    // rows 2,3 <- lane 31
+};
+
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp(float old, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, v), CTRL, ROWS, 0xf,
+                                                                 false));
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+__device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// Sum over aligned groups of W lanes (W = 8, 16, 32 or 64); every lane of a
+// group ends with the same value, from the same tree in every kernel, so a
+// dot product comes out bit-identical wherever it is computed.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+    v += dpp<kDppXor1>(0.0f, v);
+    v += dpp<kDppXor2>(0.0f, v);
+    v += dpp<kDppHalfMirror>(0.0f, v);
+    if (W == 8) return v;
+    v += dpp<kDppMirror>(0.0f, v);
+    if (W == 16) return v;
+    v += dpp<kDppBcast15, 0xa>(0.0f, v);   // rows 1 and 3 now hold 32-lane sums
+    if (W == 32) {
+        const float lo = readlane(v, 31), hi = readlane(v, 63);
+        return (threadIdx.x & 32) ? hi : lo;
+    }
+    v += dpp<kDppBcast31, 0xc>(0.0f, v);   // row 3 holds the wave sum
+    return readlane(v, 63);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    const float ninf = -__builtin_inff();
+    v = fmaxf(v, dpp<kDppXor1>(ninf, v));
+    v = fmaxf(v, dpp<kDppXor2>(ninf, v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(ninf, v));
+    v = fmaxf(v, dpp<kDppMirror>(ninf, v));
+    v = fmaxf(v, dpp<kDppBcast15, 0xa>(ninf, v));
+    v = fmaxf(v, dpp<kDppBcast31, 0xc>(ninf, v));
+    return readlane(v, 63);
+}
+
+// Wave argmax under the total order (larger value first, lower index first
+// among equal values).  Returns the winner in every lane.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ void argmax_step(float &v, int &i) {
+    const float ov = dpp<CTRL, ROWS>(-__builtin_inff(), v);
+    const int oi = dpp<CTRL, ROWS>(0x7fffffff, i);
+    if (ov > v || (ov == v && oi < i)) {
+        v = ov;
+        i = oi;
+    }
+}
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+    argmax_step<kDppXor1>(v, i);
+    argmax_step<kDppXor2>(v, i);
+    argmax_step<kDppHalfMirror>(v, i);
+    argmax_step<kDppMirror>(v, i);
+    argmax_step<kDppBcast15, 0xa>(v, i);
+    argmax_step<kDppBcast31, 0xc>(v, i);
+    v = readlane(v, 63);
+    i = readlane(i, 63);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -157,7 +224,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 // Device-side error word bits.
-enum : uint32_t { kErrBadExpertId = 1u };
+enum : uint32_t { kErrBadExpertId = 1u, kErrWaitTimeout = 2u };
 
 __device__ __forceinline__ void flag_error(uint32_t *err, uint32_t bit) {
     if (err) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -1,6 +1,7 @@
 // ffn.hip -- expert kernels for gfx950 (GEMV arm): gate/up GEMV with
 // silu*mul, the down GEMV fused with the routing-weighted blend and the
-// residual add, and the grouped variants for multi-row steps.
+// residual add, the grouped variants for multi-row steps, and the one-row
+// layer's fused kernels.
 //
 // GB10 blueprint for Qwen3.6-35B-A3B-FP8, "Kernels":
 // moe_expert_gate_up_shared_fp8 (routed and shared gate/up in one launch),
@@ -9,71 +10,22 @@
 // activations (down).  colibri pull request 1992, "A decode GEMV": a wave per
 // output row with 16 bytes per lane reads weights near the bus rate, versus a
 // whole block per row; here each wave keeps several 16-byte weight loads per
-// lane in flight and reduces across the wave64.
+// lane in flight and reduces across the wave64 with DPP.
 //
-// Weight layouts (see moe.h): fp8 rows of H (gate/up) or I (down) codes with
-// f32 scales per 128x128 block; nvfp4 rows of packed e2m1 nibbles with one
-// e4m3 scale per 16 columns and an f32 global per matrix.
-#include "device.hpp"
-#include "kernels.hpp"
+// One decode row (three launches):
+//   lead     router rows (+ shared-gate row) and the shared expert's gate/up,
+//            which does not depend on the routing; warms the shared expert's
+//            down matrix into the memory-side cache
+//   gate/up  each wave takes the top-k of the logits itself, then its slice of
+//            a routed expert's gate/up; warms that expert's down rows
+//   down     each row group streams row o of all k+1 down matrices, stages h
+//            in LDS, and blends in slot order into the residual
+#include "gemv.hpp"
 
 namespace moe {
 
-enum : int { kFp8 = 0, kNvfp4 = 1 };
-constexpr int kMaxSlots = 17;   // top_k <= 16, plus the shared expert
-
-// Bytes of one stored weight row of `cols` columns, and columns per 16-byte chunk.
-template <int FMT> __device__ __forceinline__ int row_bytes(int cols) { return FMT == kFp8 ? cols : cols / 2; }
-template <int FMT> constexpr int cols_per_chunk() { return FMT == kFp8 ? 16 : 32; }
-
-// Scale(s) of chunk `c` of weight row `row` in a matrix of `cols` columns.
-// fp8: one f32 per 128x128 block; nvfp4: two e4m3 bytes (two 16-column groups).
-template <int FMT>
-__device__ __forceinline__ f32x2 chunk_scale(const uint8_t *s, int row, int cols, int c) {
-    if (FMT == kFp8) {
-        const float *sf = reinterpret_cast<const float *>(s);
-        const float v = sf[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)];
-        return f32x2{v, v};
-    } else {
-        const uint16_t b = *reinterpret_cast<const uint16_t *>(s + (size_t)row * (cols >> 4) + 2 * c);
-        return f32x2{e4m3_f32(b, 0), e4m3_f32(b, 1)};
-    }
-}
-
-// Partial dot of one 16-byte weight chunk with bf16 activations at `xp`
-// (the chunk's first column), scaled by its block scale(s).
-template <int FMT>
-__device__ __forceinline__ float chunk_dot_bf16(u32x4 w, f32x2 sc, const uint16_t *xp) {
-    if (FMT == kFp8) {
-        return sc.x * dot16_e4m3_bf16(w, ld16(xp), ld16(xp + 8));
-    } else {
-        float a = dot8_e2m1_bf16(w.x, ld16(xp), 0.0f);
-        a = dot8_e2m1_bf16(w.y, ld16(xp + 8), a);
-        float b = dot8_e2m1_bf16(w.z, ld16(xp + 16), 0.0f);
-        b = dot8_e2m1_bf16(w.w, ld16(xp + 24), b);
-        return sc.x * a + sc.y * b;
-    }
-}
-
-// Partial dot of one 16-byte weight chunk with f32 activations at `hp`.
-template <int FMT>
-__device__ __forceinline__ float chunk_dot_f32(u32x4 w, f32x2 sc, const float *hp) {
-    const f32x4 *h4 = reinterpret_cast<const f32x4 *>(hp);
-    if (FMT == kFp8) {
-        f32x4 hv[4] = {h4[0], h4[1], h4[2], h4[3]};
-        return sc.x * dot16_e4m3_f32(w, hv);
-    } else {
-        float a = dot8_e2m1_f32(w.x, h4[0], h4[1], 0.0f);
-        a = dot8_e2m1_f32(w.y, h4[2], h4[3], a);
-        float b = dot8_e2m1_f32(w.z, h4[4], h4[5], 0.0f);
-        b = dot8_e2m1_f32(w.w, h4[6], h4[7], b);
-        return sc.x * a + sc.y * b;
-    }
-}
-
-template <int FMT> __device__ __forceinline__ float global_scale(const float *g, int e) {
-    return FMT == kNvfp4 ? g[e] : 1.0f;
-}
+constexpr int P = kPairsPerWave;
+constexpr int kWarmLoads = 4;            // 16-byte warming loads per thread (16 KB per block)
 
 // Which expert and which entries (rows of h / dbuf) a task covers.
 // R == 1: task j < k is slot j, task k the shared expert.
@@ -81,10 +33,10 @@ template <int FMT> __device__ __forceinline__ float global_scale(const float *g,
 // from the grouping), the last task the shared expert over all R rows.
 struct Task {
     const ExpertSet *X;
-    int e;          // expert index within its family
-    int n;          // number of entries
+    int e;                 // expert index within its family
+    int n;                 // number of entries
     const int32_t *list;   // entry list (routed, R >= 2) or null
-    int first;      // first entry when list is null (entries first .. first+n-1)
+    int first;             // first entry when list is null (entries first .. first+n-1)
     bool valid;
 };
 
@@ -142,132 +94,145 @@ __device__ __forceinline__ int entry_row(const FfnArgs &a, int entry) {
     return entry < nk ? entry / a.k : entry - nk;
 }
 
-// gate/up GEMV + silu*mul.  Block = 4 waves; a wave owns P (gate, up) row
-// pairs (i, I+i) of one expert, keeps their 2P rows in registers (CH 16-byte
-// chunks per lane per row, lane-strided along the row) and walks the task's
-// activation rows.  h[entry][i] = silu(g_i) * u_i in f32.
-template <int FMT, int CH, int P>
+// Warm a (at most 16 KB) slice `part` of `nparts` of a matrix of `bytes`
+// bytes into the memory-side cache; returns the folded word.
+__device__ __forceinline__ uint32_t warm_slice(const uint8_t *base, size_t bytes, int part, int nparts) {
+    size_t chunk = (bytes + nparts - 1) / nparts;
+    chunk = (chunk + 15) & ~(size_t)15;
+    const size_t cap = (size_t)kWarmLoads * 16 * 256;
+    if (chunk > cap) chunk = cap;
+    const size_t begin = (size_t)part * chunk;
+    uint32_t acc = 0;
+    u32x4 v[kWarmLoads];
+#pragma unroll
+    for (int i = 0; i < kWarmLoads; ++i) {
+        const size_t off = begin + ((size_t)i * 256 + threadIdx.x) * 16;
+        v[i] = (off + 16 <= bytes && off < begin + chunk) ? ld16(base + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kWarmLoads; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    return acc;
+}
+
+__device__ __forceinline__ void sink_word(uint32_t *sink, uint32_t acc) {
+    if (acc == 0x9E3779B9u && sink) *sink = acc;
+}
+
+// ------------------------------------------------------------------ generic gate/up
+
+// gate/up GEMV + silu*mul for the task's rows.  Block = 4 waves; a wave owns
+// P (gate, up) row pairs of one expert in registers and walks the activation
+// rows of the task.
+template <int FMT, int CH>
 __global__ __launch_bounds__(256) void k_gate_up(FfnArgs a) {
-    const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x >> 6;
     const Task t = resolve_task(a, blockIdx.y);
     if (!t.valid || t.n == 0) return;
     const ExpertSet &X = *t.X;
-    const int I = X.inter, H = a.H;
     const int i0 = (blockIdx.x * 4 + wid) * P;
-    if (i0 >= I) return;
-    const int rb = row_bytes<FMT>(H);
-    const int nch = rb >> 4;
-    const uint8_t *wbase = X.gu + (size_t)t.e * X.gu_stride;
-    const uint8_t *sbase = X.gu_s + (size_t)t.e * X.gu_s_stride;
-
-    u32x4 wv[2 * P][CH];
-    f32x2 sc[2 * P][CH];
-#pragma unroll
-    for (int q = 0; q < 2 * P; ++q) {
-        const int p = q >> 1;
-        const int row = (q & 1) ? I + i0 + p : i0 + p;
-        const bool live = i0 + p < I;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int ch = lane + kWave * c;
-            const bool ok = live && ch < nch;
-            wv[q][c] = ok ? ld16_stream(wbase + (size_t)row * rb + (size_t)ch * 16) : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < 2 * P; ++q) {
-        const int p = q >> 1;
-        const int row = (q & 1) ? I + i0 + p : i0 + p;
-        const bool live = i0 + p < I;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int ch = lane + kWave * c;
-            sc[q][c] = (live && ch < nch) ? chunk_scale<FMT>(sbase, row, H, ch) : f32x2{0.0f, 0.0f};
-        }
-    }
-    const float g = global_scale<FMT>(X.gu_g, t.e);
-
+    if (i0 >= X.inter) return;
+    GateUpRows<FMT, CH, P> rows;
+    rows.load(X, t.e, i0, a.H);
     for (int n = 0; n < t.n; ++n) {
         const int entry = task_entry(t, n, a.R * a.k);
         if (entry < 0) {
-            if (lane == 0) flag_error(a.err, kErrBadExpertId);
+            flag_error(a.err, kErrBadExpertId);
             continue;
         }
-        const uint16_t *xr = a.x + (size_t)entry_row(a, entry) * a.ldx;
-        float acc[2 * P];
-#pragma unroll
-        for (int q = 0; q < 2 * P; ++q) acc[q] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int ch = lane + kWave * c;
-            if (ch < nch) {
-                const uint16_t *xp = xr + (size_t)ch * cols_per_chunk<FMT>();
-#pragma unroll
-                for (int q = 0; q < 2 * P; ++q) acc[q] += chunk_dot_bf16<FMT>(wv[q][c], sc[q][c], xp);
+        rows.apply(a.x + (size_t)entry_row(a, entry) * a.ldx, a.H, X.inter, i0,
+                   a.h + (size_t)entry * a.hstride);
+    }
+}
+
+// ------------------------------------------------------------------ one-row fused kernels
+
+// Lead kernel of a one-row layer.  Blocks [0, nrb): one wave per router row
+// (the E router rows unless logits are given, then just the shared-gate row);
+// the logits are stored write-through (agent scope), each router block then
+// takes a ticket, and the last one runs the top-k and publishes ids and
+// weights.  No cache writeback or invalidate is needed: the last block reads
+// the logits with agent-scope loads.  Blocks [nrb, ...): the shared expert's
+// gate/up pairs for the row, each block also warming a slice of the shared
+// expert's down matrix into the memory-side cache.
+template <int FMT, int NCH, int CH, int NV>
+__global__ __launch_bounds__(256) void k_lead_r1(RouteArgs r, FfnArgs a) {
+    __shared__ unsigned ticket_s;
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+    const int n_router = r.logits_in ? 0 : r.E;
+    const int n_rows = n_router + (r.wsg ? 1 : 0);
+    const int nrb = n_rows > 0 ? (n_rows + 3) / 4 : 1;
+    if (!r.wsg && blockIdx.x == 0 && threadIdx.x == 0) r.s[0] = 1.0f;
+    if ((int)blockIdx.x < nrb) {
+        const int row = blockIdx.x * 4 + wid;
+        if (row < n_rows) {
+            const bool gate_row = row >= n_router;
+            u32x4 wv[NCH];
+            load_bf16_row<NCH>(gate_row ? r.wsg : r.wr + (size_t)row * r.H, r.H, wv);
+            const float acc = dot_bf16_row<NCH>(wv, r.x, r.H);
+            if (lane == 0) {
+                if (gate_row)
+                    r.s[0] = sigmoid(acc);
+                else
+                    st_agent(r.logits + row, acc + (r.bias ? r.bias[row] : 0.0f));
             }
         }
-#pragma unroll
-        for (int q = 0; q < 2 * P; ++q) acc[q] = group_sum<kWave>(acc[q]);
-        if (lane < P && i0 + lane < I) {
-            float gv = acc[0], uv = acc[1];
-#pragma unroll
-            for (int p = 1; p < P; ++p)
-                if (lane == p) {
-                    gv = acc[2 * p];
-                    uv = acc[2 * p + 1];
-                }
-            a.h[(size_t)entry * a.hstride + i0 + lane] = silu_mul(gv * g, uv * g);
+        __builtin_amdgcn_s_waitcnt(0);     // this wave's stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0)
+            ticket_s = __hip_atomic_fetch_add(r.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (ticket_s != (unsigned)(nrb - 1) || wid != 0) return;
+        int e;
+        float w;
+        topk_wave<NV>(r.logits_in ? r.logits_in : r.logits, r.E, r.k, r.logits_in == nullptr, e, w);
+        if (lane < r.k) {
+            r.ids[lane] = e;
+            r.w[lane] = w;
         }
+        if (lane == 0) __hip_atomic_store(r.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
     }
+    const ExpertSet &X = a.shared;
+    if (X.inter <= 0) return;
+    const int b = blockIdx.x - nrb, nsb = gridDim.x - nrb;
+    const int i0 = (b * 4 + wid) * P;
+    GateUpRows<FMT, CH, P> rows;
+    if (i0 < X.inter) rows.load(X, 0, i0, a.H);
+    const uint32_t warm = warm_slice(X.dn, (size_t)a.H * row_bytes<FMT>(X.inter), b, nsb);
+    if (i0 < X.inter) rows.apply(a.x, a.H, X.inter, i0, a.h + (size_t)a.k * a.hstride);
+    sink_word(a.sink, warm);
 }
 
-// One down-projection output element: row `o` of expert `e`, dotted with
-// h[entry], reduced over the LPR lanes of the row group.  Weight chunks and
-// scales are preloaded by the caller.
-template <int FMT, int LPR, int CH>
-__device__ __forceinline__ float down_dot(const u32x4 (&wv)[CH], const f32x2 (&sc)[CH], const float *hrow,
-                                          int sub, int nch) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int ch = sub + LPR * c;
-        if (ch < nch) acc += chunk_dot_f32<FMT>(wv[c], sc[c], hrow + (size_t)ch * cols_per_chunk<FMT>());
+// gate/up of the routed experts of a one-row layer.  Grid (slices, k): block
+// (b, j) takes slot j's expert from the published ids and its slice b; each
+// block also warms its share of that expert's down matrix.
+template <int FMT, int CH>
+__global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
+    const int wid = threadIdx.x >> 6;
+    const int slot = blockIdx.y;
+    const int e = a.ids[slot];
+    if (e < 0 || e >= a.E) {
+        if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, kErrBadExpertId);
+        return;
     }
-    return group_sum<LPR>(acc);
-}
-
-template <int FMT, int LPR, int CH>
-__device__ __forceinline__ void load_down_row(const ExpertSet &X, int e, int o, int sub, int nch, int rb,
-                                              bool live, u32x4 (&wv)[CH], f32x2 (&sc)[CH]) {
-    const uint8_t *wrow = X.dn + (size_t)e * X.dn_stride + (size_t)o * rb;
-    const uint8_t *sbase = X.dn_s + (size_t)e * X.dn_s_stride;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int ch = sub + LPR * c;
-        const bool ok = live && ch < nch;
-        wv[c] = ok ? ld16_stream(wrow + (size_t)ch * 16) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int ch = sub + LPR * c;
-        sc[c] = (live && ch < nch) ? chunk_scale<FMT>(sbase, o, X.inter, ch) : f32x2{0.0f, 0.0f};
-    }
-}
-
-__device__ __forceinline__ void store_out(const FfnArgs &a, int r, int o, float y) {
-    if (a.y) a.y[(size_t)r * a.ldy + o] = f32_to_bf16(y);
-    if (a.res) {
-        uint16_t *p = a.res + (size_t)r * a.ldy + o;
-        *p = f32_to_bf16(bf16_to_f32(*p) + y);
-    }
+    const ExpertSet &X = a.routed;
+    const int i0 = (blockIdx.x * 4 + wid) * P;
+    GateUpRows<FMT, CH, P> rows;
+    if (i0 < X.inter) rows.load(X, e, i0, a.H);
+    const uint32_t warm = warm_slice(X.dn + (size_t)e * X.dn_stride, (size_t)a.H * row_bytes<FMT>(X.inter),
+                                     blockIdx.x, gridDim.x);
+    if (i0 < X.inter) rows.apply(a.x, a.H, X.inter, i0, a.h + (size_t)slot * a.hstride);
+    sink_word(a.sink, warm);
 }
 
 // Down GEMV fused with the blend, one activation row.  A row group of LPR
 // lanes owns output element o; it loads row o of every slot's down matrix up
-// front (all k+1 experts' loads in flight), then for each slot in order
-// reduces d_j and accumulates y = fma(w_j, d_j, y), then fma(s, d_shared, y).
-template <int FMT, int LPR, int CH>
+// front (all k+1 experts' loads in flight), stages h in LDS (HLDS), then for
+// each slot in order reduces d_j and accumulates y = fma(w_j, d_j, y), then
+// fma(s, d_shared, y), and adds into the residual.
+template <int FMT, int LPR, int CH, bool HLDS>
 __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
+    extern __shared__ f32x4 hlds4[];
     constexpr int RPW = kWave / LPR;
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
     const int sub = lane % LPR;
@@ -275,21 +240,26 @@ __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
     const bool live = o < a.H;
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
 
-    u32x4 wv[kMaxSlots][CH];
-    f32x2 sc[kMaxSlots][CH];
+    DownRow<FMT, LPR, CH> rows[kMaxSlots];
     int es[kMaxSlots];
 #pragma unroll
     for (int j = 0; j < kMaxSlots; ++j) {
         if (j < nslots) {
             const bool sh = j == a.k;
             const ExpertSet &X = sh ? a.shared : a.routed;
-            int e = sh ? 0 : a.ids[j];
+            const int e = sh ? 0 : a.ids[j];
             const bool ok = sh || (e >= 0 && e < a.E);
-            if (!ok) e = -1;
-            es[j] = e;
-            const int rb = row_bytes<FMT>(X.inter);
-            load_down_row<FMT, LPR, CH>(X, ok ? e : 0, o, sub, rb >> 4, rb, live && ok, wv[j], sc[j]);
+            es[j] = ok ? e : -1;
+            rows[j].load(X, ok ? e : 0, o, sub, live && ok);
         }
+    }
+    const float *hbase = a.h;
+    if (HLDS) {
+        const int n4 = nslots * a.hstride / 4;
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.h);
+        for (int i = threadIdx.x; i < n4; i += 256) hlds4[i] = src[i];
+        __syncthreads();
+        hbase = reinterpret_cast<const float *>(hlds4);
     }
     float y = 0.0f;
 #pragma unroll
@@ -298,16 +268,15 @@ __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
             const bool sh = j == a.k;
             const ExpertSet &X = sh ? a.shared : a.routed;
             if (es[j] < 0) {
-                if (lane == 0 && blockIdx.x == 0 && wid == 0) flag_error(a.err, kErrBadExpertId);
+                if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, kErrBadExpertId);
                 continue;
             }
-            const int rb = row_bytes<FMT>(X.inter);
-            float d = down_dot<FMT, LPR, CH>(wv[j], sc[j], a.h + (size_t)j * a.hstride, sub, rb >> 4);
+            float d = rows[j].dot(hbase + (size_t)j * a.hstride, X.inter, sub);
             d *= global_scale<FMT>(X.dn_g, es[j]);
             y = fmaf(sh ? a.s[0] : a.w[j], d, y);
         }
     }
-    if (live && sub == 0) store_out(a, 0, o, y);
+    if (live && sub == 0) store_out(a.y, a.res, a.ldy, 0, o, y);
 }
 
 // Down GEMV for one expert of a multi-row step: a row group keeps row o of
@@ -322,15 +291,13 @@ __global__ __launch_bounds__(256) void k_down_grouped(FfnArgs a) {
     const int sub = lane % LPR;
     const int o = (blockIdx.x * 4 + wid) * RPW + lane / LPR;
     const bool live = o < a.H;
-    const int rb = row_bytes<FMT>(X.inter);
-    u32x4 wv[CH];
-    f32x2 sc[CH];
-    load_down_row<FMT, LPR, CH>(X, t.e, o, sub, rb >> 4, rb, live, wv, sc);
+    DownRow<FMT, LPR, CH> row;
+    row.load(X, t.e, o, sub, live);
     const float g = global_scale<FMT>(X.dn_g, t.e);
     for (int n = 0; n < t.n; ++n) {
         const int entry = task_entry(t, n, a.R * a.k);
         if (entry < 0) continue;
-        const float d = down_dot<FMT, LPR, CH>(wv, sc, a.h + (size_t)entry * a.hstride, sub, rb >> 4) * g;
+        const float d = row.dot(a.h + (size_t)entry * a.hstride, X.inter, sub) * g;
         if (live && sub == 0) a.dbuf[(size_t)entry * a.H + o] = d;
     }
 }
@@ -350,7 +317,7 @@ __global__ __launch_bounds__(256) void k_blend(FfnArgs a) {
         y = fmaf(a.w[i], a.dbuf[(size_t)i * a.H + o], y);
     }
     if (a.shared.inter > 0) y = fmaf(a.s[r], a.dbuf[(size_t)(a.R * a.k + r) * a.H + o], y);
-    store_out(a, r, o, y);
+    store_out(a.y, a.res, a.ldy, r, o, y);
 }
 
 // Decode probe: every code through the kernels' converters.
@@ -387,22 +354,22 @@ __global__ void k_decode_probe(int fmt, const uint8_t *codes, float *out, int n)
 
 static int routed_tasks(const FfnArgs &a) { return a.R == 1 ? a.k : a.max_routed_tasks; }
 static int n_tasks(const FfnArgs &a) { return routed_tasks(a) + (a.shared.inter > 0 ? 1 : 0); }
+static int gate_up_chunks(int fmt, int H) { return ((fmt == kFp8 ? H : H / 2) / 16 + kWave - 1) / kWave; }
+static int max_inter(const FfnArgs &a) { return a.routed.inter > a.shared.inter ? a.routed.inter : a.shared.inter; }
+
+#define MOE_CH_DISPATCH(CH_VALUE, LAUNCH)                                                             \
+    do {                                                                                              \
+        const int ch_ = (CH_VALUE);                                                                   \
+        if (ch_ <= 1) { constexpr int CH = 1; LAUNCH; }                                               \
+        else if (ch_ <= 2) { constexpr int CH = 2; LAUNCH; }                                          \
+        else if (ch_ <= 4) { constexpr int CH = 4; LAUNCH; }                                          \
+        else { constexpr int CH = 8; LAUNCH; }                                                        \
+    } while (0)
 
 template <int FMT>
 static hipError_t gate_up_fmt(const FfnArgs &a, hipStream_t st) {
-    constexpr int P = 2;
-    const int imax = a.routed.inter > a.shared.inter ? a.routed.inter : a.shared.inter;
-    const int nch = (FMT == kFp8 ? a.H : a.H / 2) / 16;
-    const int ch = (nch + kWave - 1) / kWave;
-    dim3 grid((imax + 4 * P - 1) / (4 * P), n_tasks(a)), block(256);
-    if (ch <= 1)
-        hipLaunchKernelGGL((k_gate_up<FMT, 1, P>), grid, block, 0, st, a);
-    else if (ch <= 2)
-        hipLaunchKernelGGL((k_gate_up<FMT, 2, P>), grid, block, 0, st, a);
-    else if (ch <= 4)
-        hipLaunchKernelGGL((k_gate_up<FMT, 4, P>), grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL((k_gate_up<FMT, 8, P>), grid, block, 0, st, a);
+    dim3 grid((max_inter(a) + 4 * P - 1) / (4 * P), n_tasks(a)), block(256);
+    MOE_CH_DISPATCH(gate_up_chunks(FMT, a.H), hipLaunchKernelGGL((k_gate_up<FMT, CH>), grid, block, 0, st, a));
     return hipGetLastError();
 }
 
@@ -410,52 +377,92 @@ hipError_t launch_gate_up(const FfnArgs &a, hipStream_t st) {
     return a.fmt == kFp8 ? gate_up_fmt<kFp8>(a, st) : gate_up_fmt<kNvfp4>(a, st);
 }
 
-// Lanes per down row: enough 16-byte chunks to cover the routed expert's row
-// (capped at the wave); chunks per lane cover the longer of routed and shared.
-template <int FMT>
-static void down_shape(const FfnArgs &a, int &lpr, int &ch) {
-    const int nch = (FMT == kFp8 ? a.routed.inter : a.routed.inter / 2) / 16;
-    const int ie = a.routed.inter > a.shared.inter ? a.routed.inter : a.shared.inter;
-    const int nchmax = (FMT == kFp8 ? ie : ie / 2) / 16;
-    lpr = nch >= 64 ? 64 : nch >= 32 ? 32 : nch >= 16 ? 16 : 8;
-    ch = (nchmax + lpr - 1) / lpr;
+template <int FMT, int NCH, int NV>
+static hipError_t lead_fmt(const RouteArgs &r, const FfnArgs &a, hipStream_t st) {
+    const int n_rows = (r.logits_in ? 0 : r.E) + (r.wsg ? 1 : 0);
+    const int nrb = n_rows > 0 ? (n_rows + 3) / 4 : 1;
+    const int nsb = a.shared.inter > 0 ? (a.shared.inter + 4 * P - 1) / (4 * P) : 0;
+    dim3 grid(nrb + nsb), block(256);
+    MOE_CH_DISPATCH(gate_up_chunks(FMT, a.H),
+                    hipLaunchKernelGGL((k_lead_r1<FMT, NCH, CH, NV>), grid, block, 0, st, r, a));
+    return hipGetLastError();
 }
 
-#define MOE_DOWN_DISPATCH(KERNEL, FMT, GRID)                                                          \
+template <int FMT, int NCH>
+static hipError_t lead_nv(const RouteArgs &r, const FfnArgs &a, hipStream_t st) {
+    switch (topk_nv(r.E)) {
+        case 1: return lead_fmt<FMT, NCH, 1>(r, a, st);
+        case 2: return lead_fmt<FMT, NCH, 2>(r, a, st);
+        case 4: return lead_fmt<FMT, NCH, 4>(r, a, st);
+        case 8: return lead_fmt<FMT, NCH, 8>(r, a, st);
+        default: return lead_fmt<FMT, NCH, 16>(r, a, st);
+    }
+}
+
+template <int FMT>
+static hipError_t lead_nch(const RouteArgs &r, const FfnArgs &a, hipStream_t st) {
+    const int nch = ((r.H >> 3) + kWave - 1) / kWave;
+    if (nch <= 1) return lead_nv<FMT, 1>(r, a, st);
+    if (nch <= 2) return lead_nv<FMT, 2>(r, a, st);
+    if (nch <= 4) return lead_nv<FMT, 4>(r, a, st);
+    if (nch <= 8) return lead_nv<FMT, 8>(r, a, st);
+    return lead_nv<FMT, 16>(r, a, st);
+}
+
+hipError_t launch_lead_r1(const RouteArgs &r, const FfnArgs &a, hipStream_t st) {
+    return a.fmt == kFp8 ? lead_nch<kFp8>(r, a, st) : lead_nch<kNvfp4>(r, a, st);
+}
+
+template <int FMT>
+static hipError_t gate_up_r1_fmt(const FfnArgs &a, hipStream_t st) {
+    dim3 grid((a.routed.inter + 4 * P - 1) / (4 * P), a.k), block(256);
+    MOE_CH_DISPATCH(gate_up_chunks(FMT, a.H), hipLaunchKernelGGL((k_gate_up_r1<FMT, CH>), grid, block, 0, st, a));
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_up_r1(const FfnArgs &a, hipStream_t st) {
+    return a.fmt == kFp8 ? gate_up_r1_fmt<kFp8>(a, st) : gate_up_r1_fmt<kNvfp4>(a, st);
+}
+
+constexpr size_t kMaxHLds = 64 * 1024;
+
+#define MOE_DOWN_CH(...)                                                                           \
     do {                                                                                              \
-        int lpr, ch;                                                                                  \
-        down_shape<FMT>(a, lpr, ch);                                                                  \
-        const int rows_per_block = 4 * (kWave / lpr);                                                 \
-        dim3 grid GRID;                                                                               \
-        dim3 block(256);                                                                              \
-        if (ch > 4) return hipErrorInvalidValue;                                                      \
-        if (lpr == 8) {                                                                               \
-            if (ch <= 1) hipLaunchKernelGGL((KERNEL<FMT, 8, 1>), grid, block, 0, st, a);              \
-            else if (ch <= 2) hipLaunchKernelGGL((KERNEL<FMT, 8, 2>), grid, block, 0, st, a);         \
-            else hipLaunchKernelGGL((KERNEL<FMT, 8, 4>), grid, block, 0, st, a);                      \
-        } else if (lpr == 16) {                                                                       \
-            if (ch <= 1) hipLaunchKernelGGL((KERNEL<FMT, 16, 1>), grid, block, 0, st, a);             \
-            else if (ch <= 2) hipLaunchKernelGGL((KERNEL<FMT, 16, 2>), grid, block, 0, st, a);        \
-            else hipLaunchKernelGGL((KERNEL<FMT, 16, 4>), grid, block, 0, st, a);                     \
-        } else if (lpr == 32) {                                                                       \
-            if (ch <= 1) hipLaunchKernelGGL((KERNEL<FMT, 32, 1>), grid, block, 0, st, a);             \
-            else if (ch <= 2) hipLaunchKernelGGL((KERNEL<FMT, 32, 2>), grid, block, 0, st, a);        \
-            else hipLaunchKernelGGL((KERNEL<FMT, 32, 4>), grid, block, 0, st, a);                     \
-        } else {                                                                                      \
-            if (ch <= 1) hipLaunchKernelGGL((KERNEL<FMT, 64, 1>), grid, block, 0, st, a);             \
-            else if (ch <= 2) hipLaunchKernelGGL((KERNEL<FMT, 64, 2>), grid, block, 0, st, a);        \
-            else hipLaunchKernelGGL((KERNEL<FMT, 64, 4>), grid, block, 0, st, a);                     \
-        }                                                                                             \
+        if (ch_ <= 1) { constexpr int CH = 1; __VA_ARGS__; }                                          \
+        else if (ch_ <= 2) { constexpr int CH = 2; __VA_ARGS__; }                                     \
+        else { constexpr int CH = 4; __VA_ARGS__; }                                                   \
+    } while (0)
+#define MOE_DOWN_DISPATCH(...)                                                                     \
+    do {                                                                                              \
+        int lpr_, ch_;                                                                                \
+        down_lane_shape(FMT, a.routed.inter, a.shared.inter, lpr_, ch_);                              \
+        if (ch_ > 4) return hipErrorInvalidValue;                                                     \
+        const int rows_per_block = 4 * (kWave / lpr_);                                                \
+        if (lpr_ == 8) { constexpr int LPR = 8; MOE_DOWN_CH(__VA_ARGS__); }                                \
+        else if (lpr_ == 16) { constexpr int LPR = 16; MOE_DOWN_CH(__VA_ARGS__); }                         \
+        else if (lpr_ == 32) { constexpr int LPR = 32; MOE_DOWN_CH(__VA_ARGS__); }                         \
+        else { constexpr int LPR = 64; MOE_DOWN_CH(__VA_ARGS__); }                                         \
         return hipGetLastError();                                                                     \
     } while (0)
 
 template <int FMT>
 static hipError_t down_r1_fmt(const FfnArgs &a, hipStream_t st) {
-    MOE_DOWN_DISPATCH(k_down_r1, FMT, ((a.H + rows_per_block - 1) / rows_per_block));
+    const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
+    const size_t hbytes = (size_t)nslots * a.hstride * 4;
+    MOE_DOWN_DISPATCH({
+        dim3 grid((a.H + rows_per_block - 1) / rows_per_block), block(256);
+        if (hbytes <= kMaxHLds)
+            hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, true>), grid, block, hbytes, st, a);
+        else
+            hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, false>), grid, block, 0, st, a);
+    });
 }
 template <int FMT>
 static hipError_t down_grouped_fmt(const FfnArgs &a, hipStream_t st) {
-    MOE_DOWN_DISPATCH(k_down_grouped, FMT, ((a.H + rows_per_block - 1) / rows_per_block, n_tasks(a)));
+    MOE_DOWN_DISPATCH({
+        dim3 grid((a.H + rows_per_block - 1) / rows_per_block, n_tasks(a)), block(256);
+        hipLaunchKernelGGL((k_down_grouped<FMT, LPR, CH>), grid, block, 0, st, a);
+    });
 }
 
 hipError_t launch_down_blend_r1(const FfnArgs &a, hipStream_t st) {

@@ -1,0 +1,386 @@
+// gemv.hpp -- the per-wave building blocks every kernel is made of: a bf16
+// router row, the wave64 top-k softmax, the fp8 / nvfp4 weight chunks of the
+// gate/up and down GEMVs.  Kernels that compute the same quantity call the
+// same function, so the fused one-row kernels and the generic multi-row
+// kernels give bit-identical values.
+#pragma once
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+enum : int { kFp8 = 0, kNvfp4 = 1 };
+constexpr int kMaxSlots = 17;          // top_k <= 16, plus the shared expert
+constexpr int kPairsPerWave = 2;       // gate/up (i, I+i) row pairs per wave
+
+__device__ __forceinline__ float sigmoid(float t) { return 1.0f / (1.0f + expf(-t)); }
+
+// ------------------------------------------------------------------ router
+
+// One bf16 router row (H values, resident in registers as NCH 16-byte chunks
+// per lane) dotted with activation row xr: the lane-strided chunks, fdot2
+// with f32 accumulation, a wave sum.
+template <int NCH>
+__device__ __forceinline__ void load_bf16_row(const uint16_t *row, int H, u32x4 (&wv)[NCH]) {
+    const int lane = threadIdx.x & (kWave - 1), nch = H >> 3;
+#pragma unroll
+    for (int t = 0; t < NCH; ++t) {
+        const int c = lane + kWave * t;
+        wv[t] = c < nch ? ld16_stream(row + (size_t)c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+template <int NCH>
+__device__ __forceinline__ float dot_bf16_row(const u32x4 (&wv)[NCH], const uint16_t *xr, int H) {
+    const int lane = threadIdx.x & (kWave - 1), nch = H >> 3;
+    float acc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NCH; ++t) {
+        const int c = lane + kWave * t;
+        if (c < nch) acc = dot8_bf16(wv[t], ld16(xr + (size_t)c * 8), acc);
+    }
+    return group_sum<kWave>(acc);
+}
+
+// ------------------------------------------------------------------ top-k
+
+__device__ __forceinline__ float ld_agent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int ld_agent(const int *p) {
+    return __hip_atomic_load(const_cast<int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int *p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld_agent(const unsigned *p) {
+    return __hip_atomic_load(const_cast<unsigned *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The top-k's total order (larger value first, lower index first among
+// equal values) as one unsigned 64-bit key: the float's bits made
+// order-preserving in the high word, the complemented index in the low word.
+// Key 0 sorts below every real entry.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+    uint32_t u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+    uint32_t u = (uint32_t)(key >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+    return __uint_as_float(u);
+}
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)~(uint32_t)key; }
+
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint64_t key_max_step(uint64_t k) {
+    const uint32_t lo = (uint32_t)dpp<CTRL, ROWS>(0, (int)(uint32_t)k);
+    const uint32_t hi = (uint32_t)dpp<CTRL, ROWS>(0, (int)(uint32_t)(k >> 32));
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > k ? o : k;
+}
+// Largest key of the wave, in every lane.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+    k = key_max_step<kDppXor1>(k);
+    k = key_max_step<kDppXor2>(k);
+    k = key_max_step<kDppHalfMirror>(k);
+    k = key_max_step<kDppMirror>(k);
+    k = key_max_step<kDppBcast15, 0xa>(k);
+    k = key_max_step<kDppBcast31, 0xc>(k);
+    const uint32_t lo = (uint32_t)readlane((int)(uint32_t)k, 63);
+    const uint32_t hi = (uint32_t)readlane((int)(uint32_t)(k >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Softmax over the E logits of one row, the k largest under the top-k order
+// and their renormalised weights, by one wave, without branches.  Each lane
+// holds NV keys (experts lane, lane+64, ...) sorted once; every round the
+// wave takes the largest lane head and the lane holding it pops its head.
+// w_j = exp(l_j - m) / sum_j exp(l_j - m), m the largest logit: the softmax
+// denominator over all E cancels in the renormalisation.  Lane j < k returns
+// slot j.  `coherent` reads the logits with agent-scope loads (written by
+// other workgroups of the same launch).  NaN logits count as -inf.
+template <int NV>
+__device__ __forceinline__ void topk_wave(const float *l, int E, int k, bool coherent, int &my_e, float &my_w) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float raw[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        const int ec = e < E ? e : E - 1;
+        raw[i] = coherent ? ld_agent(l + ec) : l[ec];
+    }
+    uint64_t key[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        const float t = raw[i] != raw[i] ? -__builtin_inff() : raw[i];
+        key[i] = e < E ? topk_key(t, e) : 0ull;
+    }
+#pragma unroll
+    for (int i = 1; i < NV; ++i) {
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const uint64_t a = key[j - 1], b = key[j];
+            const bool sw = b > a;
+            key[j - 1] = sw ? b : a;
+            key[j] = sw ? a : b;
+        }
+    }
+    uint64_t sel = 0;
+    for (int j = 0; j < k; ++j) {
+        const uint64_t best = wave_max_key(key[0]);
+        const bool pop = key[0] == best;
+#pragma unroll
+        for (int i = 0; i + 1 < NV; ++i) key[i] = pop ? key[i + 1] : key[i];
+        key[NV - 1] = pop ? 0ull : key[NV - 1];
+        sel = lane == j ? best : sel;
+    }
+    const float v = key_value(sel);
+    const float m = readlane(v, 0);
+    const float ex = lane < k ? expf(v - m) : 0.0f;
+    const float sum = group_sum<kWave>(ex);
+    const int e = key_index(sel);
+    my_e = (lane < k && e >= 0 && e < E) ? e : 0;
+    my_w = ex / sum;
+}
+
+// Logits per lane for E experts: 1, 2, 4, 8 or 16.
+__host__ __device__ constexpr int topk_nv(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16; }
+
+// ------------------------------------------------------------------ weight chunks
+
+template <int FMT> __device__ __forceinline__ int row_bytes(int cols) { return FMT == kFp8 ? cols : cols / 2; }
+template <int FMT> constexpr int cols_per_chunk() { return FMT == kFp8 ? 16 : 32; }
+
+// Scale(s) of 16-byte chunk `c` of weight row `row` of a matrix with `cols`
+// columns.  fp8: one f32 per 128x128 block; nvfp4: two e4m3 bytes (two
+// 16-column groups).
+template <int FMT>
+__device__ __forceinline__ f32x2 chunk_scale(const uint8_t *s, int row, int cols, int c) {
+    if (FMT == kFp8) {
+        const float *sf = reinterpret_cast<const float *>(s);
+        const float v = sf[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)];
+        return f32x2{v, v};
+    } else {
+        const uint16_t b = *reinterpret_cast<const uint16_t *>(s + (size_t)row * (cols >> 4) + 2 * c);
+        return f32x2{e4m3_f32(b, 0), e4m3_f32(b, 1)};
+    }
+}
+
+// One 16-byte weight chunk . bf16 activations at xp (the chunk's first column).
+template <int FMT>
+__device__ __forceinline__ float chunk_dot_bf16(u32x4 w, f32x2 sc, const uint16_t *xp) {
+    if (FMT == kFp8) {
+        return sc.x * dot16_e4m3_bf16(w, ld16(xp), ld16(xp + 8));
+    } else {
+        float a = dot8_e2m1_bf16(w.x, ld16(xp), 0.0f);
+        a = dot8_e2m1_bf16(w.y, ld16(xp + 8), a);
+        float b = dot8_e2m1_bf16(w.z, ld16(xp + 16), 0.0f);
+        b = dot8_e2m1_bf16(w.w, ld16(xp + 24), b);
+        return sc.x * a + sc.y * b;
+    }
+}
+
+// One 16-byte weight chunk . f32 activations at hp (global or LDS).
+template <int FMT>
+__device__ __forceinline__ float chunk_dot_f32(u32x4 w, f32x2 sc, const float *hp) {
+    const f32x4 *h4 = reinterpret_cast<const f32x4 *>(hp);
+    if (FMT == kFp8) {
+        f32x4 hv[4] = {h4[0], h4[1], h4[2], h4[3]};
+        return sc.x * dot16_e4m3_f32(w, hv);
+    } else {
+        float a = dot8_e2m1_f32(w.x, h4[0], h4[1], 0.0f);
+        a = dot8_e2m1_f32(w.y, h4[2], h4[3], a);
+        float b = dot8_e2m1_f32(w.z, h4[4], h4[5], 0.0f);
+        b = dot8_e2m1_f32(w.w, h4[6], h4[7], b);
+        return sc.x * a + sc.y * b;
+    }
+}
+
+template <int FMT> __device__ __forceinline__ float global_scale(const float *g, int e) {
+    return FMT == kNvfp4 ? g[e] : 1.0f;
+}
+
+// ------------------------------------------------------------------ gate/up
+
+// The 2P gate/up rows (i0+p, I+i0+p) of expert e held by one wave: CH
+// lane-strided 16-byte chunks per row, with their scales.
+template <int FMT, int CH, int P>
+struct GateUpRows {
+    u32x4 w[2 * P][CH];
+    f32x2 sc[2 * P][CH];
+    float g;
+
+    __device__ __forceinline__ void load(const ExpertSet &X, int e, int i0, int H) {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int I = X.inter, rb = row_bytes<FMT>(H), nch = rb >> 4;
+        const uint8_t *wbase = X.gu + (size_t)e * X.gu_stride;
+        const uint8_t *sbase = X.gu_s + (size_t)e * X.gu_s_stride;
+#pragma unroll
+        for (int q = 0; q < 2 * P; ++q) {
+            const int p = q >> 1;
+            const int row = (q & 1) ? I + i0 + p : i0 + p;
+            const bool live = i0 + p < I;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int ch = lane + kWave * c;
+                w[q][c] = (live && ch < nch) ? ld16_stream(wbase + (size_t)row * rb + (size_t)ch * 16)
+                                             : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 2 * P; ++q) {
+            const int p = q >> 1;
+            const int row = (q & 1) ? I + i0 + p : i0 + p;
+            const bool live = i0 + p < I;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int ch = lane + kWave * c;
+                sc[q][c] = (live && ch < nch) ? chunk_scale<FMT>(sbase, row, H, ch) : f32x2{0.0f, 0.0f};
+            }
+        }
+        g = global_scale<FMT>(X.gu_g, e);
+    }
+
+    // h[i0 + p] = silu(g) * u for activation row xr.  Plain: lane p writes
+    // pair p.  COHERENT (another workgroup of the same launch reads it): the
+    // value is written at agent scope (write-through) into `nrep` replicas
+    // `rep` floats apart, lane p + P*c writing pair p of replica c.
+    template <bool COHERENT = false>
+    __device__ __forceinline__ void apply(const uint16_t *xr, int H, int I, int i0, float *hrow,
+                                          size_t rep = 0, int nrep = 1) const {
+        const int lane = threadIdx.x & (kWave - 1), nch = row_bytes<FMT>(H) >> 4;
+        float acc[2 * P];
+#pragma unroll
+        for (int q = 0; q < 2 * P; ++q) acc[q] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int ch = lane + kWave * c;
+            if (ch < nch) {
+                const uint16_t *xp = xr + (size_t)ch * cols_per_chunk<FMT>();
+#pragma unroll
+                for (int q = 0; q < 2 * P; ++q) acc[q] += chunk_dot_bf16<FMT>(w[q][c], sc[q][c], xp);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 2 * P; ++q) acc[q] = group_sum<kWave>(acc[q]);
+        const int p = lane % P, copy = lane / P;
+        float gv = acc[0], uv = acc[1];
+#pragma unroll
+        for (int pp = 1; pp < P; ++pp)
+            if (p == pp) {
+                gv = acc[2 * pp];
+                uv = acc[2 * pp + 1];
+            }
+        if (i0 + p >= I) return;
+        const float hv = silu_mul(gv * g, uv * g);
+        if (COHERENT) {
+            if (copy < nrep)
+                __hip_atomic_store(hrow + (size_t)copy * rep + i0 + p, hv, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else if (copy == 0) {
+            hrow[i0 + p] = hv;
+        }
+    }
+};
+
+// ------------------------------------------------------------------ down
+
+// Row o of expert e's down matrix as seen by one lane of its LPR-lane row
+// group: CH chunks (lane-strided by LPR) with their scales.
+template <int FMT, int LPR, int CH>
+struct DownRow {
+    u32x4 w[CH];
+    f32x2 sc[CH];
+
+    __device__ __forceinline__ void load(const ExpertSet &X, int e, int o, int sub, bool live) {
+        const int rb = row_bytes<FMT>(X.inter), nch = rb >> 4;
+        const uint8_t *wrow = X.dn + (size_t)e * X.dn_stride + (size_t)o * rb;
+        const uint8_t *sbase = X.dn_s + (size_t)e * X.dn_s_stride;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int ch = sub + LPR * c;
+            w[c] = (live && ch < nch) ? ld16_stream(wrow + (size_t)ch * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int ch = sub + LPR * c;
+            sc[c] = (live && ch < nch) ? chunk_scale<FMT>(sbase, o, X.inter, ch) : f32x2{0.0f, 0.0f};
+        }
+    }
+
+    // d = row . h (h: the expert's f32 intermediate, global or LDS), reduced
+    // over the row group; every lane of the group gets it.
+    __device__ __forceinline__ float dot(const float *h, int inter, int sub) const {
+        const int nch = row_bytes<FMT>(inter) >> 4;
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int ch = sub + LPR * c;
+            if (ch < nch) acc += chunk_dot_f32<FMT>(w[c], sc[c], h + (size_t)ch * cols_per_chunk<FMT>());
+        }
+        return group_sum<LPR>(acc);
+    }
+
+    // The same dot product over h held in LDS in chunk-quad order (quad q of
+    // chunk c at float (q * nchunks + c) * 4), so consecutive lanes read
+    // consecutive 16-byte words: the same products in the same order.
+    __device__ __forceinline__ float dot_perm(const float *hl, int inter, int sub) const {
+        constexpr int CPC = cols_per_chunk<FMT>();
+        const int nch = row_bytes<FMT>(inter) >> 4;
+        const int nct = inter / CPC;
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int ch = sub + LPR * c;
+            if (ch < nch) {
+                f32x4 hq[CPC / 4];
+#pragma unroll
+                for (int q = 0; q < CPC / 4; ++q)
+                    hq[q] = *reinterpret_cast<const f32x4 *>(hl + ((size_t)q * nct + ch) * 4);
+                acc += chunk_dot_f32<FMT>(w[c], sc[c], reinterpret_cast<const float *>(hq));
+            }
+        }
+        return group_sum<LPR>(acc);
+    }
+};
+
+// Lanes per down row and chunks per lane for a layer (the launchers and the
+// host-side shape check agree on this rule): lanes cover the routed expert's
+// row, capped at the wave; chunks per lane cover the longer of the two rows.
+__host__ __device__ inline void down_lane_shape(int fmt, int inter, int shared_inter, int &lpr, int &ch) {
+    const int nch = (fmt == kFp8 ? inter : inter / 2) / 16;
+    const int ie = inter > shared_inter ? inter : shared_inter;
+    const int nchmax = (fmt == kFp8 ? ie : ie / 2) / 16;
+    lpr = nch >= 64 ? 64 : nch >= 32 ? 32 : nch >= 16 ? 16 : 8;
+    ch = (nchmax + lpr - 1) / lpr;
+}
+
+__device__ __forceinline__ void store_out(uint16_t *y, uint16_t *res, int64_t ldy, int r, int o, float v) {
+    if (y) y[(size_t)r * ldy + o] = f32_to_bf16(v);
+    if (res) {
+        uint16_t *p = res + (size_t)r * ldy + o;
+        *p = f32_to_bf16(bf16_to_f32(*p) + v);
+    }
+}
+
+// Reads `bytes` (a multiple of 16) starting at p, spread over the block's
+// threads, and folds them into one word so the loads cannot be dropped: a
+// plain (cache-allocating) read that leaves the lines in the memory-side
+// cache for a later kernel.
+__device__ __forceinline__ uint32_t warm_bytes(const uint8_t *p, size_t bytes) {
+    uint32_t acc = 0;
+    for (size_t off = (size_t)threadIdx.x * 16; off < bytes; off += (size_t)blockDim.x * 16) {
+        const u32x4 v = ld16(p + off);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    return acc;
+}
+
+}  // namespace moe

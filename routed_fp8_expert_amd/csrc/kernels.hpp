@@ -16,6 +16,8 @@ struct ExpertSet {
 
 // Per-step bookkeeping written by the grouping kernel, read by the expert
 // kernels (int32 words in the workspace).
+constexpr int kReplicas = 8;   // one copy per XCD (workgroups map to XCDs by index)
+
 enum MetaWord : int {
     kMetaGemvCount = 0,   // routed experts on the GEMV arm
     kMetaMfmaCount = 1,   // routed experts on the MFMA arm
@@ -33,8 +35,8 @@ struct RouteArgs {
     int32_t *counts, *offsets, *perm;   // grouping (R >= 2)
     int32_t *meta, *gemv_list, *mfma_list, *mfma_tiles;
     int mfma_min_rows;          // experts with count >= this go to the MFMA arm (0 = never)
-    unsigned *counter;          // ctx word for the router's last-block top-k
     uint32_t *err;
+    unsigned *ticket;           // ctx word: router workgroups done (one-row lead kernel)
 };
 
 struct FfnArgs {
@@ -50,16 +52,26 @@ struct FfnArgs {
     uint32_t *err;
     int max_routed_tasks;       // grid bound on routed experts for R >= 2
     int mfma_max_tiles;         // grid bound on MFMA row tiles
+    uint32_t *sink;             // word the cache-warming reads fold into
+    // single-launch one-row layer: per-XCD replicas of values crossing workgroups
+    float *logits_rep;          // [kReplicas][E]
+    float *h_rep;               // [kReplicas][k+1][hstride]
 };
 
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
-hipError_t launch_router(const RouteArgs &a, bool fuse_topk, hipStream_t st);
+hipError_t launch_router(const RouteArgs &a, hipStream_t st);
 hipError_t launch_topk(const RouteArgs &a, bool compute_s, hipStream_t st);
 hipError_t launch_group(const RouteArgs &a, bool plan, hipStream_t st);
 hipError_t launch_plan(const RouteArgs &a, hipStream_t st);
 size_t group_lds_bytes(int E, int R);
 
 hipError_t launch_gate_up(const FfnArgs &a, hipStream_t st);
+// One-row layer: router rows + shared expert, then top-k + routed gate/up.
+hipError_t launch_lead_r1(const RouteArgs &r, const FfnArgs &a, hipStream_t st);
+hipError_t launch_gate_up_r1(const FfnArgs &a, hipStream_t st);
+// One-row layer in a single launch (layer.hip); `sync` = 27 lines of 64 ctx words.
+bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a);
+hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync, hipStream_t st);
 hipError_t launch_down_blend_r1(const FfnArgs &a, hipStream_t st);
 hipError_t launch_down_grouped(const FfnArgs &a, hipStream_t st);
 hipError_t launch_blend(const FfnArgs &a, hipStream_t st);

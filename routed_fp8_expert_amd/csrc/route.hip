@@ -8,152 +8,53 @@
 // 1992, "What it is": the shared expert's gate.  The grouping serves the
 // multi-row plan arms ("Plan arms": multi_seq rows 2..64) so that each
 // touched expert's weights are read once per step.
-#include "device.hpp"
-#include "kernels.hpp"
-
-#include <math.h>
+#include "gemv.hpp"
 
 namespace moe {
 
-constexpr int kMaxTopkPerLane = 16;   // E <= 1024
-
-__device__ __forceinline__ void st_agent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Softmax over E logits, the k largest (value descending, lower index first
-// on equal values), and their renormalised weights, by one wave.  The
-// weights are exp(l_j - m) / sum_j exp(l_j - m): the softmax denominator over
-// all E cancels in the renormalisation.  `coherent` reads the logits with
-// agent-scope loads (they were written by other workgroups of this launch).
-__device__ void topk_row(const float *l, int E, int k, int32_t *ids, float *w, bool coherent) {
-    const int lane = threadIdx.x & (kWave - 1);
-    float v[kMaxTopkPerLane];
-    uint32_t taken = 0;
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kMaxTopkPerLane; ++i) {
-        const int e = lane + kWave * i;
-        float t = -INFINITY;
-        if (e < E) {
-            t = coherent ? ld_agent(l + e) : l[e];
-            if (t != t) t = -INFINITY;
-        } else {
-            taken |= 1u << i;
-        }
-        v[i] = t;
-        m = fmaxf(m, t);
-    }
-    m = wave_max(m);
-    float my_v = 0.0f;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kMaxTopkPerLane; ++i) {
-            const int e = lane + kWave * i;
-            if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-                bv = v[i];
-                be = e;
-            }
-        }
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, kWave);
-            const int oe = __shfl_xor(be, o, kWave);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if (be < E && (be & (kWave - 1)) == lane) taken |= 1u << (be >> 6);
-        if (lane == j) {
-            my_v = bv;
-            my_e = be < E ? be : 0;
-        }
-    }
-    const float ex = lane < k ? expf(my_v - m) : 0.0f;
-    const float sum = group_sum<kWave>(ex);
-    if (lane < k) {
-        ids[lane] = my_e;
-        w[lane] = ex / sum;
-    }
-}
-
-// x . v over H bf16 elements by one wave (16-byte chunks, lane-strided).
-__device__ __forceinline__ float wave_dot_bf16(const uint16_t *a, const uint16_t *b, int H) {
-    const int lane = threadIdx.x & (kWave - 1);
-    float acc = 0.0f;
-    for (int c = lane; c < (H >> 3); c += kWave) acc = dot8_bf16(ld16(a + c * 8), ld16(b + c * 8), acc);
-    return group_sum<kWave>(acc);
-}
-
-__device__ __forceinline__ float sigmoid(float t) { return 1.0f / (1.0f + expf(-t)); }
-
-// Router GEMV: one wave per router row (row E is the shared-gate vector).
-// The row stays in registers while the wave walks the R activation rows.
-// With `fuse_topk`, the last workgroup to finish runs the top-k for every
-// row (a ticket counter in the ctx, reset by that workgroup).
+// Router GEMV: one wave per router row (row E is the shared-gate vector); the
+// row stays in registers while the wave walks the R activation rows.
 template <int NCH>
-__global__ __launch_bounds__(64) void k_router(RouteArgs a, int fuse_topk, int s_mode) {
-    const int lane = threadIdx.x;
-    const int row = blockIdx.x;
-    const int nch = a.H >> 3;
-    const uint16_t *wrow = row < a.E ? a.wr + (size_t)row * a.H : a.wsg;
+__global__ __launch_bounds__(256) void k_router(RouteArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.E + (a.wsg ? 1 : 0)) return;
     u32x4 wv[NCH];
-#pragma unroll
-    for (int t = 0; t < NCH; ++t) {
-        const int c = lane + kWave * t;
-        wv[t] = c < nch ? ld16_stream(wrow + (size_t)c * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    load_bf16_row<NCH>(row < a.E ? a.wr + (size_t)row * a.H : a.wsg, a.H, wv);
     const float bias = (row < a.E && a.bias) ? a.bias[row] : 0.0f;
     for (int r = 0; r < a.R; ++r) {
-        const uint16_t *xr = a.x + (size_t)r * a.ldx;
-        float acc = 0.0f;
-#pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-            const int c = lane + kWave * t;
-            if (c < nch) acc = dot8_bf16(wv[t], ld16(xr + (size_t)c * 8), acc);
-        }
-        acc = group_sum<kWave>(acc);
+        const float acc = dot_bf16_row<NCH>(wv, a.x + (size_t)r * a.ldx, a.H);
         if (lane == 0) {
             if (row < a.E)
-                st_agent(a.logits + (size_t)r * a.E + row, acc + bias);
+                a.logits[(size_t)r * a.E + row] = acc + bias;
             else
-                st_agent(a.s + r, sigmoid(acc));
+                a.s[r] = sigmoid(acc);
         }
     }
-    if (!fuse_topk) return;
-    __threadfence();
-    unsigned ticket = 0;
-    if (lane == 0)
-        ticket = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    ticket = __shfl(ticket, 0, kWave);
-    if (ticket != gridDim.x - 1) return;
-    __threadfence();
-    for (int r = 0; r < a.R; ++r) {
-        topk_row(a.logits + (size_t)r * a.E, a.E, a.k, a.ids + (size_t)r * a.k,
-                 a.w + (size_t)r * a.k, true);
-        if (s_mode == 2 && lane == 0) a.s[r] = 1.0f;
-    }
-    if (lane == 0) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Top-k from logits (given, or written by an earlier router launch): one
-// wave per row.  s_mode 1 computes the shared gate here, 2 writes s = 1.
+// Top-k from logits (given, or written by the router launch): one wave per
+// row.  s_mode 1 also computes the shared gate here, 2 writes s = 1.
+template <int NV>
 __global__ __launch_bounds__(256) void k_topk(RouteArgs a, int s_mode) {
+    const int lane = threadIdx.x & (kWave - 1);
     const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= a.R) return;
     const float *l = a.logits_in ? a.logits_in + (size_t)r * a.E : a.logits + (size_t)r * a.E;
-    topk_row(l, a.E, a.k, a.ids + (size_t)r * a.k, a.w + (size_t)r * a.k, false);
+    int e;
+    float w;
+    topk_wave<NV>(l, a.E, a.k, false, e, w);
+    if (lane < a.k) {
+        a.ids[(size_t)r * a.k + lane] = e;
+        a.w[(size_t)r * a.k + lane] = w;
+    }
     if (s_mode == 1) {
-        const float d = wave_dot_bf16(a.x + (size_t)r * a.ldx, a.wsg, a.H);
-        if ((threadIdx.x & 63) == 0) a.s[r] = sigmoid(d);
-    } else if (s_mode == 2 && (threadIdx.x & 63) == 0) {
+        constexpr int NCH = 16;
+        u32x4 wv[NCH];
+        load_bf16_row<NCH>(a.wsg, a.H, wv);
+        const float d = dot_bf16_row<NCH>(wv, a.x + (size_t)r * a.ldx, a.H);
+        if (lane == 0) a.s[r] = sigmoid(d);
+    } else if (s_mode == 2 && lane == 0) {
         a.s[r] = 1.0f;
     }
 }
@@ -280,27 +181,33 @@ __global__ __launch_bounds__(1024) void k_group(RouteArgs a, int do_plan) {
 
 size_t group_lds_bytes(int E, int R) { return (size_t)E * (size_t)((R + 31) / 32) * 4u; }
 
-hipError_t launch_router(const RouteArgs &a, bool fuse_topk, hipStream_t st) {
+hipError_t launch_router(const RouteArgs &a, hipStream_t st) {
     const int nch = ((a.H >> 3) + kWave - 1) / kWave;
     const int rows = a.E + (a.wsg ? 1 : 0);
-    const int s_mode = a.wsg ? 0 : 2;
-    dim3 grid(rows), block(64);
+    dim3 grid((rows + 3) / 4), block(256);
     if (nch <= 1)
-        hipLaunchKernelGGL(k_router<1>, grid, block, 0, st, a, (int)fuse_topk, s_mode);
+        hipLaunchKernelGGL(k_router<1>, grid, block, 0, st, a);
     else if (nch <= 2)
-        hipLaunchKernelGGL(k_router<2>, grid, block, 0, st, a, (int)fuse_topk, s_mode);
+        hipLaunchKernelGGL(k_router<2>, grid, block, 0, st, a);
     else if (nch <= 4)
-        hipLaunchKernelGGL(k_router<4>, grid, block, 0, st, a, (int)fuse_topk, s_mode);
+        hipLaunchKernelGGL(k_router<4>, grid, block, 0, st, a);
     else if (nch <= 8)
-        hipLaunchKernelGGL(k_router<8>, grid, block, 0, st, a, (int)fuse_topk, s_mode);
+        hipLaunchKernelGGL(k_router<8>, grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL(k_router<16>, grid, block, 0, st, a, (int)fuse_topk, s_mode);
+        hipLaunchKernelGGL(k_router<16>, grid, block, 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const RouteArgs &a, bool compute_s, hipStream_t st) {
     const int s_mode = a.wsg ? (compute_s ? 1 : 0) : 2;
-    hipLaunchKernelGGL(k_topk, dim3((a.R + 3) / 4), dim3(256), 0, st, a, s_mode);
+    dim3 grid((a.R + 3) / 4), block(256);
+    switch (topk_nv(a.E)) {
+        case 1: hipLaunchKernelGGL(k_topk<1>, grid, block, 0, st, a, s_mode); break;
+        case 2: hipLaunchKernelGGL(k_topk<2>, grid, block, 0, st, a, s_mode); break;
+        case 4: hipLaunchKernelGGL(k_topk<4>, grid, block, 0, st, a, s_mode); break;
+        case 8: hipLaunchKernelGGL(k_topk<8>, grid, block, 0, st, a, s_mode); break;
+        default: hipLaunchKernelGGL(k_topk<16>, grid, block, 0, st, a, s_mode); break;
+    }
     return hipGetLastError();
 }
 

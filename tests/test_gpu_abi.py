@@ -113,13 +113,16 @@ def test_fault_injection_is_sticky(moe, tiny):
 def test_fault_mid_layer_stops_later_launches(moe, tiny):
     wl, W = tiny
     ctx = moe.Ctx(0)
+    moe.moe_ctx_set_one_row_path(ctx, 1)
     lw, x, y, rt, ws = _setup(moe, wl, W, rows=1)
-    moe.moe_ctx_set_fault_at(ctx, 2)          # routing runs, the expert launch is refused
+    # on the three-launch path (router + shared expert, routed gate/up, down +
+    # blend) the third launch is refused, the first two have run
+    moe.moe_ctx_set_fault_at(ctx, 3)
     with pytest.raises(moe.MoeError):
         moe.moe_layer_forward(ctx, lw, x, y, None, ws, routing=rt)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)                 # no output written after the fault
-    assert not torch.all(rt.topk_ids == -7)   # the routing launch before it did run
+    assert not torch.all(rt.topk_ids == -7)   # the launches before it did run
     ctx.close()
 
 
@@ -165,12 +168,30 @@ def test_kernel_timing_counts_launches(moe, tiny):
     wl, W = tiny
     ctx = moe.Ctx(0)
     lw, x, y, rt, ws = _setup(moe, wl, W, rows=1)
+    layer = moe.KERNELS.index("layer")
     moe.moe_ctx_set_timing(ctx, True)
     for _ in range(3):
         moe.moe_layer_forward(ctx, lw, x, y, None, ws, routing=rt)
-    ms, n = moe.moe_ctx_kernel_stats(ctx, 3)
+    ms, n = moe.moe_ctx_kernel_stats(ctx, layer)
     assert n == 3 and ms > 0
-    ms, n = moe.moe_ctx_kernel_stats(ctx, 0)
-    assert n == 3
+    moe.moe_ctx_set_one_row_path(ctx, 1)
+    moe.moe_ctx_set_timing(ctx, True)
+    for _ in range(2):
+        moe.moe_layer_forward(ctx, lw, x, y, None, ws, routing=rt)
+    assert moe.moe_ctx_kernel_stats(ctx, 3)[1] == 2
+    assert moe.moe_ctx_kernel_stats(ctx, 0)[1] == 2
+    assert moe.moe_ctx_kernel_stats(ctx, layer)[1] == 0
     moe.moe_ctx_set_timing(ctx, False)
+    ctx.close()
+
+
+def test_fault_injection_on_single_launch_layer(moe, tiny):
+    wl, W = tiny
+    ctx = moe.Ctx(0)
+    lw, x, y, rt, ws = _setup(moe, wl, W, rows=1)
+    moe.moe_ctx_set_fault_at(ctx, 2)
+    moe.moe_layer_forward(ctx, lw, x, y, None, ws, routing=rt)     # launch 1 runs
+    with pytest.raises(moe.MoeError):
+        moe.moe_layer_forward(ctx, lw, x, y, None, ws, routing=rt)  # launch 2 refused
+    assert moe.moe_ctx_status(ctx) == moe.binding.MOE_ERR_DEVICE_LOST
     ctx.close()

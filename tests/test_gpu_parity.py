@@ -153,6 +153,7 @@ def test_a3b_forty_layers_as_benchmarked(moe, ctx, orc):
         st = check_layer(orc, wl, res.W[n], res.x[n], None, res.residual0[n], res.y[n],
                          res.residual[n], res.routing[n], what=f"a3b L{l}")
         worst = max(worst, st[0])
+    assert moe.moe_ctx_device_errors(ctx) == 0
     _say(f"  40 layers ok, worst max|err|/rms {worst:.2e}")
 
 
@@ -234,6 +235,45 @@ def test_zero_rows_is_a_no_op(moe, ctx):
 def test_max_rows_with_given_logits(moe, ctx, orc):
     wl = syn.WORKLOADS["a3b_multi"]
     _layer(moe, ctx, orc, wl, 0, 1024, sample_rows=[0, 1, 511, 512, 1022, 1023])
+
+
+# ------------------------------------------------------------------ one-row paths
+
+@pytest.mark.parametrize("name,layer", [("tiny", 0), ("a3b", 3), ("a17b", 1)])
+def test_one_row_paths_agree(moe, orc, name, layer):
+    """The single-launch layer and the three-launch path give the same bits,
+    both match the oracle, and no bounded wait timed out."""
+    wl = syn.WORKLOADS[name]
+    W = syn.make_layer_weights(wl, layer, "cuda")
+    x, _ = tie_free_x(orc, wl, W, layer, 1, device="cuda")
+    r0 = syn.make_residual(wl, layer, 1, "cuda")
+    out = []
+    for path in (0, 1):
+        c = moe.Ctx(0)
+        moe.moe_ctx_set_one_row_path(c, path)
+        res = []
+        for _ in range(3):   # repeated calls reuse the ctx's synchronisation words
+            res.append(_run(moe, c, wl, W, x, None, r0))
+        assert moe.moe_ctx_device_errors(c) == 0
+        c.close()
+        for a in res[1:]:
+            assert torch.equal(a[0].view(torch.int16), res[0][0].view(torch.int16))
+        out.append(res[0])
+    (y0, o0, rt0, _), (y1, o1, rt1, _) = out
+    assert torch.equal(rt0.topk_ids, rt1.topk_ids) and torch.equal(rt0.topk_w, rt1.topk_w)
+    assert torch.equal(rt0.shared_gate, rt1.shared_gate)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    check_layer(orc, wl, W, x, None, r0, y0, o0, rt0, what=f"{name} single launch")
+
+
+def test_one_row_with_given_logits(moe, ctx, orc):
+    wl = syn.WORKLOADS["a3b_multi"]
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    x = syn.make_x(wl, 0, 1, 0, "cuda")
+    li = syn.make_logits_in(wl, 0, 1, "cuda")
+    y, res, rt, r0 = _run(moe, ctx, wl, W, x, li)
+    check_layer(orc, wl, W, x, li, r0, y, res, rt, what="one row, given logits")
 
 
 # ------------------------------------------------------------------ properties
