@@ -158,7 +158,9 @@ MOE_API int moe_ctx_status(const moe_ctx *ctx);
  * disables it. */
 MOE_API int moe_ctx_set_fault_at(moe_ctx *ctx, int64_t n);
 /* Rows per expert at and above which (with a step of at least 32 rows) an
- * expert takes the MFMA grouped-GEMM arm; 0 restores the default. */
+ * expert of an fp8 layer takes the MFMA grouped-GEMM arm (default 8); 0
+ * restores the default.  The shared expert takes it when the step has that
+ * many rows.  NVFP4 layers always use the GEMV arm. */
 MOE_API int moe_ctx_set_mfma_min_rows(moe_ctx *ctx, int rows);
 /* Force the arm: 0 = automatic, 1 = GEMV arm only, 2 = MFMA arm for every
  * expert with at least one row (steps of >= 2 rows). */

@@ -23,7 +23,7 @@ namespace {
 // own lines, then the single-launch layer's synchronisation lines.
 enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, kWordLayerSync = 1024,
                       kSyncWords = 1024 + 40 * 64 };
-constexpr int kDefaultMfmaMinRows = 0;   // MFMA arm off until enabled
+constexpr int kDefaultMfmaMinRows = 8;   // rows per expert from which the MFMA arm pays
 constexpr int kMaxRows = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
@@ -261,13 +261,15 @@ int check_ws(const moe_layer_weights *w, int R, const void *ws, size_t ws_bytes)
     return MOE_OK;
 }
 
-bool mfma_enabled(const moe_ctx *c, int R) {
-    if (c->force_arm == 1) return false;
+// The MFMA arm serves fp8 layers in steps of at least 32 rows (any multi-row
+// step when forced), for experts with at least the threshold's rows.
+bool mfma_enabled(const moe_ctx *c, const moe_layer_weights *w, int R) {
+    if (w->weight_format != MOE_WFMT_FP8_E4M3_B128 || c->force_arm == 1) return false;
     if (c->force_arm == 2) return R >= 2;
     return R >= 32 && c->mfma_min_rows > 0;
 }
-int mfma_threshold(const moe_ctx *c, int R) {
-    if (!mfma_enabled(c, R)) return 0;
+int mfma_threshold(const moe_ctx *c, const moe_layer_weights *w, int R) {
+    if (!mfma_enabled(c, w, R)) return 0;
     return c->force_arm == 2 ? 1 : c->mfma_min_rows;
 }
 
@@ -295,7 +297,7 @@ moe::RouteArgs route_args(moe_ctx *c, const moe_layer_weights *w, const void *x,
     a.gemv_list = at<int32_t>(ws, L.gemv);
     a.mfma_list = at<int32_t>(ws, L.mfma);
     a.mfma_tiles = at<int32_t>(ws, L.tiles);
-    a.mfma_min_rows = mfma_threshold(c, R);
+    a.mfma_min_rows = mfma_threshold(c, w, R);
     a.err = c->words + kWordError;
     a.ticket = c->words + kWordRouterTicket;
     return a;
@@ -368,7 +370,14 @@ moe::FfnArgs ffn_args(moe_ctx *c, const moe_layer_weights *w, const void *x, int
     a.logits_rep = at<float>(ws, L.lrep);
     a.h_rep = at<float>(ws, L.hrep);
     a.max_routed_tasks = std::min(w->n_experts, R * w->top_k);
+    const int thr = R >= 2 ? mfma_threshold(c, w, R) : 0;
+    a.shared_mfma = thr > 0 && w->shared_inter > 0 && R >= thr;
     a.mfma_max_tiles = 0;
+    if (thr > 0) {
+        // sum over MFMA experts of ceil(rows/32) <= R*k/32 + (number of such experts)
+        const int rk = R * w->top_k;
+        a.mfma_max_tiles = (rk + 31) / 32 + std::min(w->n_experts, rk / thr) + (a.shared_mfma ? (R + 31) / 32 : 0);
+    }
     return a;
 }
 
@@ -376,9 +385,17 @@ moe::FfnArgs ffn_args(moe_ctx *c, const moe_layer_weights *w, const void *x, int
 int do_ffn(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
     int rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up(a, st); });
     if (rc) return rc;
+    if (a.mfma_max_tiles > 0) {
+        rc = launch(c, MOE_K_MFMA_GATE_UP, st, [&] { return moe::launch_mfma_gate_up(a, st); });
+        if (rc) return rc;
+    }
     if (a.R == 1) return launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
     rc = launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_grouped(a, st); });
     if (rc) return rc;
+    if (a.mfma_max_tiles > 0) {
+        rc = launch(c, MOE_K_MFMA_DOWN, st, [&] { return moe::launch_mfma_down(a, st); });
+        if (rc) return rc;
+    }
     return launch(c, MOE_K_BLEND, st, [&] { return moe::launch_blend(a, st); });
 }
 

@@ -353,7 +353,7 @@ __global__ void k_decode_probe(int fmt, const uint8_t *codes, float *out, int n)
 // ------------------------------------------------------------------ launchers
 
 static int routed_tasks(const FfnArgs &a) { return a.R == 1 ? a.k : a.max_routed_tasks; }
-static int n_tasks(const FfnArgs &a) { return routed_tasks(a) + (a.shared.inter > 0 ? 1 : 0); }
+static int n_tasks(const FfnArgs &a) { return routed_tasks(a) + (a.shared.inter > 0 && !a.shared_mfma ? 1 : 0); }
 static int gate_up_chunks(int fmt, int H) { return ((fmt == kFp8 ? H : H / 2) / 16 + kWave - 1) / kWave; }
 static int max_inter(const FfnArgs &a) { return a.routed.inter > a.shared.inter ? a.routed.inter : a.shared.inter; }
 

@@ -51,7 +51,8 @@ struct FfnArgs {
     uint16_t *y; uint16_t *res; int64_t ldy;
     uint32_t *err;
     int max_routed_tasks;       // grid bound on routed experts for R >= 2
-    int mfma_max_tiles;         // grid bound on MFMA row tiles
+    int mfma_max_tiles;         // grid bound on MFMA row tiles (0 = MFMA arm off)
+    int shared_mfma;            // the shared expert's rows go to the MFMA arm
     uint32_t *sink;             // word the cache-warming reads fold into
     // single-launch one-row layer: per-XCD replicas of values crossing workgroups
     float *logits_rep;          // [kReplicas][E]

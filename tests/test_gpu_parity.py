@@ -237,6 +237,50 @@ def test_max_rows_with_given_logits(moe, ctx, orc):
     _layer(moe, ctx, orc, wl, 0, 1024, sample_rows=[0, 1, 511, 512, 1022, 1023])
 
 
+# ------------------------------------------------------------------ arms
+
+@pytest.mark.parametrize("rows", [2, 5, 33, 64])
+def test_mfma_arm_forced_for_every_expert(moe, ctx, orc, rows):
+    """Every expert with at least one row (and the shared expert) on the
+    matrix-core arm, including tiles with a single valid row."""
+    moe.moe_ctx_set_force_arm(ctx, 2)
+    try:
+        _layer(moe, ctx, orc, syn.WORKLOADS["a3b_multi"], 2, rows)
+        assert moe.moe_ctx_device_errors(ctx) == 0
+    finally:
+        moe.moe_ctx_set_force_arm(ctx, 0)
+
+
+def test_gemv_arm_only_at_64_rows(moe, ctx, orc):
+    moe.moe_ctx_set_force_arm(ctx, 1)
+    try:
+        _layer(moe, ctx, orc, syn.WORKLOADS["a3b_zipf"], 3, 64)
+    finally:
+        moe.moe_ctx_set_force_arm(ctx, 0)
+
+
+def test_mfma_threshold_one_and_large(moe, ctx, orc):
+    wl = syn.WORKLOADS["a3b_zipf"]
+    for thr in (1, 40):
+        moe.moe_ctx_set_mfma_min_rows(ctx, thr)
+        try:
+            _layer(moe, ctx, orc, wl, 4, 64)
+        finally:
+            moe.moe_ctx_set_mfma_min_rows(ctx, 0)
+
+
+def test_determinism_with_mfma_arm(moe, ctx, orc):
+    wl = syn.WORKLOADS["a3b_zipf"]
+    W = syn.make_layer_weights(wl, 5, "cuda")
+    x = syn.make_x(wl, 5, 64, 0, "cuda")
+    li = syn.make_logits_in(wl, 5, 64, "cuda")
+    r0 = syn.make_residual(wl, 5, 64, "cuda")
+    a = _run(moe, ctx, wl, W, x, li, r0)
+    b = _run(moe, ctx, wl, W, x, li, r0)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert moe.moe_ctx_device_errors(ctx) == 0
+
+
 # ------------------------------------------------------------------ one-row paths
 
 @pytest.mark.parametrize("name,layer", [("tiny", 0), ("a3b", 3), ("a17b", 1)])
