@@ -71,15 +71,20 @@ def source_digest() -> str:
 
 def counter_traffic(kernel: str, workload: str, rows: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this kernel and workload, if it was taken on the current sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_r{rows}.json")
+    this kernel and workload (profiles/traffic_<kernel>_<workload>_r<rows>.txt,
+    `key: value` lines), if it was taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_r{rows}.txt")
     if not os.path.exists(path):
         return None
+    kv = {}
     with open(path) as f:
-        d = json.load(f)
-    if d.get("source_digest") != source_digest():
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#")):
+                key, _, val = line.partition(":")
+                kv[key.strip()] = val.strip()
+    if kv.get("source_digest") != source_digest():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return int(kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in kv else None
 
 
 def cpu_baseline(wl, res, budget_s: float):
@@ -223,35 +228,32 @@ def main():
             kernels[name] = {"avg_us": round(ms / n * 1e3, 3), "launches_per_step": n // kt_steps}
     moe.moe_ctx_set_timing(ctx, False)
 
-    # algorithmic bytes per launch of each kernel (rows == 1 layout)
+    # Algorithmic bytes of one layer: the effective weight bytes plus the
+    # activations read (x) and the residual read and written.
     H, E, I, Is, k = wl.hidden, wl.n_experts, wl.inter, wl.shared_inter, wl.top_k
-    if wl.fmt == syn.FMT_FP8_B128:
-        gu_bytes_e = 2 * I * H + 4 * (2 * I // 128) * (H // 128)
-        dn_bytes_e = H * I + 4 * (H // 128) * (I // 128)
-    else:
-        gu_bytes_e = (2 * I * H) // 2 + (2 * I * H) // 16 + 4
-        dn_bytes_e = (H * I) // 2 + (H * I) // 16 + 4
-    u_per_layer = touched / layers
-    algo = {
-        "gate_up": (u_per_layer + (1 if Is else 0)) * gu_bytes_e + rows * H * 2 + (rows * k + rows) * I * 4,
-        "down": (u_per_layer + (1 if Is else 0)) * dn_bytes_e + (rows * k + rows) * I * 4 + 2 * rows * H * 2,
-        "router": (E * H * 2 + H * 2 + rows * H * 2) if router_gemv else 0,
-    }
-    # the dominant kernel: the largest share of the step's kernel time
-    roof_kernel = max(("gate_up", "down"),
-                      key=lambda n: kernels.get(n, {}).get("avg_us", 0) * kernels.get(n, {}).get("launches_per_step", 0))
-    kstat = kernels.get(roof_kernel)
+    act_bytes = rows * H * 2 + 2 * rows * H * 2
+    layer_bytes = eff_bytes / layers + act_bytes
     roofline = None
-    if kstat:
-        achieved = algo[roof_kernel] / (kstat["avg_us"] * 1e-6) / 1e9
-        traffic = counter_traffic(roof_kernel, wl.name, rows)
-        roofline = {"bound": "hbm", "kernel": roof_kernel, "achieved": round(achieved, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": traffic, "algorithmic_bytes_per_launch": int(algo[roof_kernel])}
-    per_kernel_roof = {}
-    for name, st in kernels.items():
-        if name in algo and algo[name]:
-            per_kernel_roof[name] = round(algo[name] / (st["avg_us"] * 1e-6) / 1e9, 1)
+    if "layer" in kernels:
+        # One kernel per layer: it is the dominant (and only) kernel, and its
+        # average launch duration is the timed region (HIP events on the
+        # launch stream) over the launches in it; the per-launch event pairs
+        # of the diagnostic pass add their own overhead and are reported aside.
+        kernels["layer"]["avg_us_timed_region"] = round(us_layer, 3)
+        achieved = layer_bytes / (us_layer * 1e-6) / 1e9
+        traffic = counter_traffic("layer", wl.name, rows)
+        roofline = {"bound": "hbm", "kernel": "layer", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "algorithmic_bytes_per_launch": int(layer_bytes)}
+    elif kernels:
+        # several kernels per layer: the layer's bytes over the sum of its kernels' times
+        us = sum(st["avg_us"] * st["launches_per_step"] for st in kernels.values()) / layers
+        achieved = layer_bytes / (us * 1e-6) / 1e9
+        dominant = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches_per_step"])
+        roofline = {"bound": "hbm", "kernel": "all kernels of a layer (dominant: %s)" % dominant,
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "algorithmic_bytes_per_launch": int(layer_bytes)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -280,7 +282,6 @@ def main():
         "launch_ms_per_step": {m: round(v, 5) for m, v in results.items()},
         "effective_bytes_per_step": int(eff_bytes),
         "kernels": kernels,
-        "kernel_effective_gbs": per_kernel_roof,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "source_digest": source_digest(),
