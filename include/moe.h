@@ -133,11 +133,11 @@ enum moe_kernel_id {
     MOE_K_ROUTER = 0,   /* router GEMV (+ shared gate, + top-k for small R) */
     MOE_K_TOPK = 1,     /* top-k softmax from logits (+ shared gate) */
     MOE_K_GROUP = 2,    /* histogram, scan, ranks, permutation */
-    MOE_K_GATE_UP = 3,  /* gate/up GEMV + silu*mul (routed and shared) */
-    MOE_K_DOWN = 4,     /* down GEMV (R == 1: fused with the blend) */
+    MOE_K_GATE_UP = 3,  /* gate/up + silu*mul (routed and shared; R >= 2: GEMV and matrix-core arms) */
+    MOE_K_DOWN = 4,     /* down (R == 1: fused with the blend; R >= 2: both arms) */
     MOE_K_BLEND = 5,    /* weighted blend + residual (R >= 2) */
-    MOE_K_MFMA_GATE_UP = 6,
-    MOE_K_MFMA_DOWN = 7,
+    MOE_K_MFMA_GATE_UP = 6, /* reserved: the matrix-core arm runs inside MOE_K_GATE_UP */
+    MOE_K_MFMA_DOWN = 7,    /* reserved: the matrix-core arm runs inside MOE_K_DOWN */
     MOE_K_LAYER = 8,    /* a whole one-row layer in one launch */
     MOE_K_COUNT = 9
 };
@@ -158,7 +158,7 @@ MOE_API int moe_ctx_status(const moe_ctx *ctx);
  * disables it. */
 MOE_API int moe_ctx_set_fault_at(moe_ctx *ctx, int64_t n);
 /* Rows per expert at and above which (with a step of at least 32 rows) an
- * expert of an fp8 layer takes the MFMA grouped-GEMM arm (default 8); 0
+ * expert of an fp8 layer takes the MFMA grouped-GEMM arm (default 4); 0
  * restores the default.  The shared expert takes it when the step has that
  * many rows.  NVFP4 layers always use the GEMV arm. */
 MOE_API int moe_ctx_set_mfma_min_rows(moe_ctx *ctx, int rows);

@@ -23,7 +23,7 @@ namespace {
 // own lines, then the single-launch layer's synchronisation lines.
 enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, kWordLayerSync = 1024,
                       kSyncWords = 1024 + 40 * 64 };
-constexpr int kDefaultMfmaMinRows = 8;   // rows per expert from which the MFMA arm pays
+constexpr int kDefaultMfmaMinRows = 4;   // rows per expert from which the MFMA arm pays (measured)
 constexpr int kMaxRows = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
@@ -376,26 +376,20 @@ moe::FfnArgs ffn_args(moe_ctx *c, const moe_layer_weights *w, const void *x, int
     if (thr > 0) {
         // sum over MFMA experts of ceil(rows/32) <= R*k/32 + (number of such experts)
         const int rk = R * w->top_k;
-        a.mfma_max_tiles = (rk + 31) / 32 + std::min(w->n_experts, rk / thr) + (a.shared_mfma ? (R + 31) / 32 : 0);
+        constexpr int T = moe::kMfmaTileRows;
+        a.mfma_max_tiles = (rk + T - 1) / T + std::min(w->n_experts, rk / thr) + (a.shared_mfma ? (R + T - 1) / T : 0);
     }
     return a;
 }
 
-// Experts and blend for routed rows (generic kernels).
+// Experts and blend for routed rows (generic kernels); the matrix-core
+// units run inside the gate/up and down launches.
 int do_ffn(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
     int rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up(a, st); });
     if (rc) return rc;
-    if (a.mfma_max_tiles > 0) {
-        rc = launch(c, MOE_K_MFMA_GATE_UP, st, [&] { return moe::launch_mfma_gate_up(a, st); });
-        if (rc) return rc;
-    }
     if (a.R == 1) return launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
     rc = launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_grouped(a, st); });
     if (rc) return rc;
-    if (a.mfma_max_tiles > 0) {
-        rc = launch(c, MOE_K_MFMA_DOWN, st, [&] { return moe::launch_mfma_down(a, st); });
-        if (rc) return rc;
-    }
     return launch(c, MOE_K_BLEND, st, [&] { return moe::launch_blend(a, st); });
 }
 

@@ -165,25 +165,96 @@ __device__ __forceinline__ float readlane(float v, int lane) {
 }
 __device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
-// Sum over aligned groups of W lanes (W = 8, 16, 32 or 64); every lane of a
-// group ends with the same value, from the same tree in every kernel, so a
-// dot product comes out bit-identical wherever it is computed.
-template <int W>
+// The two results of a lane-swap builtin, as floats.  Each result is copied
+// into a named integer before the bit cast: hipcc miscompiles bit casts of
+// both subscripts inside one expression (it reads element 0 twice).
+template <int M>
+__device__ __forceinline__ void lane_swap(float a, float b, float &ra, float &rb) {
+    static_assert(M == 32 || M == 16, "swap stride");
+    const unsigned ua = __builtin_bit_cast(unsigned, a), ub = __builtin_bit_cast(unsigned, b);
+    unsigned x, y;
+    if constexpr (M == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+        x = r[0];
+        y = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(ua, ub, false, false);
+        x = r[0];
+        y = r[1];
+    }
+    ra = __builtin_bit_cast(float, x);
+    rb = __builtin_bit_cast(float, y);
+}
+
+// One butterfly stage over lane pairs l, l ^ m (m = 32, 16: the gfx950
+// lane-swap instructions; m = 8, 4: row and half-row mirrors, which pair
+// l with the lane whose low 4 or 3 bits are inverted; m = 2, 1: quad
+// permutes).  Every lane adds its partner's value to its own.
+template <int M>
+__device__ __forceinline__ float bfly(float v) {
+    if constexpr (M == 32 || M == 16) {
+        float x, y;
+        lane_swap<M>(v, v, x, y);
+        return x + y;
+    } else {
+        constexpr int CTRL = M == 8 ? kDppMirror : M == 4 ? kDppHalfMirror : M == 2 ? kDppXor2 : kDppXor1;
+        return v + dpp<CTRL>(0.0f, v);
+    }
+}
+
+// Transposing stage over lane pairs l, l ^ m for two values a, b: lanes with
+// bit m clear end with a + a(partner), lanes with it set with b + b(partner).
+// Per kept value this is the same addition bfly<M> makes.
+template <int M>
+__device__ __forceinline__ float bfly_split(float a, float b) {
+    if constexpr (M == 32 || M == 16) {
+        float x, y;
+        lane_swap<M>(a, b, x, y);
+        return x + y;
+    } else {
+        constexpr int CTRL = M == 8 ? kDppMirror : M == 4 ? kDppHalfMirror : M == 2 ? kDppXor2 : kDppXor1;
+        const bool hi = (threadIdx.x & M) != 0;
+        const float keep = hi ? b : a, send = hi ? a : b;
+        return keep + dpp<CTRL>(0.0f, send);
+    }
+}
+
+// Sum over aligned groups of W lanes (W = 8, 16, 32 or 64) by butterfly
+// stages from stride W/2 down to 1; every lane of a group ends with the same
+// value, and the addition tree is the one xreduce uses, so a dot product
+// comes out bit-identical wherever it is computed.
+template <int W, int M = W / 2>
 __device__ __forceinline__ float group_sum(float v) {
     static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
-    v += dpp<kDppXor1>(0.0f, v);
-    v += dpp<kDppXor2>(0.0f, v);
-    v += dpp<kDppHalfMirror>(0.0f, v);
-    if (W == 8) return v;
-    v += dpp<kDppMirror>(0.0f, v);
-    if (W == 16) return v;
-    v += dpp<kDppBcast15, 0xa>(0.0f, v);   // rows 1 and 3 now hold 32-lane sums
-    if (W == 32) {
-        const float lo = readlane(v, 31), hi = readlane(v, 63);
-        return (threadIdx.x & 32) ? hi : lo;
+    if constexpr (M == 0) {
+        return v;
+    } else {
+        return group_sum<W, M / 2>(bfly<M>(v));
     }
-    v += dpp<kDppBcast31, 0xc>(0.0f, v);   // row 3 holds the wave sum
-    return readlane(v, 63);
+}
+
+// Reduce NU units of U values each over aligned groups of W lanes at once:
+// the first log2(NU) stages transpose (each halves the units a lane keeps),
+// the rest are plain butterflies.  On return v[0 .. U-1] hold unit
+// (lane % W) / (W / NU), summed over the group, with the same bits
+// group_sum would give for that value alone.
+template <int W, int NU, int U, int M = W / 2>
+__device__ __forceinline__ void xreduce(float *v) {
+    static_assert(NU >= 1 && NU <= W, "units");
+    if constexpr (M == 0) {
+        return;
+    } else if constexpr (NU > 1) {
+        constexpr int H = NU / 2;
+#pragma unroll
+        for (int u = 0; u < H; ++u)
+#pragma unroll
+            for (int e = 0; e < U; ++e) v[u * U + e] = bfly_split<M>(v[u * U + e], v[(u + H) * U + e]);
+        xreduce<W, H, U, M / 2>(v);
+    } else {
+#pragma unroll
+        for (int e = 0; e < U; ++e) v[e] = bfly<M>(v[e]);
+        xreduce<W, 1, U, M / 2>(v);
+    }
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -20,7 +20,7 @@
 //            a routed expert's gate/up; warms that expert's down rows
 //   down     each row group streams row o of all k+1 down matrices, stages h
 //            in LDS, and blends in slot order into the residual
-#include "gemv.hpp"
+#include "mfma.hpp"
 
 namespace moe {
 
@@ -32,7 +32,7 @@ constexpr int kWarmLoads = 4;            // 16-byte warming loads per thread (16
 // R >= 2: task u < max_routed_tasks is the u-th GEMV-arm expert (its rows
 // from the grouping), the last task the shared expert over all R rows.
 struct Task {
-    const ExpertSet *X;
+    ExpertSet X;           // the expert family (a copy: no pointer into the kernel arguments)
     int e;                 // expert index within its family
     int n;                 // number of entries
     const int32_t *list;   // entry list (routed, R >= 2) or null
@@ -41,7 +41,7 @@ struct Task {
 };
 
 __device__ __forceinline__ Task resolve_task(const FfnArgs &a, int task) {
-    Task t{&a.routed, 0, 0, nullptr, 0, false};
+    Task t{a.routed, 0, 0, nullptr, 0, false};
     const int nk = a.R * a.k;
     if (a.R == 1) {
         if (task < a.k) {
@@ -51,7 +51,7 @@ __device__ __forceinline__ Task resolve_task(const FfnArgs &a, int task) {
             t.valid = t.e >= 0 && t.e < a.E;
             if (!t.valid) flag_error(a.err, kErrBadExpertId);
         } else {
-            t.X = &a.shared;
+            t.X = a.shared;
             t.n = 1;
             t.first = nk;
             t.valid = a.shared.inter > 0;
@@ -74,7 +74,7 @@ __device__ __forceinline__ Task resolve_task(const FfnArgs &a, int task) {
             t.list = a.perm + off;
         }
     } else {
-        t.X = &a.shared;
+        t.X = a.shared;
         t.n = a.R;
         t.first = nk;
         t.valid = a.shared.inter > 0;
@@ -121,27 +121,61 @@ __device__ __forceinline__ void sink_word(uint32_t *sink, uint32_t acc) {
 // ------------------------------------------------------------------ generic gate/up
 
 // gate/up GEMV + silu*mul for the task's rows.  Block = 4 waves; a wave owns
-// P (gate, up) row pairs of one expert in registers and walks the activation
-// rows of the task.
-template <int FMT, int CH>
-__global__ __launch_bounds__(256) void k_gate_up(FfnArgs a) {
-    const int wid = threadIdx.x >> 6;
-    const Task t = resolve_task(a, blockIdx.y);
+// PM (gate, up) row pairs of one expert in registers and walks the task's
+// entries, loading the next entry's activation chunks before reducing the
+// current one.
+template <int FMT, int CH, int PM>
+__device__ __forceinline__ void gate_up_gemv_unit(const FfnArgs &a, int bx, int task) {
+    constexpr int XQ = x_quads<FMT>();
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+    const Task t = resolve_task(a, task);
     if (!t.valid || t.n == 0) return;
-    const ExpertSet &X = *t.X;
-    const int i0 = (blockIdx.x * 4 + wid) * P;
+    const ExpertSet &X = t.X;
+    const int i0 = (bx * 4 + wid) * PM;
     if (i0 >= X.inter) return;
-    GateUpRows<FMT, CH, P> rows;
+    using Rows = GateUpRows<FMT, CH, PM>;
+    Rows rows;
     rows.load(X, t.e, i0, a.H);
-    for (int n = 0; n < t.n; ++n) {
-        const int entry = task_entry(t, n, a.R * a.k);
-        if (entry < 0) {
-            flag_error(a.err, kErrBadExpertId);
-            continue;
+    const int nk = a.R * a.k;
+    u32x4 xc[CH][XQ], xn[CH][XQ];
+    for (int n0 = 0; n0 < t.n; n0 += kWave) {
+        const int cnt = min(kWave, t.n - n0);
+        const int mine = lane < cnt ? task_entry(t, n0 + lane, nk) : -1;
+        int ec = readlane(mine, 0);
+        if (ec >= 0) Rows::load_x(a.x + (size_t)entry_row(a, ec) * a.ldx, a.H, xc);
+        for (int j = 0; j < cnt; ++j) {
+            const int en = j + 1 < cnt ? readlane(mine, j + 1) : -1;
+            if (en >= 0) Rows::load_x(a.x + (size_t)entry_row(a, en) * a.ldx, a.H, xn);
+            if (ec < 0) {
+                flag_error(a.err, kErrBadExpertId);
+            } else {
+                float acc[2 * PM];
+                rows.partial(xc, a.H, acc);
+                rows.finish(acc, X.inter, i0, a.h + (size_t)ec * a.hstride);
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+#pragma unroll
+                for (int q = 0; q < XQ; ++q) xc[c][q] = xn[c][q];
+            ec = en;
         }
-        rows.apply(a.x + (size_t)entry_row(a, entry) * a.ldx, a.H, X.inter, i0,
-                   a.h + (size_t)entry * a.hstride);
     }
+}
+
+// gate/up of a step, both arms in one launch: workgroups [0, nm) are
+// matrix-core units (column group b % nmx of tile b / nmx, fp8 only), the
+// rest GEMV units (slice b % gx of task b / gx).
+template <int FMT, int CH, int PM>
+__global__ __launch_bounds__(256) void k_gate_up(FfnArgs a, int nmx, int nm, int gx) {
+    int b = blockIdx.x;
+    if constexpr (FMT == kFp8) {
+        if (b < nm) {
+            mfma_gate_up_unit(a, b % nmx, b / nmx);
+            return;
+        }
+    }
+    b -= nm;
+    gate_up_gemv_unit<FMT, CH, PM>(a, b % gx, b / gx);
 }
 
 // ------------------------------------------------------------------ one-row fused kernels
@@ -279,27 +313,68 @@ __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
     if (live && sub == 0) store_out(a.y, a.res, a.ldy, 0, o, y);
 }
 
-// Down GEMV for one expert of a multi-row step: a row group keeps row o of
-// the expert in registers and writes dbuf[entry][o] for each of its rows.
-template <int FMT, int LPR, int CH>
-__global__ __launch_bounds__(256) void k_down_grouped(FfnArgs a) {
-    constexpr int RPW = kWave / LPR;
+// Down GEMV for one expert of a multi-row step.  A row group of LPR lanes
+// keeps RPL consecutive rows of the expert's down matrix in registers; per
+// entry it loads the lane's h chunks once (the next entry's while reducing
+// the current one), forms the RPL partial sums and reduces them together,
+// row i ending in the group's lanes [i * LPR/RPL, (i+1) * LPR/RPL).
+template <int FMT, int LPR, int CH, int RPL>
+__device__ __forceinline__ void down_gemv_unit(const FfnArgs &a, int bx, int task) {
+    constexpr int G = kWave / LPR, HQ = h_quads<FMT>(), SPAN = LPR / RPL;
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-    const Task t = resolve_task(a, blockIdx.y);
+    const Task t = resolve_task(a, task);
     if (!t.valid || t.n == 0) return;
-    const ExpertSet &X = *t.X;
+    const ExpertSet &X = t.X;
+    const int wave_row0 = (bx * 4 + wid) * G * RPL;
+    if (wave_row0 >= a.H) return;
     const int sub = lane % LPR;
-    const int o = (blockIdx.x * 4 + wid) * RPW + lane / LPR;
-    const bool live = o < a.H;
-    DownRow<FMT, LPR, CH> row;
-    row.load(X, t.e, o, sub, live);
+    const int o0 = wave_row0 + (lane / LPR) * RPL;
+    using Row = DownRow<FMT, LPR, CH>;
+    Row rows[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) rows[i].load(X, t.e, o0 + i, sub, o0 + i < a.H);
     const float g = global_scale<FMT>(X.dn_g, t.e);
-    for (int n = 0; n < t.n; ++n) {
-        const int entry = task_entry(t, n, a.R * a.k);
-        if (entry < 0) continue;
-        const float d = row.dot(a.h + (size_t)entry * a.hstride, X.inter, sub) * g;
-        if (live && sub == 0) a.dbuf[(size_t)entry * a.H + o] = d;
+    const int orow = o0 + sub / SPAN;
+    const bool writer = sub % SPAN == 0 && orow < a.H;
+    const int nk = a.R * a.k;
+    f32x4 hc[CH][HQ], hn[CH][HQ];
+    for (int n0 = 0; n0 < t.n; n0 += kWave) {
+        const int cnt = min(kWave, t.n - n0);
+        const int mine = lane < cnt ? task_entry(t, n0 + lane, nk) : -1;
+        int ec = readlane(mine, 0);
+        if (ec >= 0) Row::load_h(a.h + (size_t)ec * a.hstride, X.inter, sub, hc);
+        for (int j = 0; j < cnt; ++j) {
+            const int en = j + 1 < cnt ? readlane(mine, j + 1) : -1;
+            if (en >= 0) Row::load_h(a.h + (size_t)en * a.hstride, X.inter, sub, hn);
+            if (ec >= 0) {
+                float v[RPL];
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) v[i] = rows[i].partial(hc, X.inter, sub);
+                xreduce<LPR, RPL, 1>(v);
+                if (writer) a.dbuf[(size_t)ec * a.H + orow] = v[0] * g;
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+#pragma unroll
+                for (int q = 0; q < HQ; ++q) hc[c][q] = hn[c][q];
+            ec = en;
+        }
     }
+}
+
+// Down projection of a multi-row step, both arms in one launch (the layout
+// of k_gate_up): matrix-core units first, then GEMV units.
+template <int FMT, int LPR, int CH, int RPL>
+__global__ __launch_bounds__(256) void k_down_grouped(FfnArgs a, int nmx, int nm, int gx) {
+    int b = blockIdx.x;
+    if constexpr (FMT == kFp8) {
+        if (b < nm) {
+            mfma_down_unit(a, b % nmx, b / nmx);
+            return;
+        }
+    }
+    b -= nm;
+    down_gemv_unit<FMT, LPR, CH, RPL>(a, b % gx, b / gx);
 }
 
 // Blend for multi-row steps: y[r][o] = sum_j w[r][j] dbuf[r*k+j][o] (slot
@@ -368,8 +443,21 @@ static int max_inter(const FfnArgs &a) { return a.routed.inter > a.shared.inter 
 
 template <int FMT>
 static hipError_t gate_up_fmt(const FfnArgs &a, hipStream_t st) {
-    dim3 grid((max_inter(a) + 4 * P - 1) / (4 * P), n_tasks(a)), block(256);
-    MOE_CH_DISPATCH(gate_up_chunks(FMT, a.H), hipLaunchKernelGGL((k_gate_up<FMT, CH>), grid, block, 0, st, a));
+    const int ch = gate_up_chunks(FMT, a.H);
+    const int pm = ch <= 2 ? 4 : P;        // 4 pairs per wave while the registers allow
+    const int gx = (max_inter(a) + 4 * pm - 1) / (4 * pm);
+    const int nmx = mfma_gate_up_groups(max_inter(a));
+    const int nm = FMT == kFp8 && a.mfma_max_tiles > 0 ? nmx * a.mfma_max_tiles : 0;
+    const long long nb = nm + (long long)gx * n_tasks(a);
+    if (nb == 0) return hipSuccess;
+    dim3 grid((unsigned)nb), block(256);
+    if (pm == 4) {
+        if (ch <= 1) hipLaunchKernelGGL((k_gate_up<FMT, 1, 4>), grid, block, 0, st, a, nmx, nm, gx);
+        else hipLaunchKernelGGL((k_gate_up<FMT, 2, 4>), grid, block, 0, st, a, nmx, nm, gx);
+    } else {
+        if (ch <= 4) hipLaunchKernelGGL((k_gate_up<FMT, 4, P>), grid, block, 0, st, a, nmx, nm, gx);
+        else hipLaunchKernelGGL((k_gate_up<FMT, 8, P>), grid, block, 0, st, a, nmx, nm, gx);
+    }
     return hipGetLastError();
 }
 
@@ -457,11 +545,21 @@ static hipError_t down_r1_fmt(const FfnArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, false>), grid, block, 0, st, a);
     });
 }
+// Rows per row group of the grouped down kernel: 8 register rows per lane
+// in all (RPL rows of CH chunks).
+constexpr int down_rpl(int ch) { return ch <= 1 ? 8 : ch <= 2 ? 4 : 2; }
+
 template <int FMT>
 static hipError_t down_grouped_fmt(const FfnArgs &a, hipStream_t st) {
     MOE_DOWN_DISPATCH({
-        dim3 grid((a.H + rows_per_block - 1) / rows_per_block, n_tasks(a)), block(256);
-        hipLaunchKernelGGL((k_down_grouped<FMT, LPR, CH>), grid, block, 0, st, a);
+        constexpr int RPL = down_rpl(CH);
+        const int rows = rows_per_block * RPL;
+        const int gx = (a.H + rows - 1) / rows;
+        const int nmx = mfma_down_groups(a.H);
+        const int nm = FMT == kFp8 && a.mfma_max_tiles > 0 ? nmx * a.mfma_max_tiles : 0;
+        const long long nb = nm + (long long)gx * n_tasks(a);
+        if (nb == 0) return hipSuccess;
+        hipLaunchKernelGGL((k_down_grouped<FMT, LPR, CH, RPL>), dim3((unsigned)nb), dim3(256), 0, st, a, nmx, nm, gx);
     });
 }
 

@@ -173,34 +173,57 @@ __device__ __forceinline__ f32x2 chunk_scale(const uint8_t *s, int row, int cols
     }
 }
 
-// One 16-byte weight chunk . bf16 activations at xp (the chunk's first column).
+// 16-byte loads of activation per weight chunk: bf16 (gate/up) and f32 (down).
+template <int FMT> constexpr int x_quads() { return FMT == kFp8 ? 2 : 4; }
+template <int FMT> constexpr int h_quads() { return FMT == kFp8 ? 4 : 8; }
+
+// One 16-byte weight chunk . the chunk's bf16 activations (in registers).
 template <int FMT>
-__device__ __forceinline__ float chunk_dot_bf16(u32x4 w, f32x2 sc, const uint16_t *xp) {
-    if (FMT == kFp8) {
-        return sc.x * dot16_e4m3_bf16(w, ld16(xp), ld16(xp + 8));
+__device__ __forceinline__ float chunk_dot_bf16(u32x4 w, f32x2 sc, const u32x4 (&x)[x_quads<FMT>()]) {
+    if constexpr (FMT == kFp8) {
+        return sc.x * dot16_e4m3_bf16(w, x[0], x[1]);
     } else {
-        float a = dot8_e2m1_bf16(w.x, ld16(xp), 0.0f);
-        a = dot8_e2m1_bf16(w.y, ld16(xp + 8), a);
-        float b = dot8_e2m1_bf16(w.z, ld16(xp + 16), 0.0f);
-        b = dot8_e2m1_bf16(w.w, ld16(xp + 24), b);
+        float a = dot8_e2m1_bf16(w.x, x[0], 0.0f);
+        a = dot8_e2m1_bf16(w.y, x[1], a);
+        float b = dot8_e2m1_bf16(w.z, x[2], 0.0f);
+        b = dot8_e2m1_bf16(w.w, x[3], b);
         return sc.x * a + sc.y * b;
     }
 }
+template <int FMT>
+__device__ __forceinline__ void load_x_chunk(const uint16_t *xp, u32x4 (&x)[x_quads<FMT>()]) {
+#pragma unroll
+    for (int q = 0; q < x_quads<FMT>(); ++q) x[q] = ld16(xp + 8 * q);
+}
+// ... with the activations at xp (the chunk's first column).
+template <int FMT>
+__device__ __forceinline__ float chunk_dot_bf16(u32x4 w, f32x2 sc, const uint16_t *xp) {
+    u32x4 x[x_quads<FMT>()];
+    load_x_chunk<FMT>(xp, x);
+    return chunk_dot_bf16<FMT>(w, sc, x);
+}
 
-// One 16-byte weight chunk . f32 activations at hp (global or LDS).
+// One 16-byte weight chunk . the chunk's f32 activations (in registers).
+template <int FMT>
+__device__ __forceinline__ float chunk_dot_f32(u32x4 w, f32x2 sc, const f32x4 (&h)[h_quads<FMT>()]) {
+    if constexpr (FMT == kFp8) {
+        return sc.x * dot16_e4m3_f32(w, h);
+    } else {
+        float a = dot8_e2m1_f32(w.x, h[0], h[1], 0.0f);
+        a = dot8_e2m1_f32(w.y, h[2], h[3], a);
+        float b = dot8_e2m1_f32(w.z, h[4], h[5], 0.0f);
+        b = dot8_e2m1_f32(w.w, h[6], h[7], b);
+        return sc.x * a + sc.y * b;
+    }
+}
+// ... with the activations at hp (global or LDS).
 template <int FMT>
 __device__ __forceinline__ float chunk_dot_f32(u32x4 w, f32x2 sc, const float *hp) {
     const f32x4 *h4 = reinterpret_cast<const f32x4 *>(hp);
-    if (FMT == kFp8) {
-        f32x4 hv[4] = {h4[0], h4[1], h4[2], h4[3]};
-        return sc.x * dot16_e4m3_f32(w, hv);
-    } else {
-        float a = dot8_e2m1_f32(w.x, h4[0], h4[1], 0.0f);
-        a = dot8_e2m1_f32(w.y, h4[2], h4[3], a);
-        float b = dot8_e2m1_f32(w.z, h4[4], h4[5], 0.0f);
-        b = dot8_e2m1_f32(w.w, h4[6], h4[7], b);
-        return sc.x * a + sc.y * b;
-    }
+    f32x4 h[h_quads<FMT>()];
+#pragma unroll
+    for (int q = 0; q < h_quads<FMT>(); ++q) h[q] = h4[q];
+    return chunk_dot_f32<FMT>(w, sc, h);
 }
 
 template <int FMT> __device__ __forceinline__ float global_scale(const float *g, int e) {
@@ -213,9 +236,16 @@ template <int FMT> __device__ __forceinline__ float global_scale(const float *g,
 // lane-strided 16-byte chunks per row, with their scales.
 template <int FMT, int CH, int P>
 struct GateUpRows {
+    // fp8: the P gate rows (and the P up rows) sit in one 128-row scale
+    // block (i0 is a multiple of P, which divides 128), so one scale per
+    // chunk serves each half; nvfp4 scales are per row.
+    static constexpr int NS = FMT == kFp8 ? 2 : 2 * P;
+    static_assert(128 % P == 0, "pairs per wave must divide the scale block");
     u32x4 w[2 * P][CH];
-    f32x2 sc[2 * P][CH];
+    f32x2 sc[NS][CH];
     float g;
+
+    __device__ __forceinline__ static constexpr int sidx(int q) { return FMT == kFp8 ? (q & 1) : q; }
 
     __device__ __forceinline__ void load(const ExpertSet &X, int e, int i0, int H) {
         const int lane = threadIdx.x & (kWave - 1);
@@ -235,7 +265,7 @@ struct GateUpRows {
             }
         }
 #pragma unroll
-        for (int q = 0; q < 2 * P; ++q) {
+        for (int q = 0; q < NS; ++q) {
             const int p = q >> 1;
             const int row = (q & 1) ? I + i0 + p : i0 + p;
             const bool live = i0 + p < I;
@@ -248,38 +278,46 @@ struct GateUpRows {
         g = global_scale<FMT>(X.gu_g, e);
     }
 
-    // h[i0 + p] = silu(g) * u for activation row xr.  Plain: lane p writes
-    // pair p.  COHERENT (another workgroup of the same launch reads it): the
-    // value is written at agent scope (write-through) into `nrep` replicas
-    // `rep` floats apart, lane p + P*c writing pair p of replica c.
-    template <bool COHERENT = false>
-    __device__ __forceinline__ void apply(const uint16_t *xr, int H, int I, int i0, float *hrow,
-                                          size_t rep = 0, int nrep = 1) const {
+    // Per-lane partial sums of the 2P rows (gate p at 2p, up p at 2p+1)
+    // against the lane's activation chunks x[c] (chunk lane + 64c).
+    __device__ __forceinline__ void partial(const u32x4 (&x)[CH][x_quads<FMT>()], int H, float (&acc)[2 * P]) const {
         const int lane = threadIdx.x & (kWave - 1), nch = row_bytes<FMT>(H) >> 4;
-        float acc[2 * P];
 #pragma unroll
         for (int q = 0; q < 2 * P; ++q) acc[q] = 0.0f;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int ch = lane + kWave * c;
-            if (ch < nch) {
-                const uint16_t *xp = xr + (size_t)ch * cols_per_chunk<FMT>();
+            if (lane + kWave * c < nch) {
 #pragma unroll
-                for (int q = 0; q < 2 * P; ++q) acc[q] += chunk_dot_bf16<FMT>(w[q][c], sc[q][c], xp);
+                for (int q = 0; q < 2 * P; ++q) acc[q] += chunk_dot_bf16<FMT>(w[q][c], sc[sidx(q)][c], x[c]);
             }
         }
+    }
+
+    // The lane's activation chunks of row xr.
+    __device__ __forceinline__ static void load_x(const uint16_t *xr, int H, u32x4 (&x)[CH][x_quads<FMT>()]) {
+        const int lane = threadIdx.x & (kWave - 1), nch = row_bytes<FMT>(H) >> 4;
 #pragma unroll
-        for (int q = 0; q < 2 * P; ++q) acc[q] = group_sum<kWave>(acc[q]);
-        const int p = lane % P, copy = lane / P;
-        float gv = acc[0], uv = acc[1];
-#pragma unroll
-        for (int pp = 1; pp < P; ++pp)
-            if (p == pp) {
-                gv = acc[2 * pp];
-                uv = acc[2 * pp + 1];
-            }
+        for (int c = 0; c < CH; ++c) {
+            const int ch = lane + kWave * c;
+            if (ch < nch) load_x_chunk<FMT>(xr + (size_t)ch * cols_per_chunk<FMT>(), x[c]);
+        }
+    }
+
+    // Reduce the partials over the wave (pair p ends in lanes
+    // [p * 64/P, (p+1) * 64/P)) and write h[i0 + p] = silu(g) * u.  Plain:
+    // the first lane of the pair's span writes.  COHERENT (another workgroup
+    // of the same launch reads it): the value is written at agent scope
+    // (write-through) into `nrep` replicas `rep` floats apart, lane c of the
+    // span writing replica c.
+    template <bool COHERENT = false>
+    __device__ __forceinline__ void finish(float (&acc)[2 * P], int I, int i0, float *hrow, size_t rep = 0,
+                                           int nrep = 1) const {
+        constexpr int SPAN = kWave / P;
+        const int lane = threadIdx.x & (kWave - 1);
+        xreduce<kWave, P, 2>(acc);
+        const int p = lane / SPAN, copy = lane % SPAN;
         if (i0 + p >= I) return;
-        const float hv = silu_mul(gv * g, uv * g);
+        const float hv = silu_mul(acc[0] * g, acc[1] * g);
         if (COHERENT) {
             if (copy < nrep)
                 __hip_atomic_store(hrow + (size_t)copy * rep + i0 + p, hv, __ATOMIC_RELAXED,
@@ -287,6 +325,17 @@ struct GateUpRows {
         } else if (copy == 0) {
             hrow[i0 + p] = hv;
         }
+    }
+
+    // h[i0 + p] = silu(g) * u for activation row xr.
+    template <bool COHERENT = false>
+    __device__ __forceinline__ void apply(const uint16_t *xr, int H, int I, int i0, float *hrow,
+                                          size_t rep = 0, int nrep = 1) const {
+        u32x4 x[CH][x_quads<FMT>()];
+        load_x(xr, H, x);
+        float acc[2 * P];
+        partial(x, H, acc);
+        finish<COHERENT>(acc, I, i0, hrow, rep, nrep);
     }
 };
 
@@ -315,17 +364,36 @@ struct DownRow {
         }
     }
 
-    // d = row . h (h: the expert's f32 intermediate, global or LDS), reduced
-    // over the row group; every lane of the group gets it.
-    __device__ __forceinline__ float dot(const float *h, int inter, int sub) const {
+    // Per-lane partial sum against the lane's h chunks hq[c] (chunk sub + LPR c).
+    __device__ __forceinline__ float partial(const f32x4 (&hq)[CH][h_quads<FMT>()], int inter, int sub) const {
         const int nch = row_bytes<FMT>(inter) >> 4;
         float acc = 0.0f;
 #pragma unroll
+        for (int c = 0; c < CH; ++c)
+            if (sub + LPR * c < nch) acc += chunk_dot_f32<FMT>(w[c], sc[c], hq[c]);
+        return acc;
+    }
+
+    // The lane's h chunks of h (global or LDS, plain layout).
+    __device__ __forceinline__ static void load_h(const float *h, int inter, int sub, f32x4 (&hq)[CH][h_quads<FMT>()]) {
+        const int nch = row_bytes<FMT>(inter) >> 4;
+#pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int ch = sub + LPR * c;
-            if (ch < nch) acc += chunk_dot_f32<FMT>(w[c], sc[c], h + (size_t)ch * cols_per_chunk<FMT>());
+            if (ch < nch) {
+                const f32x4 *h4 = reinterpret_cast<const f32x4 *>(h + (size_t)ch * cols_per_chunk<FMT>());
+#pragma unroll
+                for (int q = 0; q < h_quads<FMT>(); ++q) hq[c][q] = h4[q];
+            }
         }
-        return group_sum<LPR>(acc);
+    }
+
+    // d = row . h (h: the expert's f32 intermediate, global or LDS), reduced
+    // over the row group; every lane of the group gets it.
+    __device__ __forceinline__ float dot(const float *h, int inter, int sub) const {
+        f32x4 hq[CH][h_quads<FMT>()];
+        load_h(h, inter, sub, hq);
+        return group_sum<LPR>(partial(hq, inter, sub));
     }
 
     // The same dot product over h held in LDS in chunk-quad order (quad q of
@@ -335,19 +403,17 @@ struct DownRow {
         constexpr int CPC = cols_per_chunk<FMT>();
         const int nch = row_bytes<FMT>(inter) >> 4;
         const int nct = inter / CPC;
-        float acc = 0.0f;
+        f32x4 hq[CH][h_quads<FMT>()];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int ch = sub + LPR * c;
             if (ch < nch) {
-                f32x4 hq[CPC / 4];
 #pragma unroll
-                for (int q = 0; q < CPC / 4; ++q)
-                    hq[q] = *reinterpret_cast<const f32x4 *>(hl + ((size_t)q * nct + ch) * 4);
-                acc += chunk_dot_f32<FMT>(w[c], sc[c], reinterpret_cast<const float *>(hq));
+                for (int q = 0; q < h_quads<FMT>(); ++q)
+                    hq[c][q] = *reinterpret_cast<const f32x4 *>(hl + ((size_t)q * nct + ch) * 4);
             }
         }
-        return group_sum<LPR>(acc);
+        return group_sum<LPR>(partial(hq, inter, sub));
     }
 };
 

@@ -17,6 +17,7 @@ struct ExpertSet {
 // Per-step bookkeeping written by the grouping kernel, read by the expert
 // kernels (int32 words in the workspace).
 constexpr int kReplicas = 8;   // one copy per XCD (workgroups map to XCDs by index)
+constexpr int kMfmaTileRows = 16;   // rows of an expert per matrix-core tile
 
 enum MetaWord : int {
     kMetaGemvCount = 0,   // routed experts on the GEMV arm
@@ -76,8 +77,6 @@ hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync,
 hipError_t launch_down_blend_r1(const FfnArgs &a, hipStream_t st);
 hipError_t launch_down_grouped(const FfnArgs &a, hipStream_t st);
 hipError_t launch_blend(const FfnArgs &a, hipStream_t st);
-hipError_t launch_mfma_gate_up(const FfnArgs &a, hipStream_t st);
-hipError_t launch_mfma_down(const FfnArgs &a, hipStream_t st);
 
 // Diagnostics: decode n codes with the kernels' own converters.
 hipError_t launch_decode_probe(int fmt, const uint8_t *codes, float *out, int n, hipStream_t st);

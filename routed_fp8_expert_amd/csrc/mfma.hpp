@@ -1,0 +1,290 @@
+// mfma.hpp -- the grouped-GEMM arm on gfx950 matrix cores, for experts that
+// receive many rows in a multi-row step (the same arithmetic as the GEMV arm).
+//
+// GB10 blueprint for Qwen3.6-35B-A3B-FP8, "Kernels": w8a16_gemm_pipelined_m32
+// (fp8 block-128 weights times bf16 activations on tensor cores), and "Plan
+// arms": the plan changes shape at the larger multi-row arms.  Here the fp8
+// codes are converted exactly to bf16 and fed to v_mfma_f32_16x16x32_bf16
+// with f32 accumulation; the block scale (one per 128x128 block) multiplies a
+// per-K-block partial sum.  The down projection's f32 intermediate h enters
+// as a bf16 pair hi + lo (hi = bf16(h), lo = bf16(h - hi)), two MFMAs, so h
+// keeps about 16 significant bits.
+//
+// Work unit: an expert's 16-row tile by 16 gate (+ 16 up) columns (gate/up)
+// or 32 output columns (down) per wave, over all of K, with the next K
+// block's loads in flight while one is multiplied; no cross-wave reduction.
+// The units run as the leading workgroups of the grouped gate/up and down
+// launches (ffn.hip), beside the GEMV arm's.  Operand layout of the
+// 16x16x32 MFMA: A[i][k] in lane i + 16*(k/8) element k%8, B[k][j] in lane
+// j + 16*(k/8) element k%8, D[i][j] in lane j + 16*(i/4) element i%4.  The K
+// order inside a 64-wide chunk is permuted the same way for A and B (lane
+// group g holds k = 16g..16g+15, split over two MFMAs), which leaves the
+// products unchanged.
+#pragma once
+#include "gemv.hpp"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTileRows = kMfmaTileRows;
+
+// 8 e4m3 codes (2 dwords) to 8 bf16, exact.
+__device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
+    const bf16x2 a = e4m3x2_bf16<false>(w0), b = e4m3x2_bf16<true>(w0);
+    const bf16x2 c = e4m3x2_bf16<false>(w1), d = e4m3x2_bf16<true>(w1);
+    return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The tile a workgroup row (blockIdx.y) covers: an expert of the MFMA list
+// and 16 of its rows, or 16 rows of the shared expert.
+struct MTile {
+    ExpertSet X;           // the expert family (a copy: no pointer into the kernel arguments)
+    int e, row0, n;           // expert, first row within the expert, rows in the tile
+    const int32_t *list;      // routed: the expert's entries; shared: null (entries first + m)
+    int first;
+    bool valid;
+};
+
+__device__ __forceinline__ MTile resolve_mtile(const FfnArgs &a, int t) {
+    MTile m{a.routed, 0, 0, 0, nullptr, 0, false};
+    const int nk = a.R * a.k;
+    const int n_routed = a.meta[kMetaMfmaTiles];
+    if (t < n_routed) {
+        // the expert whose tile range holds t (prefix over the MFMA list)
+        int lo = 0, hi = a.meta[kMetaMfmaCount] - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.mfma_tiles[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        const int e = a.mfma_list[lo];
+        if (e < 0 || e >= a.E) return m;
+        const int cnt = a.counts[e], off = a.offsets[e];
+        if (cnt < 0 || off < 0 || off + cnt > nk) return m;
+        m.e = e;
+        m.row0 = (t - a.mfma_tiles[lo]) * kTileRows;
+        m.n = min(kTileRows, cnt - m.row0);
+        m.list = a.perm + off + m.row0;
+        m.valid = m.n > 0;
+        return m;
+    }
+    if (!a.shared_mfma) return m;
+    const int ts = t - n_routed;
+    if (ts * kTileRows >= a.R) return m;
+    m.X = a.shared;
+    m.row0 = ts * kTileRows;
+    m.n = min(kTileRows, a.R - m.row0);
+    m.first = nk + m.row0;
+    m.valid = true;
+    return m;
+}
+
+__device__ __forceinline__ int mtile_entry(const MTile &m, int i, int nk) {
+    if (i >= m.n) return -1;
+    if (!m.list) return m.first + i;
+    const int e = m.list[i];
+    return (e >= 0 && e < nk) ? e : -1;
+}
+
+// ------------------------------------------------------------------ gate/up
+
+constexpr int kMfmaWaves = 4;    // waves per workgroup; each owns its own columns over all of K
+
+// Per-lane operands of one 128-wide K block of the gate/up tile: the gate
+// and up weight chunks (16 codes each, two 64-wide halves) and the lane's
+// row of activations for the same k (two 8-value pieces per half).
+struct GuStage {
+    u32x4 g[2], u[2], x[2][2];
+};
+
+__device__ __forceinline__ void gu_load(GuStage &s, const uint8_t *wg, const uint8_t *wu, const uint16_t *xr,
+                                        bool rv, int kb, int grp) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int k0 = kb * 128 + c * 64 + grp * 16;
+        s.g[c] = ld16_stream(wg + k0);
+        s.u[c] = ld16_stream(wu + k0);
+        s.x[c][0] = rv ? ld16(xr + k0) : u32x4{0u, 0u, 0u, 0u};
+        s.x[c][1] = rv ? ld16(xr + k0 + 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// acc += scale * (X_tile . W^T) over one K block, gate and up.
+__device__ __forceinline__ void gu_step(const GuStage &s, float sg, float su, f32x4 &accg, f32x4 &accu) {
+    f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const bf16x8 x0 = as_bf16x8(s.x[c][0]), x1 = as_bf16x8(s.x[c][1]);
+        tg = mfma(x0, e4m3x8_bf16(s.g[c].x, s.g[c].y), tg);
+        tg = mfma(x1, e4m3x8_bf16(s.g[c].z, s.g[c].w), tg);
+        tu = mfma(x0, e4m3x8_bf16(s.u[c].x, s.u[c].y), tu);
+        tu = mfma(x1, e4m3x8_bf16(s.u[c].z, s.u[c].w), tu);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        accg[i] = fmaf(sg, tg[i], accg[i]);
+        accu[i] = fmaf(su, tu[i], accu[i]);
+    }
+}
+
+// h = silu(X_tile . Wg^T) * (X_tile . Wu^T) for a 16-row tile and 16 gate
+// columns (+ the 16 matching up columns) per wave, all of K; two K blocks of
+// loads are in flight while one is multiplied.
+__device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int tile) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+    const MTile t = resolve_mtile(a, tile);
+    if (!t.valid) return;
+    const ExpertSet &X = t.X;
+    const int I = X.inter, H = a.H, nk = a.R * a.k;
+    const int n0 = (bx * kMfmaWaves + wid) * 16;
+    if (n0 >= I) return;
+    const int col = lane & 15, grp = lane >> 4;
+    const int nkb = H >> 7;
+    const int ent = mtile_entry(t, col, nk);
+    const bool rv = ent >= 0;
+    const uint16_t *xr = a.x + (size_t)(rv ? (ent < nk ? ent / a.k : ent - nk) : 0) * a.ldx;
+    const uint8_t *wg = X.gu + (size_t)t.e * X.gu_stride + (size_t)(n0 + col) * H;
+    const uint8_t *wu = X.gu + (size_t)t.e * X.gu_stride + (size_t)(I + n0 + col) * H;
+    // the K block's scales, lane j holding block j (H <= 8192: at most 64)
+    const float *sbase = reinterpret_cast<const float *>(X.gu_s + (size_t)t.e * X.gu_s_stride);
+    const float sgl = lane < nkb ? sbase[(size_t)(n0 >> 7) * nkb + lane] : 0.0f;
+    const float sul = lane < nkb ? sbase[(size_t)((I + n0) >> 7) * nkb + lane] : 0.0f;
+
+    f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+    GuStage s0, s1;
+    gu_load(s0, wg, wu, xr, rv, 0, grp);
+    if (nkb > 1) gu_load(s1, wg, wu, xr, rv, 1, grp);
+    for (int kb = 0; kb < nkb; kb += 2) {
+        gu_step(s0, readlane(sgl, kb), readlane(sul, kb), accg, accu);
+        if (kb + 2 < nkb) gu_load(s0, wg, wu, xr, rv, kb + 2, grp);
+        if (kb + 1 < nkb) {
+            gu_step(s1, readlane(sgl, kb + 1), readlane(sul, kb + 1), accg, accu);
+            if (kb + 3 < nkb) gu_load(s1, wg, wu, xr, rv, kb + 3, grp);
+        }
+    }
+    // D[i][j]: lane holds column j = col, rows 4*grp .. 4*grp+3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = mtile_entry(t, 4 * grp + i, nk);
+        if (e >= 0) a.h[(size_t)e * a.hstride + n0 + col] = silu_mul(accg[i], accu[i]);
+    }
+}
+
+// ------------------------------------------------------------------ down
+
+// Per-lane operands of one 128-wide K block of the down tile: the weight
+// chunks of the wave's two 16-column tiles and the lane's row of h (f32).
+struct DnStage {
+    u32x4 w[2][2];
+    f32x4 h[2][4];
+};
+
+__device__ __forceinline__ void dn_load(DnStage &s, const uint8_t *const (&wd)[2], const float *hr, bool rv, int kb,
+                                        int grp) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int k0 = kb * 128 + c * 64 + grp * 16;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) s.w[nt][c] = ld16_stream(wd[nt] + k0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            s.h[c][q] = rv ? *reinterpret_cast<const f32x4 *>(hr + k0 + 4 * q) : f32x4{0, 0, 0, 0};
+    }
+}
+
+// acc[nt] += scale[nt] * (h_tile . W^T) over one K block; h enters as
+// hi + lo bf16.
+__device__ __forceinline__ void dn_step(const DnStage &s, const float (&sc)[2], f32x4 (&acc)[2]) {
+    f32x4 td[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        bf16x8 hi0, lo0, hi1, lo1;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v0 = s.h[c][q][i], v1 = s.h[c][q + 2][i];
+                const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1;
+                hi0[q * 4 + i] = b0;
+                lo0[q * 4 + i] = (__bf16)(v0 - (float)b0);
+                hi1[q * 4 + i] = b1;
+                lo1[q * 4 + i] = (__bf16)(v1 - (float)b1);
+            }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const bf16x8 w0 = e4m3x8_bf16(s.w[nt][c].x, s.w[nt][c].y), w1 = e4m3x8_bf16(s.w[nt][c].z, s.w[nt][c].w);
+            td[nt] = mfma(hi0, w0, td[nt]);
+            td[nt] = mfma(lo0, w0, td[nt]);
+            td[nt] = mfma(hi1, w1, td[nt]);
+            td[nt] = mfma(lo1, w1, td[nt]);
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nt][i] = fmaf(sc[nt], td[nt][i], acc[nt][i]);
+}
+
+// D = h_tile . W_dn^T for a 16-row tile and 32 output columns per wave (two
+// 16-column tiles), all of K = I; two K blocks of loads in flight.
+__device__ __forceinline__ void mfma_down_unit(const FfnArgs &a, int bx, int tile) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+    const MTile t = resolve_mtile(a, tile);
+    if (!t.valid) return;
+    const ExpertSet &X = t.X;
+    const int I = X.inter, H = a.H, nk = a.R * a.k;
+    const int n0 = (bx * kMfmaWaves + wid) * 32;
+    if (n0 >= H) return;
+    const int col = lane & 15, grp = lane >> 4;
+    const int nkb = I >> 7;
+    const int ent = mtile_entry(t, col, nk);
+    const bool rv = ent >= 0;
+    const float *hr = a.h + (size_t)(rv ? ent : 0) * a.hstride;
+    const uint8_t *wd[2];
+    float sl[2];
+    const float *sbase = reinterpret_cast<const float *>(X.dn_s + (size_t)t.e * X.dn_s_stride);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        wd[nt] = X.dn + (size_t)t.e * X.dn_stride + (size_t)(n0 + nt * 16 + col) * I;
+        sl[nt] = lane < nkb ? sbase[(size_t)((n0 + nt * 16) >> 7) * nkb + lane] : 0.0f;
+    }
+    f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    DnStage s0, s1;
+    dn_load(s0, wd, hr, rv, 0, grp);
+    if (nkb > 1) dn_load(s1, wd, hr, rv, 1, grp);
+    for (int kb = 0; kb < nkb; kb += 2) {
+        {
+            const float sc[2] = {readlane(sl[0], kb), readlane(sl[1], kb)};
+            dn_step(s0, sc, acc);
+        }
+        if (kb + 2 < nkb) dn_load(s0, wd, hr, rv, kb + 2, grp);
+        if (kb + 1 < nkb) {
+            const float sc[2] = {readlane(sl[0], kb + 1), readlane(sl[1], kb + 1)};
+            dn_step(s1, sc, acc);
+            if (kb + 3 < nkb) dn_load(s1, wd, hr, rv, kb + 3, grp);
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int o = n0 + nt * 16 + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = mtile_entry(t, 4 * grp + i, nk);
+            if (e >= 0) a.dbuf[(size_t)e * a.H + o] = acc[nt][i];
+        }
+    }
+}
+
+// Workgroups of matrix-core units in a grouped launch: column groups of 64
+// gate/up pairs (gate/up) or 128 output columns (down), times the tile bound.
+__host__ __device__ inline int mfma_gate_up_groups(int imax) { return (imax + kMfmaWaves * 16 - 1) / (kMfmaWaves * 16); }
+__host__ __device__ inline int mfma_down_groups(int H) { return (H + kMfmaWaves * 32 - 1) / (kMfmaWaves * 32); }
+
+}  // namespace moe

@@ -88,8 +88,6 @@ __device__ int block_excl_scan(int v, int *wave_tot, int *total) {
     return excl;
 }
 
-constexpr int kMfmaTileRows = 32;
-
 // Splits the touched experts into the GEMV-arm list and the MFMA-arm list
 // (rows >= threshold), both ascending, and the MFMA row-tile prefix.  Thread
 // e of a 1024-thread block holds expert e's row count c.
