@@ -61,50 +61,101 @@ __device__ __forceinline__ unsigned ld_agent(const unsigned *p) {
     return __hip_atomic_load(const_cast<unsigned *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The top-k's total order (larger value first, lower index first among
-// equal values) as one unsigned 64-bit key: the float's bits made
-// order-preserving in the high word, the complemented index in the low word.
-// Key 0 sorts below every real entry.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-    uint32_t u = __float_as_uint(v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+// A logit as an order-preserving unsigned 32-bit key (larger value, larger
+// key; -0 and +0 share one key, NaN counts as -inf).  Key 0 sorts below
+// every real logit.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+    v = v != v ? -__builtin_inff() : (v == 0.0f ? 0.0f : v);
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float key_value(uint64_t key) {
-    uint32_t u = (uint32_t)(key >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-    return __uint_as_float(u);
+__device__ __forceinline__ float key_logit(uint32_t u) {
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
-__device__ __forceinline__ int key_index(uint64_t key) { return (int)~(uint32_t)key; }
 
-template <int CTRL, int ROWS = 0xf>
-__device__ __forceinline__ uint64_t key_max_step(uint64_t k) {
-    const uint32_t lo = (uint32_t)dpp<CTRL, ROWS>(0, (int)(uint32_t)k);
-    const uint32_t hi = (uint32_t)dpp<CTRL, ROWS>(0, (int)(uint32_t)(k >> 32));
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    return o > k ? o : k;
-}
-// Largest key of the wave, in every lane.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-    k = key_max_step<kDppXor1>(k);
-    k = key_max_step<kDppXor2>(k);
-    k = key_max_step<kDppHalfMirror>(k);
-    k = key_max_step<kDppMirror>(k);
-    k = key_max_step<kDppBcast15, 0xa>(k);
-    k = key_max_step<kDppBcast31, 0xc>(k);
-    const uint32_t lo = (uint32_t)readlane((int)(uint32_t)k, 63);
-    const uint32_t hi = (uint32_t)readlane((int)(uint32_t)(k >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+// Largest (smallest) unsigned value of the wave, uniform: row stages by DPP,
+// then the two lane swaps.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
+    const int id = MAX ? 0 : -1;
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = op(v, (uint32_t)dpp<kDppXor1>(id, (int)v));
+    v = op(v, (uint32_t)dpp<kDppXor2>(id, (int)v));
+    v = op(v, (uint32_t)dpp<kDppHalfMirror>(id, (int)v));
+    v = op(v, (uint32_t)dpp<kDppMirror>(id, (int)v));
+    float x, y;
+    lane_swap<16>(__uint_as_float(v), __uint_as_float(v), x, y);
+    v = op(__float_as_uint(x), __float_as_uint(y));
+    lane_swap<32>(__uint_as_float(v), __uint_as_float(v), x, y);
+    v = op(__float_as_uint(x), __float_as_uint(y));
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
 // Softmax over the E logits of one row, the k largest under the top-k order
-// and their renormalised weights, by one wave, without branches.  Each lane
-// holds NV keys (experts lane, lane+64, ...) sorted once; every round the
-// wave takes the largest lane head and the lane holding it pops its head.
+// (larger value first, lower index first among equal values) and their
+// renormalised weights, by one wave.  Each lane holds NV logits (experts
+// lane, lane+64, ...) sorted once; every round the wave takes the largest
+// lane head by a 32-bit wave max, the lane holding it (the lowest expert
+// index among equal heads: a second, rarely taken pass) pops its head.
 // w_j = exp(l_j - m) / sum_j exp(l_j - m), m the largest logit: the softmax
 // denominator over all E cancels in the renormalisation.  Lane j < k returns
-// slot j.  `coherent` reads the logits with agent-scope loads (written by
-// other workgroups of the same launch).  NaN logits count as -inf.
+// slot j.  raw[i] is the logit of expert lane + 64 i (entries past E unused).
+template <int NV>
+__device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, int &my_e, float &my_w) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t key[NV];
+    int idx[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        key[i] = e < E ? logit_key(raw[i]) : 0u;
+        idx[i] = e;
+    }
+    // stable sort by key, descending: equal keys keep ascending index
+#pragma unroll
+    for (int i = 1; i < NV; ++i) {
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const bool sw = key[j] > key[j - 1];
+            const uint32_t ka = key[j - 1], kb = key[j];
+            const int ia = idx[j - 1], ib = idx[j];
+            key[j - 1] = sw ? kb : ka;
+            key[j] = sw ? ka : kb;
+            idx[j - 1] = sw ? ib : ia;
+            idx[j] = sw ? ia : ib;
+        }
+    }
+    uint32_t sel_key = 0;
+    int sel_idx = 0;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t best = wave_ext_u32<true>(key[0]);
+        uint64_t hit = __builtin_amdgcn_ballot_w64(key[0] == best);
+        if (__builtin_popcountll(hit) > 1) {
+            const uint32_t least = wave_ext_u32<false>(key[0] == best ? (uint32_t)idx[0] : 0xffffffffu);
+            hit = __builtin_amdgcn_ballot_w64(key[0] == best && (uint32_t)idx[0] == least);
+        }
+        const int wl = __builtin_ctzll(hit);
+        const int bi = __builtin_amdgcn_readlane(idx[0], wl);
+        const bool pop = lane == wl;
+#pragma unroll
+        for (int i = 0; i + 1 < NV; ++i) {
+            key[i] = pop ? key[i + 1] : key[i];
+            idx[i] = pop ? idx[i + 1] : idx[i];
+        }
+        key[NV - 1] = pop ? 0u : key[NV - 1];
+        sel_key = lane == j ? best : sel_key;
+        sel_idx = lane == j ? bi : sel_idx;
+    }
+    const float v = key_logit(sel_key);
+    const float m = readlane(v, 0);
+    const float ex = lane < k ? expf(v - m) : 0.0f;
+    const float sum = group_sum<kWave>(ex);
+    my_e = (lane < k && sel_idx >= 0 && sel_idx < E) ? sel_idx : 0;
+    my_w = ex / sum;
+}
+
+// The same from logits in memory; `coherent` reads them with agent-scope
+// loads (written by other workgroups of the same launch).
 template <int NV>
 __device__ __forceinline__ void topk_wave(const float *l, int E, int k, bool coherent, int &my_e, float &my_w) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -115,39 +166,7 @@ __device__ __forceinline__ void topk_wave(const float *l, int E, int k, bool coh
         const int ec = e < E ? e : E - 1;
         raw[i] = coherent ? ld_agent(l + ec) : l[ec];
     }
-    uint64_t key[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = lane + kWave * i;
-        const float t = raw[i] != raw[i] ? -__builtin_inff() : raw[i];
-        key[i] = e < E ? topk_key(t, e) : 0ull;
-    }
-#pragma unroll
-    for (int i = 1; i < NV; ++i) {
-#pragma unroll
-        for (int j = i; j > 0; --j) {
-            const uint64_t a = key[j - 1], b = key[j];
-            const bool sw = b > a;
-            key[j - 1] = sw ? b : a;
-            key[j] = sw ? a : b;
-        }
-    }
-    uint64_t sel = 0;
-    for (int j = 0; j < k; ++j) {
-        const uint64_t best = wave_max_key(key[0]);
-        const bool pop = key[0] == best;
-#pragma unroll
-        for (int i = 0; i + 1 < NV; ++i) key[i] = pop ? key[i + 1] : key[i];
-        key[NV - 1] = pop ? 0ull : key[NV - 1];
-        sel = lane == j ? best : sel;
-    }
-    const float v = key_value(sel);
-    const float m = readlane(v, 0);
-    const float ex = lane < k ? expf(v - m) : 0.0f;
-    const float sum = group_sum<kWave>(ex);
-    const int e = key_index(sel);
-    my_e = (lane < k && e >= 0 && e < E) ? e : 0;
-    my_w = ex / sum;
+    topk_regs<NV>(raw, E, k, my_e, my_w);
 }
 
 // Logits per lane for E experts: 1, 2, 4, 8 or 16.
