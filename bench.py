@@ -111,6 +111,15 @@ def cpu_baseline(wl, res, budget_s: float):
         bytes_total += syn.effective_weight_bytes(wl, int(np.unique(ids).size), li is None)
         if t_total >= budget_s:
             break
+    # the first layer again on one thread
+    oracle.set_threads(1)
+    ids = res.routing[0].topk_ids.cpu().numpy()
+    L = oracle_layer(oracle, wl, res.W[0], experts=np.unique(ids))
+    x, li = bits(res.x[0]), host(res.logits_in[0])
+    t0 = time.perf_counter()
+    oracle.layer_forward(L, x, logits_in=li)
+    t_one = time.perf_counter() - t0
+    oracle.set_threads(threads)
     return {
         "value": round(bytes_total / t_total / 1e9, 4),
         "unit": "GB/s",
@@ -118,7 +127,8 @@ def cpu_baseline(wl, res, budget_s: float):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{done_layers} of {len(res.layer_ids)} layers of the same workload, one pass each, "
-                  f"{threads} OpenMP threads, f64 arithmetic",
+                  f"{threads} OpenMP threads, f64 arithmetic; layer 0 once more on 1 thread",
+        "single_thread_us_per_layer": round(t_one * 1e6, 1),
     }
 
 
@@ -173,15 +183,19 @@ def main():
             step()
     torch.cuda.synchronize()
 
-    def time_plain():
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # An event after every step on the launch stream: the timed region is
+    # first..last event, and the per-step spans give the distribution.
+    def timed(run_one):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            step()
-        e1.record(stream)
+        with torch.cuda.stream(stream):
+            ev[0].record(stream)
+            for i in range(args.steps):
+                run_one()
+                ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        spans = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+        return ev[0].elapsed_time(ev[-1]) / args.steps, spans
 
     def time_graph():
         g = torch.cuda.CUDAGraph()
@@ -191,24 +205,36 @@ def main():
         for _ in range(max(3, args.warmup // 4)):
             g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for _ in range(args.steps):
-                g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        return timed(g.replay)
 
+    spans_by_mode = {}
     if args.launch in ("stream", "both"):
-        results["stream"] = time_plain()
+        results["stream"], spans_by_mode["stream"] = timed(step)
     if args.launch in ("graph", "both"):
-        results["graph"] = time_graph()
+        results["graph"], spans_by_mode["graph"] = time_graph()
     assert moe.moe_ctx_status(ctx) == 0
     best_mode = min(results, key=results.get)
     ms_per_step = results[best_mode]
 
-    touched = distinct_routed(res)
+    def pct(v, q):
+        v = sorted(v)
+        return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    spans = spans_by_mode[best_mode]
+    dist = {f"p{q}": round(pct(spans, q / 100) * 1e3 / layers, 3) for q in (10, 50, 90)}
+
+    # rows per expert over the step (multi-row steps): the grouping's counts
+    routing_stats = None
+    if rows >= 2:
+        cnt = torch.stack([rt.expert_count.to(torch.int64) for rt in res.routing])   # [layers, E]
+        routing_stats = {
+            "distinct_experts_per_layer": round(float((cnt > 0).sum(1).float().mean()), 2),
+            "zero_row_experts_per_layer": round(float((cnt == 0).sum(1).float().mean()), 2),
+            "max_rows_per_expert": int(cnt.max()),
+            "experts_ge_4_rows_per_layer": round(float((cnt >= 4).sum(1).float().mean()), 2),
+            "experts_ge_32_rows_per_layer": round(float((cnt >= 32).sum(1).float().mean()), 2),
+            "row_histogram_layer0": {str(int(b)): int(n) for b, n in
+                                     zip(*torch.unique(cnt[0], return_counts=True))},
+        }
     router_gemv = wl.router == "gemv"
     eff_bytes = sum(syn.effective_weight_bytes(wl, int(torch.unique(rt.topk_ids).numel()), router_gemv)
                     for rt in res.routing)
@@ -269,6 +295,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "us_per_layer_dist": dist,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -281,6 +308,7 @@ def main():
                    "router": wl.router},
         "launch_ms_per_step": {m: round(v, 5) for m, v in results.items()},
         "effective_bytes_per_step": int(eff_bytes),
+        "routing": routing_stats,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
