@@ -12,23 +12,51 @@
 
 namespace moe {
 
-// Router GEMV: one wave per router row (row E is the shared-gate vector); the
-// row stays in registers while the wave walks the R activation rows.
-template <int NCH>
+// Router GEMV for multi-row steps: one wave per router row (row E is the
+// shared-gate vector) holds it in registers.  The workgroup stages blocks of
+// RB activation rows in LDS (each read from memory once per workgroup); every
+// wave forms its row's RB partial sums and reduces them together (the
+// transposing reduction: the same bits as the one-row wave sum), so lane
+// group i of the wave ends with row r0 + i.
+template <int NCH, int RB>
 __global__ __launch_bounds__(256) void k_router(RouteArgs a) {
+    extern __shared__ u32x4 xs[];    // [RB][H/8] 16-byte activation chunks
+    constexpr int SPAN = kWave / RB;
     const int lane = threadIdx.x & (kWave - 1);
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.E + (a.wsg ? 1 : 0)) return;
+    const bool live = row < a.E + (a.wsg ? 1 : 0);
+    const bool gate_row = row >= a.E;
+    const int nch = a.H >> 3;
     u32x4 wv[NCH];
-    load_bf16_row<NCH>(row < a.E ? a.wr + (size_t)row * a.H : a.wsg, a.H, wv);
-    const float bias = (row < a.E && a.bias) ? a.bias[row] : 0.0f;
-    for (int r = 0; r < a.R; ++r) {
-        const float acc = dot_bf16_row<NCH>(wv, a.x + (size_t)r * a.ldx, a.H);
-        if (lane == 0) {
-            if (row < a.E)
-                a.logits[(size_t)r * a.E + row] = acc + bias;
-            else
-                a.s[r] = sigmoid(acc);
+    if (live) load_bf16_row<NCH>(gate_row ? a.wsg : a.wr + (size_t)row * a.H, a.H, wv);
+    const float bias = (live && !gate_row && a.bias) ? a.bias[row] : 0.0f;
+    for (int r0 = 0; r0 < a.R; r0 += RB) {
+        const int nr = min(RB, a.R - r0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nr * nch; i += 256) {
+            const int rr = i / nch, c = i - rr * nch;
+            xs[rr * nch + c] = ld16(a.x + (size_t)(r0 + rr) * a.ldx + (size_t)c * 8);
+        }
+        __syncthreads();
+        if (!live) continue;
+        float p[RB];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+            float acc = 0.0f;
+            if (rr < nr) {
+#pragma unroll
+                for (int t = 0; t < NCH; ++t) {
+                    const int c = lane + kWave * t;
+                    if (c < nch) acc = dot8_bf16(wv[t], xs[rr * nch + c], acc);
+                }
+            }
+            p[rr] = acc;
+        }
+        xreduce<kWave, RB, 1>(p);
+        const int mine = lane / SPAN;
+        if (lane % SPAN == 0 && mine < nr) {
+            if (gate_row) a.s[r0 + mine] = sigmoid(p[0]);
+            else a.logits[(size_t)(r0 + mine) * a.E + row] = p[0] + bias;
         }
     }
 }
@@ -179,21 +207,35 @@ __global__ __launch_bounds__(1024) void k_group(RouteArgs a, int do_plan) {
 
 size_t group_lds_bytes(int E, int R) { return (size_t)E * (size_t)((R + 31) / 32) * 4u; }
 
+// Activation rows staged per block: 64 KB of LDS at most.
+static int router_rows_per_block(int H, int R) {
+    int rb = H <= 2048 ? 16 : H <= 4096 ? 8 : 4;
+    while (rb > 2 && rb / 2 >= R) rb /= 2;
+    return rb;
+}
+
+template <int NCH>
+static hipError_t router_nch(const RouteArgs &a, hipStream_t st) {
+    const int rows = a.E + (a.wsg ? 1 : 0);
+    const int rb = router_rows_per_block(a.H, a.R);
+    const size_t lds = (size_t)rb * (size_t)a.H * 2;
+    dim3 grid((rows + 3) / 4), block(256);
+    switch (rb) {
+        case 2: hipLaunchKernelGGL((k_router<NCH, 2>), grid, block, lds, st, a); break;
+        case 4: hipLaunchKernelGGL((k_router<NCH, 4>), grid, block, lds, st, a); break;
+        case 8: hipLaunchKernelGGL((k_router<NCH, 8>), grid, block, lds, st, a); break;
+        default: hipLaunchKernelGGL((k_router<NCH, 16>), grid, block, lds, st, a); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_router(const RouteArgs &a, hipStream_t st) {
     const int nch = ((a.H >> 3) + kWave - 1) / kWave;
-    const int rows = a.E + (a.wsg ? 1 : 0);
-    dim3 grid((rows + 3) / 4), block(256);
-    if (nch <= 1)
-        hipLaunchKernelGGL(k_router<1>, grid, block, 0, st, a);
-    else if (nch <= 2)
-        hipLaunchKernelGGL(k_router<2>, grid, block, 0, st, a);
-    else if (nch <= 4)
-        hipLaunchKernelGGL(k_router<4>, grid, block, 0, st, a);
-    else if (nch <= 8)
-        hipLaunchKernelGGL(k_router<8>, grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL(k_router<16>, grid, block, 0, st, a);
-    return hipGetLastError();
+    if (nch <= 1) return router_nch<1>(a, st);
+    if (nch <= 2) return router_nch<2>(a, st);
+    if (nch <= 4) return router_nch<4>(a, st);
+    if (nch <= 8) return router_nch<8>(a, st);
+    return router_nch<16>(a, st);
 }
 
 hipError_t launch_topk(const RouteArgs &a, bool compute_s, hipStream_t st) {
