@@ -166,9 +166,10 @@ MOE_API int moe_ctx_set_mfma_min_rows(moe_ctx *ctx, int rows);
  * expert with at least one row (steps of >= 2 rows). */
 MOE_API int moe_ctx_set_force_arm(moe_ctx *ctx, int arm);
 /* One-row layers: 0 = one launch per layer (router, top-k, routed and shared
- * experts and the blend in one kernel; built for the 16-, 256- and
- * 512-expert layer shapes, other shapes use the three launches), 1 = three
- * launches (router and shared expert; routed gate/up; down and blend).
+ * experts and the blend in one kernel; built for the 16- and 256-expert fp8
+ * layer shapes and taken only when all its workgroups fit on the device at
+ * once; other layers use the three launches), 1 = three launches (router and
+ * shared expert; routed gate/up; down and blend).
  * Also MOE_ONE_ROW_PATH=split in the environment.  Both give the same bits. */
 MOE_API int moe_ctx_set_one_row_path(moe_ctx *ctx, int path);
 /* Device-side error word: kernels that meet an expert id outside [0, E)

@@ -28,6 +28,9 @@
 // The last down workgroup resets the synchronisation words for the next call.
 #include "gemv.hpp"
 
+#include <mutex>
+#include <vector>
+
 namespace moe {
 
 constexpr int P1 = kPairsPerWave;
@@ -296,32 +299,68 @@ static LayerShape layer_shape(const RouteArgs &r, const FfnArgs &a) {
     return s;
 }
 
-template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
-static hipError_t layer_launch(const RouteArgs &r, const FfnArgs &a, unsigned *sync, hipStream_t st) {
+static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, unsigned *sync) {
     LayerGrid g;
     const int n_rows = (r.logits_in ? 0 : r.E) + (r.wsg ? 1 : 0);
     g.nrb = n_rows > 0 ? (n_rows + 3) / 4 : 1;
     g.nsb = a.shared.inter > 0 ? (a.shared.inter + 4 * P1 - 1) / (4 * P1) : 0;
     g.ngb = (a.routed.inter + 4 * P1 - 1) / (4 * P1);
-    const int rows_per_block = 4 * (kWave / LPR);
+    const int rows_per_block = 4 * (kWave / lpr);
     g.ndb = (a.H + rows_per_block - 1) / rows_per_block;
     g.sync = sync;
-    const int blocks = g.nrb + g.nsb + a.k * g.ngb + g.ndb;
-    const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
-    const size_t lds = (size_t)nslots * a.hstride * 4;
-    hipLaunchKernelGGL((k_layer_r1<FMT, NCH, NV, LPR, DCH, KS, HS>), dim3(blocks), dim3(256), lds, st, r, a, g);
+    return g;
+}
+static int layer_blocks(const LayerGrid &g, const FfnArgs &a) { return g.nrb + g.nsb + a.k * g.ngb + g.ndb; }
+static size_t layer_lds(const FfnArgs &a) { return (size_t)(a.k + (a.shared.inter > 0 ? 1 : 0)) * a.hstride * 4; }
+
+template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
+static hipError_t layer_launch(const RouteArgs &r, const FfnArgs &a, unsigned *sync, hipStream_t st) {
+    const LayerGrid g = layer_grid(r, a, LPR, sync);
+    hipLaunchKernelGGL((k_layer_r1<FMT, NCH, NV, LPR, DCH, KS, HS>), dim3(layer_blocks(g, a)), dim3(256),
+                       layer_lds(a), st, r, a, g);
     return hipGetLastError();
 }
 
+// Whether every workgroup of the launch can be resident at once on the
+// current device: the workgroups that wait are then running while the ones
+// they wait on run, and the phases overlap.  (The waits are correct either
+// way: a workgroup only waits on lower-indexed ones.)
+template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
+static bool layer_resident(const RouteArgs &r, const FfnArgs &a) {
+    struct Entry { int device; size_t lds; int per_cu; };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    const size_t lds = layer_lds(a);
+    int per_cu = -1;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry &e : cache)
+            if (e.device == dev && e.lds == lds) per_cu = e.per_cu;
+        if (per_cu < 0) {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &per_cu, reinterpret_cast<const void *>(&k_layer_r1<FMT, NCH, NV, LPR, DCH, KS, HS>), 256,
+                    lds) != hipSuccess)
+                return false;
+            cache.push_back({dev, lds, per_cu});
+        }
+    }
+    return layer_blocks(layer_grid(r, a, LPR, nullptr), a) <= per_cu * cus;
+}
+
 // The shapes the single launch is built for: the tiny layer (H 256, E 16,
-// I 128), the 35B-A3B layer (H 2048, E 256, I 512, fp8) and the 397B-A17B
-// layer (H 4096, E 512, I 1024, nvfp4).  Others take the three-launch path.
-// KS: the most slots (routed + shared) an instantiation holds; HS: the
-// intermediate size of every slot (routed and shared alike).
+// I 128) and the 35B-A3B layer (H 2048, E 256, I 512, fp8).  KS: the most
+// slots (routed + shared) an instantiation holds; HS: the intermediate size
+// of every slot (routed and shared alike).  Other shapes, and any launch
+// whose workgroups do not all fit on the device at once (the 397B-A17B
+// shape, for one: 2049 workgroups against about 768 resident, measured
+// slower than the three launches), take the three-launch path.
 #define MOE_LAYER_SHAPES(X)             \
     X(kFp8, 1, 1, 8, 1, 17, 128)        \
-    X(kFp8, 4, 4, 32, 1, 9, 512)        \
-    X(kNvfp4, 8, 8, 32, 1, 11, 1024)
+    X(kFp8, 4, 4, 32, 1, 9, 512)
 
 bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
@@ -330,7 +369,7 @@ bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
 #define MOE_MATCH(F, N, V, L, D, K, HSV)                                                               \
     if (s.fmt == F && s.nch == N && s.nv == V && s.lpr == L && s.dch == D && nslots <= K &&              \
         a.routed.inter == HSV && (a.shared.inter == 0 || a.shared.inter == HSV))                          \
-        return true;
+        return layer_resident<F, N, V, L, D, K, HSV>(r, a);
     MOE_LAYER_SHAPES(MOE_MATCH)
 #undef MOE_MATCH
     return false;

@@ -185,6 +185,25 @@ def test_kernel_timing_counts_launches(moe, tiny):
     ctx.close()
 
 
+@pytest.mark.parametrize("name,single", [("a3b", True), ("a17b", False)])
+def test_single_launch_only_where_resident(moe, name, single):
+    """The one-row layer takes the single launch for the 35B-A3B shape (all
+    its workgroups fit on the GPU at once) and the three launches for the
+    397B-A17B shape (they do not)."""
+    wl = syn.WORKLOADS[name]
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    ctx = moe.Ctx(0)
+    lw, x, y, rt, ws = _setup(moe, wl, W, rows=1)
+    moe.moe_ctx_set_timing(ctx, True)
+    moe.moe_layer_forward(ctx, lw, x, y, None, ws, routing=rt)
+    layer = moe.moe_ctx_kernel_stats(ctx, moe.KERNELS.index("layer"))[1]
+    router = moe.moe_ctx_kernel_stats(ctx, moe.KERNELS.index("router"))[1]
+    assert (layer, router) == ((1, 0) if single else (0, 1))
+    assert moe.moe_ctx_device_errors(ctx) == 0
+    moe.moe_ctx_set_timing(ctx, False)
+    ctx.close()
+
+
 def test_fault_injection_on_single_launch_layer(moe, tiny):
     wl, W = tiny
     ctx = moe.Ctx(0)
