@@ -63,6 +63,7 @@ def lib():
         L.orc_layer_forward.argtypes = [C.POINTER(_Layer), C.c_void_p, C.c_int, C.c_void_p,
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_void_p]
+        L.orc_rms_norm.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_double, C.c_void_p]
     return _lib
 
 
@@ -251,3 +252,17 @@ def layer_forward(layer: Layer, x: np.ndarray, logits_in: Optional[np.ndarray] =
     if rc != 0:
         raise ValueError(f"orc_layer_forward failed ({rc})")
     return {"ids": ids, "w": w, "s": s, "y": y, "out": out}
+
+
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of bf16 rows (uint16 bit patterns [R][H]) with bf16 weights
+    gamma [H]: x / sqrt(mean(x^2) + eps) * gamma, one bf16 rounding."""
+    x = _c(np.atleast_2d(x), np.uint16)
+    gamma = _c(gamma, np.uint16)
+    R, H = x.shape
+    if gamma.shape != (H,):
+        raise ValueError("gamma must have one value per column")
+    out = np.empty((R, H), np.uint16)
+    if lib().orc_rms_norm(_ptr(x), R, H, _ptr(gamma), float(eps), _ptr(out)) != 0:
+        raise ValueError("orc_rms_norm rejected its arguments")
+    return out

@@ -389,3 +389,25 @@ done:
     free(y);
     return rc;
 }
+
+/* ------------------------------------------------------------------ norm */
+
+int orc_rms_norm(const uint16_t *x, int R, int H, const uint16_t *gamma, double eps, uint16_t *out)
+{
+    if (!x || !gamma || !out || R < 0 || H <= 0 || !(eps >= 0.0))
+        return -1;
+    for (int r = 0; r < R; r++) {
+        const uint16_t *xr = x + (size_t)r * H;
+        double ss = 0.0;
+        for (int o = 0; o < H; o++) {
+            double v = (double)orc_bf16_to_f32(xr[o]);
+            ss += v * v;
+        }
+        double inv = 1.0 / sqrt(ss / (double)H + eps);
+        for (int o = 0; o < H; o++) {
+            double v = (double)orc_bf16_to_f32(xr[o]) * inv * (double)orc_bf16_to_f32(gamma[o]);
+            out[(size_t)r * H + o] = orc_f32_to_bf16_rne((float)v);
+        }
+    }
+    return 0;
+}

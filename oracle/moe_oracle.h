@@ -97,6 +97,13 @@ int orc_layer_forward(const orc_layer *L, const uint16_t *x, int R,
                       const float *logits_in, const uint16_t *residual,
                       int32_t *ids, float *w, float *s, float *y, uint16_t *out);
 
+/* RMSNorm of R bf16 rows of H values (GB10 blueprint, "Kernels":
+ * residual_add_rms_norm, the norm that follows the MoE output joining the
+ * residual; Qwen3-8B card, "Structure": RMSNorm over the hidden size):
+ *   out[r,o] = bf16_rne( x[r,o] / sqrt(mean_o x[r,o]^2 + eps) * gamma[o] ),
+ * in double, one rounding at the end. */
+int orc_rms_norm(const uint16_t *x, int R, int H, const uint16_t *gamma, double eps, uint16_t *out);
+
 #ifdef __cplusplus
 }
 #endif
