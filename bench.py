@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--rows", type=int, default=None)
     p.add_argument("--layers", type=int, default=None)
     p.add_argument("--launch", choices=["graph", "stream", "both"], default="both")
+    p.add_argument("--norm", action="store_true",
+                   help="with the RMSNorm epilogue of the layer output (moe_layer_forward_norm)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--profile-steps", type=int, default=None,
@@ -161,7 +163,7 @@ def main():
     layers = args.layers if args.layers is not None else wl.layers
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    res = Resident(wl, rows, layers, device=dev, keep_y=False)
+    res = Resident(wl, rows, layers, device=dev, keep_y=False, norm=args.norm)
     ctx = moe.Ctx(0)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -305,7 +307,7 @@ def main():
                                f"{'fp8 e4m3 block-128' if wl.fmt == 0 else 'nvfp4'} weights, "
                                f"{rows} row(s), {layers} layers back to back",
                    "rows": rows, "layers": layers, "launch": best_mode,
-                   "router": wl.router},
+                   "router": wl.router, "epilogue": "rmsnorm" if args.norm else None},
         "launch_ms_per_step": {m: round(v, 5) for m, v in results.items()},
         "effective_bytes_per_step": int(eff_bytes),
         "routing": routing_stats,

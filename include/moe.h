@@ -59,7 +59,7 @@ extern "C" {
 #endif
 
 #define MOE_API __attribute__((visibility("default")))
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum moe_status {
     MOE_OK = 0,
@@ -139,7 +139,8 @@ enum moe_kernel_id {
     MOE_K_MFMA_GATE_UP = 6, /* reserved: the matrix-core arm runs inside MOE_K_GATE_UP */
     MOE_K_MFMA_DOWN = 7,    /* reserved: the matrix-core arm runs inside MOE_K_DOWN */
     MOE_K_LAYER = 8,    /* a whole one-row layer in one launch */
-    MOE_K_COUNT = 9
+    MOE_K_NORM = 9,     /* RMSNorm epilogue on its own (one-row layers outside the single launch) */
+    MOE_K_COUNT = 10
 };
 
 MOE_API int moe_abi_version(void);
@@ -218,6 +219,31 @@ MOE_API int moe_layer_forward(moe_ctx *ctx, const moe_layer_weights *w, const vo
                               int64_t ldx, const float *logits_in, const moe_routing *routing,
                               void *y, void *residual, int64_t ldy, void *ws, size_t ws_bytes,
                               void *stream);
+
+/* Epilogue of moe_layer_forward_norm: RMSNorm of every output row for the
+ * next layer (GB10 blueprint, "Kernels": residual_add_rms_norm, the norm that
+ * follows the MoE output joining the residual; Qwen3-8B card, "Structure":
+ * RMSNorm over the hidden size):
+ *   out[r,o] = bf16_rne( v[r,o] / sqrt(mean_o v[r,o]^2 + eps) * weight[o] )
+ * with v the row as written (the residual after the add, or y when the call
+ * has no residual), in f32.  A zero-centred weight w is weight = 1 + w. */
+typedef struct moe_norm {
+    size_t struct_size;         /* sizeof(moe_norm) */
+    const void *weight;         /* device bf16 [H] */
+    float eps;                  /* finite, >= 0 */
+    void *out;                  /* device bf16 [rows][ldo] */
+    int64_t ldo;                /* >= H */
+} moe_norm;
+
+/* moe_layer_forward with the RMSNorm epilogue (`norm` non-NULL; NULL is
+ * moe_layer_forward).  One-row layers on the single launch normalise in its
+ * last down workgroup, multi-row steps in the blend; the three-launch
+ * one-row path adds one launch (MOE_K_NORM).  Errors as moe_layer_forward,
+ * plus MOE_ERR_INVALID_ARG for a bad `norm`. */
+MOE_API int moe_layer_forward_norm(moe_ctx *ctx, const moe_layer_weights *w, const void *x, int rows,
+                                   int64_t ldx, const float *logits_in, const moe_routing *routing,
+                                   void *y, void *residual, int64_t ldy, const moe_norm *norm, void *ws,
+                                   size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ MOE_ERR_DEVICE_LOST = -6
 MOE_WFMT_FP8_E4M3_B128 = 0
 MOE_WFMT_NVFP4 = 1
 
-KERNELS = ["router", "topk", "group", "gate_up", "down", "blend", "mfma_gate_up", "mfma_down", "layer"]
+KERNELS = ["router", "topk", "group", "gate_up", "down", "blend", "mfma_gate_up", "mfma_down", "layer", "norm"]
 
 
 class MoeError(RuntimeError):
@@ -56,6 +56,12 @@ class RoutingC(C.Structure):
     _fields_ = [("struct_size", C.c_size_t), ("topk_ids", C.c_void_p), ("topk_w", C.c_void_p),
                 ("shared_gate", C.c_void_p), ("expert_count", C.c_void_p),
                 ("expert_offset", C.c_void_p), ("perm", C.c_void_p), ("logits", C.c_void_p)]
+
+
+class NormC(C.Structure):
+    """moe_norm: the RMSNorm epilogue of moe_layer_forward_norm."""
+    _fields_ = [("struct_size", C.c_size_t), ("weight", C.c_void_p), ("eps", C.c_float),
+                ("out", C.c_void_p), ("ldo", C.c_int64)]
 
 
 _lib = None
@@ -89,6 +95,8 @@ def lib():
                                 vp, vp, i64, vp, sz, vp], i32),
             "moe_layer_forward": ([vp, C.POINTER(LayerWeightsC), vp, i32, i64, vp,
                                    C.POINTER(RoutingC), vp, vp, i64, vp, sz, vp], i32),
+            "moe_layer_forward_norm": ([vp, C.POINTER(LayerWeightsC), vp, i32, i64, vp,
+                                        C.POINTER(RoutingC), vp, vp, i64, C.POINTER(NormC), vp, sz, vp], i32),
             "moe_debug_decode": ([vp, i32, vp, vp, i32, vp], i32),
         }
         for name, (args, res) in sig.items():
@@ -311,6 +319,21 @@ def moe_layer_forward(ctx: Ctx, w: LayerWeights, x: torch.Tensor, y: Optional[to
                                    _p(logits_in), routing.ref if routing is not None else None,
                                    _p(y), _p(residual), ldy, _p(ws), ws.numel(), _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_norm(ctx: Ctx, w: LayerWeights, x: torch.Tensor, y: Optional[torch.Tensor],
+                           residual: Optional[torch.Tensor], ws: torch.Tensor, norm_weight: torch.Tensor,
+                           eps: float, norm_out: torch.Tensor, logits_in: Optional[torch.Tensor] = None,
+                           routing: Optional[Routing] = None, stream=None) -> None:
+    """moe_layer_forward plus the RMSNorm of every output row into norm_out."""
+    rows = x.shape[0]
+    ldy = _ld(y if y is not None else residual, w.hidden)
+    n = NormC(C.sizeof(NormC), _p(norm_weight), float(eps), _p(norm_out), _ld(norm_out, w.hidden))
+    _check(lib().moe_layer_forward_norm(ctx.handle, w.ref, _p(x), rows, _ld(x, w.hidden),
+                                        _p(logits_in), routing.ref if routing is not None else None,
+                                        _p(y), _p(residual), ldy, C.byref(n), _p(ws), ws.numel(),
+                                        _stream(stream)),
+           "moe_layer_forward_norm")
 
 
 def moe_debug_decode(ctx: Ctx, fmt: int, codes: torch.Tensor, out: torch.Tensor,

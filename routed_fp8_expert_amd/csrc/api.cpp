@@ -15,6 +15,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <cmath>
 #include <vector>
 
 namespace {
@@ -253,6 +254,15 @@ int check_out(const moe_layer_weights *w, const void *y, const void *res, int R,
     return MOE_OK;
 }
 
+int check_norm(const moe_layer_weights *w, const moe_norm *n, const void *y, const void *res) {
+    if (!n) return MOE_OK;
+    if (n->struct_size < sizeof(moe_norm) || !n->weight || !n->out || n->ldo < w->hidden ||
+        !(n->eps >= 0.0f) || !std::isfinite(n->eps) || (!y && !res))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(n->weight, 2) || !aligned(n->out, 2)) return MOE_ERR_MISALIGNED;
+    return MOE_OK;
+}
+
 int check_ws(const moe_layer_weights *w, int R, const void *ws, size_t ws_bytes) {
     if (R == 0) return MOE_OK;
     if (!ws) return MOE_ERR_INVALID_ARG;
@@ -387,7 +397,11 @@ moe::FfnArgs ffn_args(moe_ctx *c, const moe_layer_weights *w, const void *x, int
 int do_ffn(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
     int rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up(a, st); });
     if (rc) return rc;
-    if (a.R == 1) return launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
+    if (a.R == 1) {
+        rc = launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
+        if (rc || !a.norm_w) return rc;
+        return launch(c, MOE_K_NORM, st, [&] { return moe::launch_rmsnorm(a, st); });
+    }
     rc = launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_grouped(a, st); });
     if (rc) return rc;
     return launch(c, MOE_K_BLEND, st, [&] { return moe::launch_blend(a, st); });
@@ -402,7 +416,9 @@ int do_layer_r1(moe_ctx *c, const moe::RouteArgs &r, moe::FfnArgs a, hipStream_t
     if (rc) return rc;
     rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up_r1(a, st); });
     if (rc) return rc;
-    return launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
+    rc = launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
+    if (rc || !a.norm_w) return rc;
+    return launch(c, MOE_K_NORM, st, [&] { return moe::launch_rmsnorm(a, st); });
 }
 
 RoutingPtrs routing_ptrs(const moe_routing *r, void *ws, const Layout &L) {
@@ -592,15 +608,15 @@ MOE_API int moe_expert_ffn(moe_ctx *c, const moe_layer_weights *w, const void *x
     return do_ffn(c, ffn_args(c, w, x, R, ldx, rp, y, res, ldy, ws, L), st);
 }
 
-MOE_API int moe_layer_forward(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
-                              const float *logits_in, const moe_routing *routing, void *y, void *res, int64_t ldy,
-                              void *ws, size_t ws_bytes, void *stream) {
+MOE_API int moe_layer_forward_norm(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
+                                   const float *logits_in, const moe_routing *routing, void *y, void *res,
+                                   int64_t ldy, const moe_norm *norm, void *ws, size_t ws_bytes, void *stream) {
     if (!c) return MOE_ERR_INVALID_ARG;
     if (c->status) return MOE_ERR_DEVICE_LOST;
     int rc;
     if ((rc = validate_weights(w)) || (rc = validate_rows(w, R)) || (rc = check_x(w, x, R, ldx)) ||
         (routing && (rc = check_routing(routing, R, true))) || (rc = check_out(w, y, res, R, ldy)) ||
-        (rc = check_ws(w, R, ws, ws_bytes)))
+        (rc = check_ws(w, R, ws, ws_bytes)) || (rc = check_norm(w, norm, y, res)))
         return rc;
     if (!logits_in && !w->router_w) return MOE_ERR_INVALID_ARG;
     if (logits_in && !aligned(logits_in, 4)) return MOE_ERR_MISALIGNED;
@@ -611,11 +627,23 @@ MOE_API int moe_layer_forward(moe_ctx *c, const moe_layer_weights *w, const void
     const Layout L = make_layout(w, R);
     const RoutingPtrs rp = routing_ptrs(routing, ws, L);
     const moe::RouteArgs ra = route_args(c, w, x, R, ldx, logits_in, rp, ws, L);
-    const moe::FfnArgs fa = ffn_args(c, w, x, R, ldx, rp, y, res, ldy, ws, L);
+    moe::FfnArgs fa = ffn_args(c, w, x, R, ldx, rp, y, res, ldy, ws, L);
+    if (norm) {
+        fa.norm_w = static_cast<const uint16_t *>(norm->weight);
+        fa.norm_eps = norm->eps;
+        fa.norm_out = static_cast<uint16_t *>(norm->out);
+        fa.ldn = norm->ldo;
+    }
     if (R == 1) return do_layer_r1(c, ra, fa, st);
     rc = do_route(c, ra, true, st);
     if (rc) return rc;
     return do_ffn(c, fa, st);
+}
+
+MOE_API int moe_layer_forward(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
+                              const float *logits_in, const moe_routing *routing, void *y, void *res, int64_t ldy,
+                              void *ws, size_t ws_bytes, void *stream) {
+    return moe_layer_forward_norm(c, w, x, R, ldx, logits_in, routing, y, res, ldy, nullptr, ws, ws_bytes, stream);
 }
 
 MOE_API int moe_debug_decode(moe_ctx *c, int fmt, const void *codes, float *out, int n, void *stream) {

@@ -332,7 +332,7 @@ __device__ __forceinline__ void down_gemv_unit(const FfnArgs &a, int bx, int tas
     using Row = DownRow<FMT, LPR, CH>;
     Row rows[RPL];
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) rows[i].load(X, t.e, o0 + i, sub, o0 + i < a.H);
+    for (int i = 0; i < RPL; ++i) rows[i].template load<true>(X, t.e, o0 + i, sub, o0 + i < a.H);
     const float g = global_scale<FMT>(X.dn_g, t.e);
     const int orow = o0 + sub / SPAN;
     const bool writer = sub % SPAN == 0 && orow < a.H;
@@ -378,21 +378,117 @@ __global__ __launch_bounds__(256) void k_down_grouped(FfnArgs a, int nmx, int nm
 }
 
 // Blend for multi-row steps: y[r][o] = sum_j w[r][j] dbuf[r*k+j][o] (slot
-// order) + s[r] dbuf[shared r][o], then the residual add and bf16 rounding,
-// with the same operation sequence as the one-row fused kernel.
+// order) + s[r] dbuf[shared r][o], with the same operation sequence as the
+// one-row fused kernel.
+// (The slot loads are unconditional and a skipped slot is a select, so the
+// k + 1 loads of a column are in flight together; a slot with an expert id
+// outside [0, E) leaves y unchanged, as in the one-row kernels.)
+__device__ __forceinline__ float blend_value(const FfnArgs &a, int r, int o) {
+    float d[kMaxSlots];
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j)
+        if (j < a.k) d[j] = a.dbuf[(size_t)(r * a.k + j) * a.H + o];
+    const float ds = a.shared.inter > 0 ? a.dbuf[(size_t)(a.R * a.k + r) * a.H + o] : 0.0f;
+    float y = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j) {
+        if (j < a.k) {
+            const int i = r * a.k + j;
+            const int e = a.ids[i];
+            const float t = fmaf(a.w[i], d[j], y);
+            y = (e >= 0 && e < a.E) ? t : y;
+        }
+    }
+    if (a.shared.inter > 0) y = fmaf(a.s[r], ds, y);
+    return y;
+}
+
+// ... then the residual add and bf16 rounding.
 __global__ __launch_bounds__(256) void k_blend(FfnArgs a) {
     const int o = blockIdx.x * 256 + threadIdx.x;
     const int r = blockIdx.y;
     if (o >= a.H) return;
-    float y = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-        const int i = r * a.k + j;
-        const int e = a.ids[i];
-        if (e < 0 || e >= a.E) continue;
-        y = fmaf(a.w[i], a.dbuf[(size_t)i * a.H + o], y);
+    store_out(a.y, a.res, a.ldy, r, o, blend_value(a, r, o));
+}
+
+// The same with the RMSNorm epilogue: one workgroup per row (the norm needs
+// the whole row); the normalised row is the residual after the add (the
+// output y without a residual).  The row's routing is read once, and each
+// thread loads a batch of columns' down outputs before using any.
+__global__ __launch_bounds__(256) void k_blend_norm(FfnArgs a) {
+    extern __shared__ float vrow[];   // [2H]: the row, then the staged weight
+    __shared__ int ids_s[kMaxSlots];
+    __shared__ float w_s[kMaxSlots];
+    const int r = blockIdx.x;
+    if (threadIdx.x < a.k) {
+        ids_s[threadIdx.x] = a.ids[r * a.k + threadIdx.x];
+        w_s[threadIdx.x] = a.w[r * a.k + threadIdx.x];
     }
-    if (a.shared.inter > 0) y = fmaf(a.s[r], a.dbuf[(size_t)(a.R * a.k + r) * a.H + o], y);
-    store_out(a.y, a.res, a.ldy, r, o, y);
+    __syncthreads();
+    const bool sh = a.shared.inter > 0;
+    const float sr = sh ? a.s[r] : 0.0f;
+    for (int o0 = threadIdx.x; o0 < a.H; o0 += 256 * kNormBatch) {
+        float y[kNormBatch];
+#pragma unroll
+        for (int u = 0; u < kNormBatch; ++u) y[u] = 0.0f;
+        for (int j = 0; j < a.k; ++j) {
+            const int e = ids_s[j];
+            const bool ok = e >= 0 && e < a.E;
+            const float *d = a.dbuf + (size_t)(r * a.k + j) * a.H;
+            float t[kNormBatch];
+#pragma unroll
+            for (int u = 0; u < kNormBatch; ++u) {
+                const int o = o0 + 256 * u;
+                t[u] = d[o < a.H ? o : a.H - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < kNormBatch; ++u) {
+                const float v = fmaf(w_s[j], t[u], y[u]);
+                y[u] = ok ? v : y[u];
+            }
+        }
+        if (sh) {
+            const float *d = a.dbuf + (size_t)(a.R * a.k + r) * a.H;
+            float t[kNormBatch];
+#pragma unroll
+            for (int u = 0; u < kNormBatch; ++u) {
+                const int o = o0 + 256 * u;
+                t[u] = d[o < a.H ? o : a.H - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < kNormBatch; ++u) y[u] = fmaf(sr, t[u], y[u]);
+        }
+        uint16_t rin[kNormBatch];
+#pragma unroll
+        for (int u = 0; u < kNormBatch; ++u) {
+            const int o = o0 + 256 * u;
+            rin[u] = a.res ? a.res[(size_t)r * a.ldy + (o < a.H ? o : a.H - 1)] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int u = 0; u < kNormBatch; ++u) {
+            const int o = o0 + 256 * u;
+            if (o >= a.H) continue;
+            const uint16_t yb = f32_to_bf16(y[u]);
+            uint16_t src = yb;
+            if (a.y) a.y[(size_t)r * a.ldy + o] = yb;
+            if (a.res) {
+                src = f32_to_bf16(bf16_to_f32(rin[u]) + y[u]);
+                a.res[(size_t)r * a.ldy + o] = src;
+            }
+            vrow[o] = bf16_to_f32(src);
+        }
+    }
+    __syncthreads();
+    block_rms_norm(vrow, a.H, a.norm_w, a.norm_eps, a.norm_out + (size_t)r * a.ldn);
+}
+
+// The RMSNorm epilogue alone, on rows a previous launch wrote (one workgroup
+// per row).
+__global__ __launch_bounds__(256) void k_rmsnorm(FfnArgs a) {
+    extern __shared__ float vrow[];   // [2H]
+    const int r = blockIdx.x;
+    stage_row<false>((a.res ? a.res : a.y) + (size_t)r * a.ldy, a.H, vrow);
+    block_rms_norm(vrow, a.H, a.norm_w, a.norm_eps, a.norm_out + (size_t)r * a.ldn);
 }
 
 // Decode probe: every code through the kernels' converters.
@@ -570,7 +666,14 @@ hipError_t launch_down_grouped(const FfnArgs &a, hipStream_t st) {
     return a.fmt == kFp8 ? down_grouped_fmt<kFp8>(a, st) : down_grouped_fmt<kNvfp4>(a, st);
 }
 hipError_t launch_blend(const FfnArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(k_blend, dim3((a.H + 255) / 256, a.R), dim3(256), 0, st, a);
+    if (a.norm_w)
+        hipLaunchKernelGGL(k_blend_norm, dim3(a.R), dim3(256), (size_t)a.H * 8, st, a);
+    else
+        hipLaunchKernelGGL(k_blend, dim3((a.H + 255) / 256, a.R), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_rmsnorm(const FfnArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(k_rmsnorm, dim3(a.R), dim3(256), (size_t)a.H * 8, st, a);
     return hipGetLastError();
 }
 

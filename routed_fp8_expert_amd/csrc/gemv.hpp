@@ -21,23 +21,33 @@ __device__ __forceinline__ float sigmoid(float t) { return 1.0f / (1.0f + expf(-
 // One bf16 router row (H values, resident in registers as NCH 16-byte chunks
 // per lane) dotted with activation row xr: the lane-strided chunks, fdot2
 // with f32 accumulation, a wave sum.
+// Every load below is unconditional, from a clamped chunk index, with the
+// bounds applied to the value: a load under a per-lane condition compiles to
+// a branch that waits for it, which serialises the loads.
 template <int NCH>
 __device__ __forceinline__ void load_bf16_row(const uint16_t *row, int H, u32x4 (&wv)[NCH]) {
     const int lane = threadIdx.x & (kWave - 1), nch = H >> 3;
 #pragma unroll
     for (int t = 0; t < NCH; ++t) {
         const int c = lane + kWave * t;
-        wv[t] = c < nch ? ld16_stream(row + (size_t)c * 8) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 v = ld16_stream(row + (size_t)(c < nch ? c : nch - 1) * 8);
+        wv[t] = c < nch ? v : u32x4{0u, 0u, 0u, 0u};
     }
 }
 template <int NCH>
 __device__ __forceinline__ float dot_bf16_row(const u32x4 (&wv)[NCH], const uint16_t *xr, int H) {
     const int lane = threadIdx.x & (kWave - 1), nch = H >> 3;
+    u32x4 xv[NCH];
+#pragma unroll
+    for (int t = 0; t < NCH; ++t) {
+        const int c = lane + kWave * t;
+        xv[t] = ld16(xr + (size_t)(c < nch ? c : nch - 1) * 8);
+    }
     float acc = 0.0f;
 #pragma unroll
     for (int t = 0; t < NCH; ++t) {
         const int c = lane + kWave * t;
-        if (c < nch) acc = dot8_bf16(wv[t], ld16(xr + (size_t)c * 8), acc);
+        if (c < nch) acc = dot8_bf16(wv[t], xv[t], acc);
     }
     return group_sum<kWave>(acc);
 }
@@ -172,6 +182,71 @@ __device__ __forceinline__ void topk_wave(const float *l, int E, int k, bool coh
 // Logits per lane for E experts: 1, 2, 4, 8 or 16.
 __host__ __device__ constexpr int topk_nv(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16; }
 
+// ------------------------------------------------------------------ RMSNorm epilogue
+
+// Columns a 256-thread block loads per batch of the norm epilogue: eight per
+// thread, issued before any is used (a loop that used each load at once
+// would pay the memory latency once per column).
+constexpr int kNormBatch = 8;
+
+// out[o] = bf16(v[o] * rsqrt(mean v^2 + eps) * gamma[o]) for one row whose
+// f32 values v (already bf16-rounded) are in LDS, with room for H more
+// floats after them (the weight is staged there); every thread of the
+// 256-thread block calls it.  The sum of squares runs in a fixed order (per
+// thread over its columns, the wave sum, then the four waves in order), so
+// the result does not depend on timing.
+__device__ __forceinline__ void block_rms_norm(float *v, int H, const uint16_t *gamma, float eps, uint16_t *out) {
+    __shared__ float part[4];
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+    float *gs = v + H;
+    for (int o0 = threadIdx.x; o0 < H; o0 += 256 * kNormBatch) {
+        uint16_t t[kNormBatch];
+#pragma unroll
+        for (int u = 0; u < kNormBatch; ++u) {
+            const int o = o0 + 256 * u;
+            t[u] = gamma[o < H ? o : H - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kNormBatch; ++u) {
+            const int o = o0 + 256 * u;
+            if (o < H) gs[o] = bf16_to_f32(t[u]);
+        }
+    }
+    float ss = 0.0f;
+    for (int o = threadIdx.x; o < H; o += 256) ss = fmaf(v[o], v[o], ss);
+    ss = group_sum<kWave>(ss);
+    if (lane == 0) part[wid] = ss;
+    __syncthreads();
+    const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+    const float r = 1.0f / sqrtf(tot / (float)H + eps);
+    for (int o = threadIdx.x; o < H; o += 256) out[o] = f32_to_bf16(v[o] * r * gs[o]);
+    __syncthreads();
+}
+
+// Stage a bf16 row into LDS as f32, kNormBatch loads in flight per thread
+// (COHERENT: agent-scope loads of values other workgroups of the launch wrote).
+template <bool COHERENT>
+__device__ __forceinline__ void stage_row(const uint16_t *src, int H, float *v) {
+    for (int o0 = threadIdx.x; o0 < H; o0 += 256 * kNormBatch) {
+        uint16_t t[kNormBatch];
+#pragma unroll
+        for (int u = 0; u < kNormBatch; ++u) {
+            const int o = o0 + 256 * u;
+            const int oc = o < H ? o : H - 1;
+            if constexpr (COHERENT)
+                t[u] = __hip_atomic_load(const_cast<uint16_t *>(src + oc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                t[u] = src[oc];
+        }
+#pragma unroll
+        for (int u = 0; u < kNormBatch; ++u) {
+            const int o = o0 + 256 * u;
+            if (o < H) v[o] = bf16_to_f32(t[u]);
+        }
+    }
+    __syncthreads();
+}
+
 // ------------------------------------------------------------------ weight chunks
 
 template <int FMT> __device__ __forceinline__ int row_bytes(int cols) { return FMT == kFp8 ? cols : cols / 2; }
@@ -274,24 +349,25 @@ struct GateUpRows {
 #pragma unroll
         for (int q = 0; q < 2 * P; ++q) {
             const int p = q >> 1;
-            const int row = (q & 1) ? I + i0 + p : i0 + p;
             const bool live = i0 + p < I;
+            const int row = ((q & 1) ? I : 0) + (live ? i0 + p : i0);
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const int ch = lane + kWave * c;
-                w[q][c] = (live && ch < nch) ? ld16_stream(wbase + (size_t)row * rb + (size_t)ch * 16)
-                                             : u32x4{0u, 0u, 0u, 0u};
+                const u32x4 v = ld16_stream(wbase + (size_t)row * rb + (size_t)(ch < nch ? ch : nch - 1) * 16);
+                w[q][c] = (live && ch < nch) ? v : u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
             const int p = q >> 1;
-            const int row = (q & 1) ? I + i0 + p : i0 + p;
             const bool live = i0 + p < I;
+            const int row = ((q & 1) ? I : 0) + (live ? i0 + p : i0);
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const int ch = lane + kWave * c;
-                sc[q][c] = (live && ch < nch) ? chunk_scale<FMT>(sbase, row, H, ch) : f32x2{0.0f, 0.0f};
+                const f32x2 v = chunk_scale<FMT>(sbase, row, H, ch < nch ? ch : nch - 1);
+                sc[q][c] = (live && ch < nch) ? v : f32x2{0.0f, 0.0f};
             }
         }
         g = global_scale<FMT>(X.gu_g, e);
@@ -317,8 +393,8 @@ struct GateUpRows {
         const int lane = threadIdx.x & (kWave - 1), nch = row_bytes<FMT>(H) >> 4;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int ch = lane + kWave * c;
-            if (ch < nch) load_x_chunk<FMT>(xr + (size_t)ch * cols_per_chunk<FMT>(), x[c]);
+            const int ch = lane + kWave * c;   // chunks past the row are loaded clamped, never used
+            load_x_chunk<FMT>(xr + (size_t)(ch < nch ? ch : nch - 1) * cols_per_chunk<FMT>(), x[c]);
         }
     }
 
@@ -367,19 +443,36 @@ struct DownRow {
     u32x4 w[CH];
     f32x2 sc[CH];
 
+    // CLAMPED: unconditional loads from a clamped row and chunk, zeroed past
+    // the matrix (the grouped kernel: its loads then overlap, 176 against
+    // 192 us per 8-row 397B-A17B layer); otherwise loads under the row/chunk
+    // condition (the one-row kernels: measured faster there, 19.1 against
+    // 20.2 us per 35B-A3B layer).
+    template <bool CLAMPED = false>
     __device__ __forceinline__ void load(const ExpertSet &X, int e, int o, int sub, bool live) {
         const int rb = row_bytes<FMT>(X.inter), nch = rb >> 4;
-        const uint8_t *wrow = X.dn + (size_t)e * X.dn_stride + (size_t)o * rb;
+        const int oc = CLAMPED && !live ? 0 : o;
+        const uint8_t *wrow = X.dn + (size_t)e * X.dn_stride + (size_t)oc * rb;
         const uint8_t *sbase = X.dn_s + (size_t)e * X.dn_s_stride;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int ch = sub + LPR * c;
-            w[c] = (live && ch < nch) ? ld16_stream(wrow + (size_t)ch * 16) : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (CLAMPED) {
+                const u32x4 v = ld16_stream(wrow + (size_t)(ch < nch ? ch : nch - 1) * 16);
+                w[c] = (live && ch < nch) ? v : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                w[c] = (live && ch < nch) ? ld16_stream(wrow + (size_t)ch * 16) : u32x4{0u, 0u, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int ch = sub + LPR * c;
-            sc[c] = (live && ch < nch) ? chunk_scale<FMT>(sbase, o, X.inter, ch) : f32x2{0.0f, 0.0f};
+            if constexpr (CLAMPED) {
+                const f32x2 v = chunk_scale<FMT>(sbase, oc, X.inter, ch < nch ? ch : nch - 1);
+                sc[c] = (live && ch < nch) ? v : f32x2{0.0f, 0.0f};
+            } else {
+                sc[c] = (live && ch < nch) ? chunk_scale<FMT>(sbase, o, X.inter, ch) : f32x2{0.0f, 0.0f};
+            }
         }
     }
 
@@ -398,12 +491,11 @@ struct DownRow {
         const int nch = row_bytes<FMT>(inter) >> 4;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int ch = sub + LPR * c;
-            if (ch < nch) {
-                const f32x4 *h4 = reinterpret_cast<const f32x4 *>(h + (size_t)ch * cols_per_chunk<FMT>());
+            const int ch = sub + LPR * c;   // chunks past the row: loaded clamped, never used
+            const f32x4 *h4 =
+                reinterpret_cast<const f32x4 *>(h + (size_t)(ch < nch ? ch : nch - 1) * cols_per_chunk<FMT>());
 #pragma unroll
-                for (int q = 0; q < h_quads<FMT>(); ++q) hq[c][q] = h4[q];
-            }
+            for (int q = 0; q < h_quads<FMT>(); ++q) hq[c][q] = h4[q];
         }
     }
 

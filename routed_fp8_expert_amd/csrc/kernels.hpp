@@ -58,6 +58,11 @@ struct FfnArgs {
     // single-launch one-row layer: per-XCD replicas of values crossing workgroups
     float *logits_rep;          // [kReplicas][E]
     float *h_rep;               // [kReplicas][k+1][hstride]
+    // optional epilogue: RMSNorm of each output row (res after the add, else y)
+    const uint16_t *norm_w;     // bf16 [H] weight; null = no epilogue
+    float norm_eps;
+    uint16_t *norm_out;         // bf16 [R][ldn]
+    int64_t ldn;
 };
 
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
@@ -77,6 +82,7 @@ hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync,
 hipError_t launch_down_blend_r1(const FfnArgs &a, hipStream_t st);
 hipError_t launch_down_grouped(const FfnArgs &a, hipStream_t st);
 hipError_t launch_blend(const FfnArgs &a, hipStream_t st);
+hipError_t launch_rmsnorm(const FfnArgs &a, hipStream_t st);
 
 // Diagnostics: decode n codes with the kernels' own converters.
 hipError_t launch_decode_probe(int fmt, const uint8_t *codes, float *out, int n, hipStream_t st);

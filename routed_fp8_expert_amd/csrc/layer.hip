@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
         }
     }
     const float s_gate = has_shared ? ld_agent(a.s) : 0.0f;
-    const float res_in = (live && a.res) ? bf16_to_f32(a.res[o]) : 0.0f;
+    const float res_in = a.res ? bf16_to_f32(a.res[live ? o : 0]) : 0.0f;   // unconditional load (clamped)
     // every slot's h is complete once the h-ready flag is up
     block_wait(sync + kSyncHReady + rep_id * kLine, 1u, a.err);
     stage_h<cols_per_chunk<FMT>(), HS, KS>(a.h_rep + (size_t)rep_id * hrep_stride, nslots,
@@ -263,10 +263,25 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
         }
     }
     if (live && sub == 0) {
-        if (a.y) a.y[o] = f32_to_bf16(y);
-        if (a.res) a.res[o] = f32_to_bf16(res_in + y);
+        const uint16_t yb = f32_to_bf16(y), rb = f32_to_bf16(res_in + y);
+        if (a.norm_w) {
+            // written through: the last down workgroup reads the whole row back
+            if (a.y) __hip_atomic_store(a.y + o, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (a.res) __hip_atomic_store(a.res + o, rb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            if (a.y) a.y[o] = yb;
+            if (a.res) a.res[o] = rb;
+        }
     }
-    if (block_arrive(sync + kSyncDownDone, &ticket_s) == (unsigned)(g.ndb - 1) && threadIdx.x == 0) {
+    const bool last = block_arrive(sync + kSyncDownDone, &ticket_s) == (unsigned)(g.ndb - 1);
+    if (last && a.norm_w) {
+        // RMSNorm epilogue of the row (the residual after the add, else y):
+        // every down workgroup's stores completed before its arrival
+        float *vrow = reinterpret_cast<float *>(hlds4);
+        stage_row<true>(a.res ? a.res : a.y, a.H, vrow);
+        block_rms_norm(vrow, a.H, a.norm_w, a.norm_eps, a.norm_out);
+    }
+    if (last && threadIdx.x == 0) {
         for (int c = 0; c < kReadyCopies; ++c) {
             __hip_atomic_store(sync + kSyncReady + c * kLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(sync + kSyncHReady + c * kLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -311,7 +326,11 @@ static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, unsig
     return g;
 }
 static int layer_blocks(const LayerGrid &g, const FfnArgs &a) { return g.nrb + g.nsb + a.k * g.ngb + g.ndb; }
-static size_t layer_lds(const FfnArgs &a) { return (size_t)(a.k + (a.shared.inter > 0 ? 1 : 0)) * a.hstride * 4; }
+static size_t layer_lds(const FfnArgs &a) {
+    const size_t h = (size_t)(a.k + (a.shared.inter > 0 ? 1 : 0)) * a.hstride * 4;
+    const size_t row = a.norm_w ? (size_t)a.H * 8 : 0;   // the epilogue's row and weight
+    return h > row ? h : row;
+}
 
 template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
 static hipError_t layer_launch(const RouteArgs &r, const FfnArgs &a, unsigned *sync, hipStream_t st) {
@@ -364,7 +383,7 @@ static bool layer_resident(const RouteArgs &r, const FfnArgs &a) {
 
 bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
-    if ((size_t)nslots * a.hstride * 4 > kLayerMaxHLds || (a.hstride & 1)) return false;
+    if (layer_lds(a) > kLayerMaxHLds || (a.hstride & 1)) return false;
     const LayerShape s = layer_shape(r, a);
 #define MOE_MATCH(F, N, V, L, D, K, HSV)                                                               \
     if (s.fmt == F && s.nch == N && s.nv == V && s.lpr == L && s.dch == D && nslots <= K &&              \

@@ -86,11 +86,15 @@ __device__ __forceinline__ MTile resolve_mtile(const FfnArgs &a, int t) {
     return m;
 }
 
+// Entry of row i of the tile, -1 past the tile's rows or for a listed entry
+// outside the step's R*k routed entries (shared-expert entries, first + i,
+// lie past them by construction).  The list load is unconditional, from a
+// clamped index: a valid tile has at least one row.
 __device__ __forceinline__ int mtile_entry(const MTile &m, int i, int nk) {
-    if (i >= m.n) return -1;
-    if (!m.list) return m.first + i;
-    const int e = m.list[i];
-    return (e >= 0 && e < nk) ? e : -1;
+    const int ic = i < m.n ? i : 0;
+    if (!m.list) return i < m.n ? m.first + ic : -1;
+    const int e = m.list[ic];
+    return (i < m.n && e >= 0 && e < nk) ? e : -1;
 }
 
 // ------------------------------------------------------------------ gate/up
@@ -150,6 +154,9 @@ __device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int 
     const int ent = mtile_entry(t, col, nk);
     const bool rv = ent >= 0;
     const uint16_t *xr = a.x + (size_t)(rv ? (ent < nk ? ent / a.k : ent - nk) : 0) * a.ldx;
+    int oent[4];   // entries of the output rows this lane holds (D layout), loaded early
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oent[i] = mtile_entry(t, 4 * grp + i, nk);
     const uint8_t *wg = X.gu + (size_t)t.e * X.gu_stride + (size_t)(n0 + col) * H;
     const uint8_t *wu = X.gu + (size_t)t.e * X.gu_stride + (size_t)(I + n0 + col) * H;
     // the K block's scales, lane j holding block j (H <= 8192: at most 64)
@@ -172,7 +179,7 @@ __device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int 
     // D[i][j]: lane holds column j = col, rows 4*grp .. 4*grp+3
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int e = mtile_entry(t, 4 * grp + i, nk);
+        const int e = oent[i];
         if (e >= 0) a.h[(size_t)e * a.hstride + n0 + col] = silu_mul(accg[i], accu[i]);
     }
 }
@@ -247,6 +254,9 @@ __device__ __forceinline__ void mfma_down_unit(const FfnArgs &a, int bx, int til
     const int ent = mtile_entry(t, col, nk);
     const bool rv = ent >= 0;
     const float *hr = a.h + (size_t)(rv ? ent : 0) * a.hstride;
+    int oent[4];   // entries of the output rows this lane holds (D layout), loaded early
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oent[i] = mtile_entry(t, 4 * grp + i, nk);
     const uint8_t *wd[2];
     float sl[2];
     const float *sbase = reinterpret_cast<const float *>(X.dn_s + (size_t)t.e * X.dn_s_stride);
@@ -276,7 +286,7 @@ __device__ __forceinline__ void mfma_down_unit(const FfnArgs &a, int bx, int til
         const int o = n0 + nt * 16 + col;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int e = mtile_entry(t, 4 * grp + i, nk);
+            const int e = oent[i];
             if (e >= 0) a.dbuf[(size_t)e * a.H + o] = acc[nt][i];
         }
     }

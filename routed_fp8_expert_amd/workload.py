@@ -25,7 +25,7 @@ class Resident:
 
     def __init__(self, wl: syn.Workload, rows: int, layers: Optional[int] = None, device="cuda",
                  x_attempts: Optional[Sequence[int]] = None, layer_ids: Optional[Sequence[int]] = None,
-                 keep_y: bool = True, with_routing: bool = True):
+                 keep_y: bool = True, with_routing: bool = True, norm: bool = False):
         self.wl, self.rows, self.device = wl, rows, torch.device(device)
         ids = list(layer_ids) if layer_ids is not None else list(range(layers or wl.layers))
         self.layer_ids = ids
@@ -46,6 +46,16 @@ class Resident:
                                 if with_routing else None)
         self.residual = [r.clone() for r in self.residual0]
         self.ws = B.workspace(self.lw[0], rows, self.device)
+        # optional RMSNorm epilogue: a weight near 1 per layer and the output rows
+        self.norm = norm
+        self.norm_w, self.norm_out = [], []
+        if norm:
+            for l in ids:
+                g = torch.Generator(device=self.device)
+                g.manual_seed(syn.subseed("norm-weight", wl.name, l))
+                w = 1.0 + 0.1 * torch.randn(wl.hidden, generator=g, device=self.device)
+                self.norm_w.append(w.to(torch.bfloat16))
+                self.norm_out.append(torch.empty((rows, wl.hidden), dtype=torch.bfloat16, device=self.device))
 
     def reset_residual(self):
         for r, r0 in zip(self.residual, self.residual0):
@@ -53,9 +63,14 @@ class Resident:
 
     def run(self, ctx: B.Ctx, stream=None, write_y: bool = True):
         for n in range(len(self.lw)):
-            B.moe_layer_forward(ctx, self.lw[n], self.x[n], self.y[n] if write_y else None,
-                                self.residual[n], self.ws, logits_in=self.logits_in[n],
-                                routing=self.routing[n], stream=stream)
+            if self.norm:
+                B.moe_layer_forward_norm(ctx, self.lw[n], self.x[n], self.y[n] if write_y else None,
+                                         self.residual[n], self.ws, self.norm_w[n], 1e-6, self.norm_out[n],
+                                         logits_in=self.logits_in[n], routing=self.routing[n], stream=stream)
+            else:
+                B.moe_layer_forward(ctx, self.lw[n], self.x[n], self.y[n] if write_y else None,
+                                    self.residual[n], self.ws, logits_in=self.logits_in[n],
+                                    routing=self.routing[n], stream=stream)
 
     def weight_bytes_resident(self) -> int:
         total = 0
