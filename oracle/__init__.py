@@ -64,6 +64,7 @@ def lib():
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_void_p]
         L.orc_rms_norm.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_double, C.c_void_p]
+        L.orc_dense_fp8.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p]
     return _lib
 
 
@@ -266,3 +267,19 @@ def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     if lib().orc_rms_norm(_ptr(x), R, H, _ptr(gamma), float(eps), _ptr(out)) != 0:
         raise ValueError("orc_rms_norm rejected its arguments")
     return out
+
+
+def dense_fp8(q: np.ndarray, scale: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """y = x . dequant(W)^T in double: q e4m3 codes [N][K], scale f32
+    [N/128][K/128], x bf16 bit patterns [R][K]."""
+    q = _c(q, np.uint8)
+    scale = _c(scale, np.float32)
+    x = _c(np.atleast_2d(x), np.uint16)
+    N, K = q.shape
+    R = x.shape[0]
+    if x.shape[1] != K or scale.shape != (N // 128, K // 128):
+        raise ValueError("shape mismatch")
+    y = np.empty((R, N), np.float64)
+    if lib().orc_dense_fp8(_ptr(q), _ptr(scale), N, K, _ptr(x), R, _ptr(y)) != 0:
+        raise ValueError("orc_dense_fp8 rejected its arguments")
+    return y

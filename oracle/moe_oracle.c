@@ -411,3 +411,30 @@ int orc_rms_norm(const uint16_t *x, int R, int H, const uint16_t *gamma, double 
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ dense */
+
+int orc_dense_fp8(const uint8_t *q, const float *scale, int N, int K, const uint16_t *x, int R, double *y)
+{
+    if (!q || !scale || !x || !y || N <= 0 || K <= 0 || R < 0 || N % 128 || K % 128)
+        return -1;
+    float *W = (float *)malloc(sizeof(float) * (size_t)N * K);
+    if (!W)
+        return -2;
+    int rc = orc_dequant_fp8(q, scale, N, K, W);
+    if (rc == 0) {
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+        for (int n = 0; n < N; n++) {
+            const float *wn = W + (size_t)n * K;
+            for (int r = 0; r < R; r++) {
+                const uint16_t *xr = x + (size_t)r * K;
+                double acc = 0.0;
+                for (int k = 0; k < K; k++)
+                    acc += (double)orc_bf16_to_f32(xr[k]) * (double)wn[k];
+                y[(size_t)r * N + n] = acc;
+            }
+        }
+    }
+    free(W);
+    return rc;
+}

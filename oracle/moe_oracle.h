@@ -104,6 +104,12 @@ int orc_layer_forward(const orc_layer *L, const uint16_t *x, int R,
  * in double, one rounding at the end. */
 int orc_rms_norm(const uint16_t *x, int R, int H, const uint16_t *gamma, double eps, uint16_t *out);
 
+/* Dense fp8 block-128 projection (GB10 blueprint, "Kernels":
+ * w8a16_gemm_pipelined_m32; "Precision": fp8/block128x128 weights read bf16
+ * activations): y[r][n] = sum_k x[r][k] * dequant(W)[n][k] in double, W the
+ * e4m3 codes [N][K] with f32 scales [N/128][K/128]. */
+int orc_dense_fp8(const uint8_t *q, const float *scale, int N, int K, const uint16_t *x, int R, double *y);
+
 #ifdef __cplusplus
 }
 #endif
