@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--launch", choices=["graph", "stream", "both"], default="both")
     p.add_argument("--norm", action="store_true",
                    help="with the RMSNorm epilogue of the layer output (moe_layer_forward_norm)")
+    p.add_argument("--dense", default=None, metavar="SHAPE",
+                   help="time the dense fp8 block-128 projection (moe_dense_fp8) of this shape instead")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--profile-steps", type=int, default=None,
@@ -134,6 +136,106 @@ def cpu_baseline(wl, res, budget_s: float):
     }
 
 
+def run_dense(args):
+    """The dense fp8 block-128 projection: `copies` resident matrices of one
+    shape (together beyond the on-package cache) applied in turn to the same
+    rows; one step = one projection per copy."""
+    import numpy as np
+    import torch
+    import moe_synth as syn
+    import routed_fp8_expert_amd as moe
+
+    name = args.dense
+    n, k = syn.DENSE_SHAPES[name]
+    rows = args.rows if args.rows is not None else 1
+    wbytes = n * k + (n // 128) * (k // 128) * 4
+    copies = args.layers if args.layers is not None else max(8, -(-(1 << 30) // wbytes))
+    torch.cuda.set_device(0)
+    q, s = syn.make_dense_weights(name, n, k, "cuda")
+    mats = []
+    for c in range(copies):
+        qc, sc = q.clone(), s.clone()
+        mats.append((qc, sc, moe.DenseWeights(qc, sc)))
+    x = syn.make_dense_x(name, rows, k, "cuda")
+    y = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
+    ctx = moe.Ctx(0)
+    stream = torch.cuda.Stream()
+
+    def step():
+        for _, _, w in mats:
+            moe.moe_dense_fp8(ctx, w, x, y, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    with torch.cuda.stream(stream):
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            step()
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev[0].elapsed_time(ev[1]) / args.steps
+    us = ms_per_step * 1e3 / copies
+    assert moe.moe_ctx_status(ctx) == 0
+
+    moe.moe_ctx_set_timing(ctx, True)
+    kt_steps = min(args.steps, 20)
+    for _ in range(kt_steps):
+        step()
+    torch.cuda.synchronize()
+    kms, kn = moe.moe_ctx_kernel_stats(ctx, moe.KERNELS.index("dense"))
+    moe.moe_ctx_set_timing(ctx, False)
+    ctx.close()
+    # algorithmic bytes per launch: codes + scales once, x read, y written
+    alg = wbytes + rows * k * 2 + rows * n * 2
+    flops = 2.0 * rows * n * k
+    achieved = alg / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        oracle.set_threads(threads)
+        qh, sh = q.cpu().numpy(), s.cpu().numpy()
+        xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
+        t0, done = time.perf_counter(), 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.dense_fp8(qh, sh, xb)
+            done += 1
+        t = (time.perf_counter() - t0) / done
+        cpu = {"value": round(alg / t / 1e9, 4), "unit": "GB/s", "us_per_projection": round(t * 1e6, 1),
+               "cores": threads, "kind": "oracle",
+               "sample": f"{done} projections of the same shape and rows, {threads} OpenMP threads, f64"}
+    line = {
+        "metric": f"us per dense fp8 block-128 projection {n}x{k} + weight GB/s (% of HBM peak), {rows} row(s)",
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "us_per_projection": round(us, 3),
+        "pct_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
+        "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-w/bf16-x/f32-acc",
+        "data": "synthetic (seeded; weights N(0,0.02) quantised, activations N(0,1))",
+        "config": {"workload": f"dense {name}: y[{rows},{n}] = x[{rows},{k}] . W^T, fp8 e4m3 block-128 weights, "
+                               f"{copies} resident copies in turn",
+                   "rows": rows, "copies": copies,
+                   "arm": "matrix cores" if rows >= 32 else "gemv"},
+        "kernels": {"dense": {"avg_us": round(kms / max(kn, 1) * 1e3, 3), "launches_per_step": kn // kt_steps}},
+        "roofline": {"bound": "hbm", "kernel": "dense", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(alg)},
+        "cpu_baseline": cpu,
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -152,6 +254,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 10}))
+        return
+
+    if args.dense is not None:
+        run_dense(args)
         return
 
     import moe_synth as syn

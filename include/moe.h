@@ -59,7 +59,7 @@ extern "C" {
 #endif
 
 #define MOE_API __attribute__((visibility("default")))
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 enum moe_status {
     MOE_OK = 0,
@@ -140,7 +140,8 @@ enum moe_kernel_id {
     MOE_K_MFMA_DOWN = 7,    /* reserved: the matrix-core arm runs inside MOE_K_DOWN */
     MOE_K_LAYER = 8,    /* a whole one-row layer in one launch */
     MOE_K_NORM = 9,     /* RMSNorm epilogue on its own (one-row layers outside the single launch) */
-    MOE_K_COUNT = 10
+    MOE_K_DENSE = 10,   /* dense fp8 block-128 projection (moe_dense_fp8) */
+    MOE_K_COUNT = 11
 };
 
 MOE_API int moe_abi_version(void);
@@ -244,6 +245,33 @@ MOE_API int moe_layer_forward_norm(moe_ctx *ctx, const moe_layer_weights *w, con
                                    int64_t ldx, const float *logits_in, const moe_routing *routing,
                                    void *y, void *residual, int64_t ldy, const moe_norm *norm, void *ws,
                                    size_t ws_bytes, void *stream);
+
+/* Dense fp8 block-128 weights for moe_dense_fp8 (GB10 blueprint, "Kernels":
+ * w8a16_gemm_pipelined_m32; "Precision": fp8 weights in 128x128 blocks read
+ * bf16 activations).  The dequantised matrix is
+ *   W[n][k] = e4m3(codes[n*ldw + k]) * scales[(n/128)*(k/128 count) + k/128]. */
+typedef struct moe_dense_weights {
+    size_t struct_size;         /* sizeof(moe_dense_weights) */
+    const void *codes;          /* device e4m3 [n][ldw], 16-byte aligned */
+    int64_t ldw;                /* bytes between rows: >= k, a multiple of 16 */
+    const float *scales;        /* device f32 [n/128][k/128] */
+    int32_t n;                  /* output columns: a positive multiple of 128 */
+    int32_t k;                  /* input columns: a positive multiple of 128, <= 8192 */
+} moe_dense_weights;
+
+/* Dense projection of bf16 rows (one MOE_K_DENSE launch; the caller keeps
+ * every buffer):
+ *   y[r][n] = bf16_rne( sum_k x[r][k] * W[n][k] ), f32 accumulation.
+ *   x     device bf16 [rows][ldx], 16-byte aligned, ldx >= k and a multiple of 8
+ *   y     device bf16 [rows][ldy], ldy >= n; must not overlap x
+ *   rows  0 .. 1048576 (0 enqueues nothing).  Below 32 rows a GEMV, from 32
+ *         rows 16-row matrix-core tiles; within an arm a row's result does not
+ *         depend on the other rows of the call.
+ * Errors: MOE_ERR_INVALID_ARG for a NULL or malformed argument or a shape
+ * outside the limits, MOE_ERR_MISALIGNED for a misaligned pointer or stride,
+ * MOE_ERR_DEVICE_LOST on a lost ctx; nothing is enqueued on an error. */
+MOE_API int moe_dense_fp8(moe_ctx *ctx, const moe_dense_weights *w, const void *x, int rows, int64_t ldx,
+                          void *y, int64_t ldy, void *stream);
 
 #ifdef __cplusplus
 }

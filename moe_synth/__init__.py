@@ -178,6 +178,32 @@ def make_layer_weights(wl: Workload, layer: int, device="cpu", n_experts: Option
     return out
 
 
+# ----------------------------------------------------------------- dense projections
+
+# Dense fp8 block-128 projections next to the experts (GB10 blueprint,
+# "Kernels": w8a16_gemm_pipelined_m32): the pages give no shapes, so two
+# stand-ins into and out of the 35B-A3B hidden size, and a small ragged one.
+DENSE_SHAPES: Dict[str, tuple] = {
+    "up_4096x2048": (4096, 2048),      # (n, k): hidden 2048 -> 4096
+    "down_2048x4096": (2048, 4096),    # 4096 -> hidden 2048
+    "small_384x640": (384, 640),
+    "wide_256x8192": (256, 8192),
+}
+
+
+def make_dense_weights(name: str, n: int, k: int, device="cpu", std: float = 0.02):
+    """A dense matrix N(0, std) [n, k] encoded fp8 block-128: (codes u8 [n, k],
+    scales f32 [n/128, k/128])."""
+    g = _gen(device, "dense", name, n, k)
+    return quant_fp8_b128(_normal((n, k), std, g, device))
+
+
+def make_dense_x(name: str, rows: int, k: int, device="cpu") -> torch.Tensor:
+    """Activation rows for a dense projection, bf16 [rows, k], N(0, 1)."""
+    g = _gen(device, "dense-x", name, rows, k)
+    return torch.randn((rows, k), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
 # ----------------------------------------------------------------- activations
 
 def make_x(wl: Workload, layer: int, rows: int, attempt: int = 0, device="cpu") -> torch.Tensor:

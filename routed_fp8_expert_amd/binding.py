@@ -27,7 +27,7 @@ MOE_ERR_DEVICE_LOST = -6
 MOE_WFMT_FP8_E4M3_B128 = 0
 MOE_WFMT_NVFP4 = 1
 
-KERNELS = ["router", "topk", "group", "gate_up", "down", "blend", "mfma_gate_up", "mfma_down", "layer", "norm"]
+KERNELS = ["router", "topk", "group", "gate_up", "down", "blend", "mfma_gate_up", "mfma_down", "layer", "norm", "dense"]
 
 
 class MoeError(RuntimeError):
@@ -64,6 +64,12 @@ class NormC(C.Structure):
                 ("out", C.c_void_p), ("ldo", C.c_int64)]
 
 
+class DenseWeightsC(C.Structure):
+    """moe_dense_weights: e4m3 codes [n][ldw] with f32 scales [n/128][k/128]."""
+    _fields_ = [("struct_size", C.c_size_t), ("codes", C.c_void_p), ("ldw", C.c_int64),
+                ("scales", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32)]
+
+
 _lib = None
 
 
@@ -97,6 +103,7 @@ def lib():
                                    C.POINTER(RoutingC), vp, vp, i64, vp, sz, vp], i32),
             "moe_layer_forward_norm": ([vp, C.POINTER(LayerWeightsC), vp, i32, i64, vp,
                                         C.POINTER(RoutingC), vp, vp, i64, C.POINTER(NormC), vp, sz, vp], i32),
+            "moe_dense_fp8": ([vp, C.POINTER(DenseWeightsC), vp, i32, i64, vp, i64, vp], i32),
             "moe_debug_decode": ([vp, i32, vp, vp, i32, vp], i32),
         }
         for name, (args, res) in sig.items():
@@ -334,6 +341,24 @@ def moe_layer_forward_norm(ctx: Ctx, w: LayerWeights, x: torch.Tensor, y: Option
                                         _p(y), _p(residual), ldy, C.byref(n), _p(ws), ws.numel(),
                                         _stream(stream)),
            "moe_layer_forward_norm")
+
+
+class DenseWeights:
+    """A dense fp8 block-128 matrix for moe_dense_fp8: codes u8 [n][k] (row
+    stride codes.stride(0) bytes) and scales f32 [n/128][k/128], device
+    tensors the caller keeps alive."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor):
+        n, k = codes.shape
+        self.codes, self.scales = codes, scales
+        self.n, self.k = n, k
+        self.ref = DenseWeightsC(C.sizeof(DenseWeightsC), _p(codes), codes.stride(0), _p(scales), n, k)
+
+
+def moe_dense_fp8(ctx: Ctx, w: DenseWeights, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """y[r] = x[r] . dequant(W)^T in bf16 (one launch)."""
+    _check(lib().moe_dense_fp8(ctx.handle, C.byref(w.ref), _p(x), x.shape[0], _ld(x, w.k), _p(y),
+                               _ld(y, w.n), _stream(stream)), "moe_dense_fp8")
 
 
 def moe_debug_decode(ctx: Ctx, fmt: int, codes: torch.Tensor, out: torch.Tensor,

@@ -16,7 +16,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["route.hip", "ffn.hip", "layer.hip", "api.cpp"]
+SOURCES = ["route.hip", "ffn.hip", "layer.hip", "dense.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -24,6 +24,8 @@ namespace {
 // own lines, then the single-launch layer's synchronisation lines.
 enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, kWordLayerSync = 1024,
                       kSyncWords = 1024 + 40 * 64 };
+constexpr int kDenseMaxK = 8192;         // a wave's 64 lanes hold one scale per 128-wide block
+constexpr int kDenseMaxRows = 1 << 20;   // matrix-core grid rows stay far below 65535
 constexpr int kDefaultMfmaMinRows = 4;   // rows per expert from which the MFMA arm pays (measured)
 constexpr int kMaxRows = 1024;
 constexpr int kMaxExperts = 1024;
@@ -644,6 +646,35 @@ MOE_API int moe_layer_forward(moe_ctx *c, const moe_layer_weights *w, const void
                               const float *logits_in, const moe_routing *routing, void *y, void *res, int64_t ldy,
                               void *ws, size_t ws_bytes, void *stream) {
     return moe_layer_forward_norm(c, w, x, R, ldx, logits_in, routing, y, res, ldy, nullptr, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_dense_fp8(moe_ctx *c, const moe_dense_weights *w, const void *x, int R, int64_t ldx, void *y,
+                          int64_t ldy, void *stream) {
+    if (!c || !w || w->struct_size < sizeof(moe_dense_weights)) return MOE_ERR_INVALID_ARG;
+    if (c->status) return MOE_ERR_DEVICE_LOST;
+    const int N = w->n, K = w->k;
+    if (N <= 0 || K <= 0 || N % 128 || K % 128 || K > kDenseMaxK || R < 0 || R > kDenseMaxRows)
+        return MOE_ERR_INVALID_ARG;
+    if (!w->codes || !w->scales || w->ldw < K) return MOE_ERR_INVALID_ARG;
+    if (!aligned(w->codes, 16) || w->ldw % 16 || !aligned(w->scales, 4)) return MOE_ERR_MISALIGNED;
+    if (R == 0) return MOE_OK;
+    if (!x || !y || ldx < K || ldy < N) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || ldx % 8 || !aligned(y, 2)) return MOE_ERR_MISALIGNED;
+    DeviceGuard g(c->device);
+    if (!g.ok()) return fail(c, MOE_ERR_HIP);
+    moe::DenseArgs a{};
+    a.w = static_cast<const uint8_t *>(w->codes);
+    a.w_stride = w->ldw;
+    a.s = w->scales;
+    a.x = static_cast<const uint16_t *>(x);
+    a.ldx = ldx;
+    a.y = static_cast<uint16_t *>(y);
+    a.ldy = ldy;
+    a.N = N;
+    a.K = K;
+    a.R = R;
+    const hipStream_t st = (hipStream_t)stream;
+    return launch(c, MOE_K_DENSE, st, [&] { return moe::launch_dense(a, st); });
 }
 
 MOE_API int moe_debug_decode(moe_ctx *c, int fmt, const void *codes, float *out, int n, void *stream) {

@@ -65,6 +65,15 @@ struct FfnArgs {
     int64_t ldn;
 };
 
+// Dense fp8 block-128 projection y = x . dequant(W)^T.
+struct DenseArgs {
+    const uint8_t *w; int64_t w_stride;   // e4m3 codes [N][w_stride bytes]
+    const float *s;                       // f32 scales [N/128][K/128]
+    const uint16_t *x; int64_t ldx;       // bf16 [R][ldx]
+    uint16_t *y; int64_t ldy;             // bf16 [R][ldy]
+    int N, K, R;
+};
+
 // Each launcher returns the hipError_t of its launch (hipGetLastError).
 hipError_t launch_router(const RouteArgs &a, hipStream_t st);
 hipError_t launch_topk(const RouteArgs &a, bool compute_s, hipStream_t st);
@@ -83,6 +92,7 @@ hipError_t launch_down_blend_r1(const FfnArgs &a, hipStream_t st);
 hipError_t launch_down_grouped(const FfnArgs &a, hipStream_t st);
 hipError_t launch_blend(const FfnArgs &a, hipStream_t st);
 hipError_t launch_rmsnorm(const FfnArgs &a, hipStream_t st);
+hipError_t launch_dense(const DenseArgs &a, hipStream_t st);
 
 // Diagnostics: decode n codes with the kernels' own converters.
 hipError_t launch_decode_probe(int fmt, const uint8_t *codes, float *out, int n, hipStream_t st);
