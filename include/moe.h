@@ -264,9 +264,9 @@ typedef struct moe_dense_weights {
  *   y[r][n] = bf16_rne( sum_k x[r][k] * W[n][k] ), f32 accumulation.
  *   x     device bf16 [rows][ldx], 16-byte aligned, ldx >= k and a multiple of 8
  *   y     device bf16 [rows][ldy], ldy >= n; must not overlap x
- *   rows  0 .. 1048576 (0 enqueues nothing).  Below 32 rows a GEMV, from 32
+ *   rows  0 .. 1048576 (0 enqueues nothing).  Below 8 rows a GEMV, from 8
  *         rows 16-row matrix-core tiles; within an arm a row's result does not
- *         depend on the other rows of the call.
+ *         depend on the other rows of the call (rows 1 to 7 give one-row bits).
  * Errors: MOE_ERR_INVALID_ARG for a NULL or malformed argument or a shape
  * outside the limits, MOE_ERR_MISALIGNED for a misaligned pointer or stride,
  * MOE_ERR_DEVICE_LOST on a lost ctx; nothing is enqueued on an error. */

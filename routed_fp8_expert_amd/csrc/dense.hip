@@ -7,17 +7,20 @@
 // 128 by the "Plan arms" table); "Precision": fp8/block128x128 weights read
 // bf16 activations.  Two arms, as for the experts:
 //
-//   GEMV (fewer than 32 rows)   a wave holds NR weight rows (16-byte lane
+//   GEMV (fewer than 8 rows)    a wave holds NR weight rows (16-byte lane
 //                               chunks, one scale per chunk: the NR rows share
 //                               a 128-row scale block) and walks the
 //                               activation rows, loading the next row while
 //                               reducing the current one; the NR outputs are
 //                               reduced together (transposing reduction).
-//   matrix cores (>= 32 rows)   a wave owns a 16-row tile by 32 output
-//                               columns over all of K; fp8 codes converted
-//                               exactly to bf16, v_mfma_f32_16x16x32_bf16,
-//                               the block scale applied per 128-wide K block,
-//                               two K blocks of loads in flight.
+//   matrix cores (>= 8 rows)    a workgroup of 8 waves owns 16 output
+//                               columns for every row; its waves split K (at
+//                               most eight 128-wide blocks each, the codes
+//                               held in registers from entry) and the row
+//                               tiles; fp8 codes converted exactly to bf16 for
+//                               v_mfma_f32_16x16x32_bf16, each block's
+//                               products scaled, the partial tiles summed
+//                               through LDS in K-slice order.
 #include "mfma.hpp"
 
 namespace moe {
@@ -78,103 +81,171 @@ __global__ __launch_bounds__(256) void k_dense_gemv(DenseArgs a) {
 
 // ------------------------------------------------------------------ matrix-core arm
 
-struct DenseStage {
-    u32x4 w[2][2];      // [column tile][64-wide half of the K block]
-    u32x4 x[2][2];      // [half][8-value piece]
+// A workgroup of KS x RS waves owns 16*CT output columns for every row.  Wave
+// (ks, rg) owns K slice ks (at most KBMAX 128-wide blocks, contiguous; its
+// weight codes loaded once, at entry, kept in registers) and the 16-row
+// tiles rg, rg + RS, ...; it walks them with the next tile's activations in
+// flight, each tile's K-block products scaled and summed in K order, and
+// leaves its partial tiles in LDS.  Every 8 tiles (128 rows) the partials are
+// summed over the K slices in slice order and rounded once.  A row's result
+// depends on nothing but the row, so any row count gives the same bits for it.
+template <int KBMAX>
+struct DenseXs {
+    u32x4 v[KBMAX][2][2];   // [K block][64-wide half][8-value piece]
 };
 
-__device__ __forceinline__ void dense_load(DenseStage &s, const uint8_t *const (&wd)[2], const uint16_t *xr, int kb,
-                                           int grp) {
+template <int KBMAX>
+__device__ __forceinline__ void dense_load_x(DenseXs<KBMAX> &xs, const DenseArgs &a, int rt, int kb0, int nkb,
+                                             int col, int grp) {
+    const int ra = rt * 16 + col;
+    const uint16_t *xr = a.x + (size_t)(ra < a.R ? ra : 0) * a.ldx;   // rows past R: row 0, results dropped
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int k0 = kb * 128 + c * 64 + grp * 16;
+    for (int b = 0; b < KBMAX; ++b) {
+        const int kb = kb0 + b < nkb ? kb0 + b : nkb - 1;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) s.w[nt][c] = ld16_stream(wd[nt] + k0);
-        s.x[c][0] = ld16(xr + k0);
-        s.x[c][1] = ld16(xr + k0 + 8);
-    }
-}
-
-__device__ __forceinline__ void dense_step(const DenseStage &s, const float (&sc)[2], f32x4 (&acc)[2]) {
-    f32x4 td[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const bf16x8 x0 = as_bf16x8(s.x[c][0]), x1 = as_bf16x8(s.x[c][1]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            td[nt] = mfma(x0, e4m3x8_bf16(s.w[nt][c].x, s.w[nt][c].y), td[nt]);
-            td[nt] = mfma(x1, e4m3x8_bf16(s.w[nt][c].z, s.w[nt][c].w), td[nt]);
+        for (int c = 0; c < 2; ++c) {
+            const int k0 = kb * 128 + c * 64 + grp * 16;
+            xs.v[b][c][0] = ld16(xr + k0);
+            xs.v[b][c][1] = ld16(xr + k0 + 8);
         }
     }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[nt][i] = fmaf(sc[nt], td[nt][i], acc[nt][i]);
 }
 
-// Grid (N/128, ceil(R/16)); a workgroup is 4 waves x 32 output columns.
-__global__ __launch_bounds__(256) void k_dense_mfma(DenseArgs a) {
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-    const int n0 = (blockIdx.x * 4 + wid) * 32;
-    if (n0 >= a.N) return;
-    const int r0 = blockIdx.y * 16;
+// This wave's K-slice products for one tile; nmine is wave-uniform.
+template <int CT, int KBMAX>
+__device__ __forceinline__ void dense_products(f32x4 (&acc)[CT], const u32x4 (&w)[KBMAX][CT][2], float sl,
+                                               const DenseXs<KBMAX> &cur, int nmine) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < KBMAX; ++b) {
+        if (b < nmine) {
+            f32x4 td[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) td[ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const bf16x8 xa = as_bf16x8(cur.v[b][c][0]), xb = as_bf16x8(cur.v[b][c][1]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    u32x4 q = w[b][ct][c];
+                    // more than four 16x128 code tiles a wave: convert per
+                    // tile (converted codes kept across tiles would not fit
+                    // beside the activations)
+                    if (KBMAX * CT > 4) asm volatile("" : "+v"(q));
+                    td[ct] = mfma(xa, e4m3x8_bf16(q.x, q.y), td[ct]);
+                    td[ct] = mfma(xb, e4m3x8_bf16(q.z, q.w), td[ct]);
+                }
+            }
+            const float sc = readlane(sl, b);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[ct][i] = fmaf(sc, td[ct][i], acc[ct][i]);
+        }
+    }
+}
+
+constexpr int kDenseChunkTiles = 8;   // 128 rows of partial tiles in LDS
+
+template <int CT, int KS, int RS, int KBMAX, int D>
+__global__ __launch_bounds__(KS * RS * 64) void k_dense_mfma(DenseArgs a) {
+    static_assert((kDenseChunkTiles / RS) % D == 0, "the activation ring turns whole within a chunk");
+    constexpr int NT = KS * RS * 64;
+    extern __shared__ float part[];   // [kDenseChunkTiles][KS][CT][256]
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = wid % KS, rg = wid / KS;
     const int col = lane & 15, grp = lane >> 4;
+    const int n0 = blockIdx.x * (16 * CT);
     const int nkb = a.K >> 7;
-    const int ra = r0 + col;   // the A-operand row this lane loads (row 0 past R: its outputs are dropped)
-    const uint16_t *xr = a.x + (size_t)(ra < a.R ? ra : 0) * a.ldx;
-    const uint8_t *wd[2];
-    float sl[2];
+    const int kb0 = ks * nkb / KS, nmine = (ks + 1) * nkb / KS - kb0;   // nmine <= KBMAX (host)
+
+    u32x4 w[KBMAX][CT][2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        wd[nt] = a.w + (size_t)(n0 + nt * 16 + col) * a.w_stride;
-        sl[nt] = a.s[(size_t)((n0 + nt * 16) >> 7) * nkb + (lane < nkb ? lane : 0)];
+    for (int b = 0; b < KBMAX; ++b) {
+        const int kb = kb0 + b < nkb ? kb0 + b : nkb - 1;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                w[b][ct][c] = ld16_stream(a.w + (size_t)(n0 + ct * 16 + col) * a.w_stride + kb * 128 + c * 64 + grp * 16);
     }
-    f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-    DenseStage s0, s1;
-    dense_load(s0, wd, xr, 0, grp);
-    if (nkb > 1) dense_load(s1, wd, xr, 1, grp);
-    for (int kb = 0; kb < nkb; kb += 2) {
-        {
-            const float sc[2] = {readlane(sl[0], kb), readlane(sl[1], kb)};
-            dense_step(s0, sc, acc);
+    // one scale per K block: the CT column tiles share a 128-row block
+    const float sl = a.s[(size_t)(n0 >> 7) * nkb + (kb0 + lane < nkb ? kb0 + lane : nkb - 1)];
+
+    // a ring of D activation buffers: this wave's next D-1 tiles in flight
+    const int nrt = (a.R + 15) >> 4;
+    DenseXs<KBMAX> xb[D];
+#pragma unroll
+    for (int d = 0; d + 1 < D; ++d)
+        if (rg + d * RS < nrt) dense_load_x(xb[d], a, rg + d * RS, kb0, nkb, col, grp);
+    for (int t0 = 0; t0 < nrt; t0 += kDenseChunkTiles) {
+#pragma unroll
+        for (int j = 0; j < kDenseChunkTiles / RS; ++j) {
+            const int t = t0 + rg + j * RS;
+            if (t < nrt) {
+                if (D == 1) dense_load_x(xb[0], a, t, kb0, nkb, col, grp);   // no ring: this tile now
+                f32x4 acc[CT];
+                dense_products<CT, KBMAX>(acc, w, sl, xb[j % D], nmine);
+                const int tn = t + (D - 1) * RS;
+                if (D > 1 && tn < nrt) dense_load_x(xb[(j + D - 1) % D], a, tn, kb0, nkb, col, grp);
+                float *pp = part + ((j * RS + rg) * KS + ks) * CT * 256;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pp[ct * 256 + i * 64 + lane] = acc[ct][i];
+            }
         }
-        if (kb + 2 < nkb) dense_load(s0, wd, xr, kb + 2, grp);
-        if (kb + 1 < nkb) {
-            const float sc[2] = {readlane(sl[0], kb + 1), readlane(sl[1], kb + 1)};
-            dense_step(s1, sc, acc);
-            if (kb + 3 < nkb) dense_load(s1, wd, xr, kb + 3, grp);
+        __syncthreads();
+        const int ntile = nrt - t0 < kDenseChunkTiles ? nrt - t0 : kDenseChunkTiles;
+        for (int v = threadIdx.x; v < ntile * CT * 256; v += NT) {
+            const int tt = v / (CT * 256), rem = v - tt * (CT * 256);
+            float sum = 0.0f;
+#pragma unroll
+            for (int k2 = 0; k2 < KS; ++k2) sum += part[(tt * KS + k2) * CT * 256 + rem];
+            const int ct = rem >> 8, i = (rem >> 6) & 3, l = rem & 63;
+            const int r = (t0 + tt) * 16 + 4 * (l >> 4) + i;
+            if (r < a.R) a.y[(size_t)r * a.ldy + n0 + ct * 16 + (l & 15)] = f32_to_bf16(sum);
         }
+        __syncthreads();
     }
-    // D[i][j]: lane holds column j = col, rows 4*grp .. 4*grp+3
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = r0 + 4 * grp + i;
-            if (r < a.R) a.y[(size_t)r * a.ldy + n0 + nt * 16 + col] = f32_to_bf16(acc[nt][i]);
-        }
 }
 
 // ------------------------------------------------------------------ launcher
 
-constexpr int kDenseMfmaRows = 32;   // rows from which the matrix-core arm runs
+// Rows from which the matrix-core arm runs.  Below it the GEMV arm, whose
+// bits for a row do not depend on the call's row count (so one-row calls and
+// calls of up to seven rows agree bit for bit).
+constexpr int kDenseMfmaRows = 8;
 
 template <int CH, int NR>
 static void dense_gemv_launch(const DenseArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((k_dense_gemv<CH, NR>), dim3((a.N + 4 * NR - 1) / (4 * NR)), dim3(256), 0, st, a);
 }
 
+template <int CT, int KS, int RS, int KBMAX, int D>
+static void dense_mfma_launch(const DenseArgs &a, hipStream_t st) {
+    const size_t lds = (size_t)kDenseChunkTiles * KS * CT * 256 * sizeof(float);
+    hipLaunchKernelGGL((k_dense_mfma<CT, KS, RS, KBMAX, D>), dim3(a.N / (16 * CT)), dim3(KS * RS * 64), lds, st, a);
+}
+
 hipError_t launch_dense(const DenseArgs &a, hipStream_t st) {
+    const int nkb = a.K >> 7;
     if (a.R >= kDenseMfmaRows) {
-        hipLaunchKernelGGL(k_dense_mfma, dim3((a.N + 127) / 128, (a.R + 15) / 16), dim3(256), 0, st, a);
+        // eight waves splitting K: two 128-wide blocks a wave (the next tile's
+        // activations in flight) up to K 2048, four up to 4096, eight beyond
+        if (nkb <= 16) dense_mfma_launch<1, 8, 1, 2, 2>(a, st);
+        else if (nkb <= 32) dense_mfma_launch<1, 8, 1, 4, 2>(a, st);
+        else dense_mfma_launch<1, 8, 1, 8, 1>(a, st);
         return hipGetLastError();
     }
     // 16-byte weight chunks per lane and row: K/1024 rounded up to a power of
-    // two; at most 16 weight chunks per lane in all (K <= 8192)
+    // two; four weight rows a wave up to K 2048, two beyond (measured)
     const int ch = (a.K + 1023) / 1024;
-    if (ch <= 1) dense_gemv_launch<1, 8>(a, st);
-    else if (ch <= 2) dense_gemv_launch<2, 8>(a, st);
-    else if (ch <= 4) dense_gemv_launch<4, 4>(a, st);
+    if (ch <= 1) dense_gemv_launch<1, 4>(a, st);
+    else if (ch <= 2) dense_gemv_launch<2, 4>(a, st);
+    else if (ch <= 4) dense_gemv_launch<4, 2>(a, st);
     else dense_gemv_launch<8, 2>(a, st);
     return hipGetLastError();
 }

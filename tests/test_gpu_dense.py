@@ -5,9 +5,10 @@ Bar (f32 accumulation, one bf16 rounding): every output within
 2^-8 |y| + 2^-14 sum_k |x_k W_nk| of the oracle's exact f64 value (the first
 term covers the bf16 rounding, the second the f32 sums of up to 8192 terms),
 and at least 95 % of the outputs bit-equal to the oracle value rounded to
-bf16.  Both arms (GEMV below 32 rows, matrix cores from 32) at ragged row
-counts and every K tier of the GEMV; rows are batch-invariant within an arm;
-strided operands; rejected arguments enqueue nothing.
+bf16.  Both arms (GEMV below 8 rows, matrix cores from 8) at ragged row
+counts on both sides of the switch and every K tier of each arm; rows are
+batch-invariant within an arm (rows 1 to 7 give one-row bits); strided
+operands; rejected arguments enqueue nothing.
 """
 import ctypes as C
 
@@ -62,13 +63,13 @@ def _check(orc, q, s, x, y, sel):
 
 
 CASES = [
-    ("small_384x640", r) for r in (1, 3, 16, 31, 32, 33, 64, 128)
+    ("small_384x640", r) for r in (1, 3, 7, 8, 17, 33, 64, 128)
 ] + [
-    ("up_4096x2048", r) for r in (1, 8, 31, 32, 64, 128)
+    ("up_4096x2048", r) for r in (1, 5, 7, 8, 31, 64, 128)
 ] + [
-    ("down_2048x4096", r) for r in (1, 31, 32, 128)
+    ("down_2048x4096", r) for r in (1, 7, 8, 32, 128)
 ] + [
-    ("wide_256x8192", r) for r in (1, 5, 40)
+    ("wide_256x8192", r) for r in (1, 5, 8, 40)
 ]
 
 
@@ -86,26 +87,31 @@ def test_dense_parity(moe, orc, name, rows):
     _check(orc, q, s, x, y, sel)
 
 
-@pytest.mark.parametrize("name", ["small_384x640", "up_4096x2048"])
+@pytest.mark.parametrize("name", ["small_384x640", "up_4096x2048", "down_2048x4096"])
 def test_dense_batch_invariance(moe, name):
-    """Within an arm a row's bits do not depend on the call's other rows."""
+    """Within an arm a row's bits do not depend on the call's other rows: one
+    to seven rows (GEMV) agree with one-row calls, and matrix-core calls of
+    any row count agree with each other."""
     print(f"dense batch invariance: {name}", flush=True)
     q, s = _weights(name)
     w = moe.DenseWeights(q, s)
     x = syn.make_dense_x(name, 130, q.shape[1], "cuda")
     ctx = moe.Ctx(0)
-    y1 = _run(moe, ctx, w, x[:1])
-    y31 = _run(moe, ctx, w, x[:31])
-    y7 = _run(moe, ctx, w, x[24:31])
-    y32 = _run(moe, ctx, w, x[:32])
+    y7 = _run(moe, ctx, w, x[:7])
+    ones = [_run(moe, ctx, w, x[i:i + 1]) for i in range(7)]
+    y3 = _run(moe, ctx, w, x[2:5])
+    y8 = _run(moe, ctx, w, x[:8])
     y130 = _run(moe, ctx, w, x)
     y45 = _run(moe, ctx, w, x[85:130])
+    y17 = _run(moe, ctx, w, x[100:117])
     ctx.close()
     v = lambda t: t.view(torch.int16)
-    assert torch.equal(v(y31[:1]), v(y1))
-    assert torch.equal(v(y31[24:31]), v(y7))
-    assert torch.equal(v(y130[:32]), v(y32))
+    for i in range(7):
+        assert torch.equal(v(y7[i:i + 1]), v(ones[i])), f"row {i}: seven-row call differs from one-row call"
+    assert torch.equal(v(y7[2:5]), v(y3))
+    assert torch.equal(v(y130[:8]), v(y8))
     assert torch.equal(v(y130[85:130]), v(y45))
+    assert torch.equal(v(y130[100:117]), v(y17))
 
 
 @pytest.mark.parametrize("rows", [7, 48])
