@@ -17,6 +17,9 @@ layers, 512 experts, 10 per token, NVFP4):
   a3b_multi as a3b, rows 2..64, router logits iid U(0,1)
   a17b      H 4096, E 512, k 10, I 1024, nvfp4, 12 layers, router GEMV
   a3b_zipf  as a3b, rows 64 and 512, Gumbel-top-k logits with Zipf(1.2)
+  a3b_i8, a3b_i4, a3b_i4g64   as a3b with int8 per-row, int4 per-row and
+            int4-g64 experts (colibri PR: per-row int4 and int4-g64 experts)
+  tiny_i4g64  as tiny with int4-g64 experts
 """
 from __future__ import annotations
 
@@ -33,6 +36,10 @@ E2M1_MAX = 6.0
 
 FMT_FP8_B128 = 0
 FMT_NVFP4 = 1
+FMT_INT8_ROW = 2
+FMT_INT4_ROW = 3
+FMT_INT4_G64 = 4
+INT_FORMATS = (FMT_INT8_ROW, FMT_INT4_ROW, FMT_INT4_G64)
 
 
 @dataclass(frozen=True)
@@ -60,6 +67,10 @@ WORKLOADS: Dict[str, Workload] = {
     "a17b": Workload("a17b", 4096, 512, 10, 1024, 1024, FMT_NVFP4, 12, [1, 8]),
     "a3b_zipf": Workload("a3b_zipf", 2048, 256, 8, 512, 512, FMT_FP8_B128, 40, [64, 512],
                          "zipf"),
+    "a3b_i8": Workload("a3b_i8", 2048, 256, 8, 512, 512, FMT_INT8_ROW, 40, [1, 8]),
+    "a3b_i4": Workload("a3b_i4", 2048, 256, 8, 512, 512, FMT_INT4_ROW, 40, [1, 8]),
+    "a3b_i4g64": Workload("a3b_i4g64", 2048, 256, 8, 512, 512, FMT_INT4_G64, 40, [1, 8]),
+    "tiny_i4g64": Workload("tiny_i4g64", 256, 16, 2, 128, 128, FMT_INT4_G64, 1, [1], "gemv", True, False),
 }
 
 
@@ -118,6 +129,29 @@ def quant_nvfp4(w: torch.Tensor):
     return packed, sc.view(torch.uint8).contiguous(), g.to(torch.float32).contiguous()
 
 
+def quant_int(w: torch.Tensor, fmt: int):
+    """Encode f32 weights [..., O, I] in an integer format: symmetric codes
+    round(w / scale) clamped to +-qmax (127 for int8, 7 for int4), one f32
+    scale amax/qmax per group of G consecutive input columns of a row (G = I
+    per row, 64 for g64; 1 for an all-zero group).  int8 codes are bytes
+    [..., O, I]; int4 codes two per byte, the even column in the low nibble,
+    [..., O, I/2].  Returns (codes u8, scales f32 [..., O, I/G])."""
+    *lead, O, I = w.shape
+    G = 64 if fmt == FMT_INT4_G64 else I
+    qmax = 127.0 if fmt == FMT_INT8_ROW else 7.0
+    assert I % G == 0
+    b = w.reshape(*lead, O, I // G, G)
+    amax = b.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / qmax, torch.ones_like(amax))
+    code = torch.round(b / scale[..., None]).clamp(-qmax, qmax).to(torch.int32).reshape(*lead, O, I)
+    if fmt == FMT_INT8_ROW:
+        packed = (code & 0xFF).to(torch.uint8)
+    else:
+        nib = code & 0xF
+        packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).to(torch.uint8)
+    return packed.contiguous(), scale.to(torch.float32).contiguous()
+
+
 # ----------------------------------------------------------------- weights
 
 EXPERT_CHUNK = 32
@@ -130,6 +164,9 @@ def _normal(shape, std, gen, device):
 def _encode(w: torch.Tensor, fmt: int):
     if fmt == FMT_FP8_B128:
         q, s = quant_fp8_b128(w)
+        return q, s, None
+    if fmt in INT_FORMATS:
+        q, s = quant_int(w, fmt)
         return q, s, None
     return quant_nvfp4(w)
 
@@ -251,10 +288,16 @@ def effective_weight_bytes(wl: Workload, distinct_routed: int, router_gemv: bool
     H, I, Is, E = wl.hidden, wl.inter, wl.shared_inter, wl.n_experts
 
     def expert_bytes(inter):
+        n = 2 * inter * H + H * inter          # weights of gate|up and down
         if wl.fmt == FMT_FP8_B128:
-            return (2 * inter * H + H * inter) + 4 * ((2 * inter // 128) * (H // 128)
-                                                      + (H // 128) * (inter // 128))
-        return ((2 * inter * H + H * inter) // 2 + (2 * inter * H + H * inter) // 16 + 8)
+            return n + 4 * ((2 * inter // 128) * (H // 128) + (H // 128) * (inter // 128))
+        if wl.fmt == FMT_INT8_ROW:
+            return n + 4 * (2 * inter + H)
+        if wl.fmt == FMT_INT4_ROW:
+            return n // 2 + 4 * (2 * inter + H)
+        if wl.fmt == FMT_INT4_G64:
+            return n // 2 + 4 * (n // 64)
+        return n // 2 + n // 16 + 8
 
     b = distinct_routed * expert_bytes(I)
     if Is > 0:

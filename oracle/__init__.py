@@ -17,6 +17,10 @@ from . import build as _build
 
 FMT_FP8_B128 = 0
 FMT_NVFP4 = 1
+FMT_INT8_ROW = 2
+FMT_INT4_ROW = 3
+FMT_INT4_G64 = 4
+INT_FORMATS = (FMT_INT8_ROW, FMT_INT4_ROW, FMT_INT4_G64)
 
 _lib = None
 
@@ -47,6 +51,11 @@ def lib():
         L.orc_e4m3_to_f32.restype = C.c_float
         L.orc_e2m1_to_f32.argtypes = [C.c_uint8]
         L.orc_e2m1_to_f32.restype = C.c_float
+        L.orc_int8_to_f32.argtypes = [C.c_uint8]
+        L.orc_int8_to_f32.restype = C.c_float
+        L.orc_int4_to_f32.argtypes = [C.c_uint8]
+        L.orc_int4_to_f32.restype = C.c_float
+        L.orc_dequant_int.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
         L.orc_set_threads.argtypes = [C.c_int]
         L.orc_get_threads.restype = C.c_int
         L.orc_dequant_fp8.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
@@ -110,6 +119,31 @@ def e2m1_to_f32(nibbles) -> np.ndarray:
     return np.array([f(int(v)) for v in c], dtype=np.float32).reshape(np.shape(nibbles))
 
 
+def int8_to_f32(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8).ravel()
+    f = lib().orc_int8_to_f32
+    return np.array([f(int(v)) for v in c], dtype=np.float32).reshape(np.shape(codes))
+
+
+def int4_to_f32(nibbles) -> np.ndarray:
+    c = np.asarray(nibbles, dtype=np.uint8).ravel()
+    f = lib().orc_int4_to_f32
+    return np.array([f(int(v)) for v in c], dtype=np.float32).reshape(np.shape(nibbles))
+
+
+def dequant_int(fmt: int, q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Integer-format codes (int8 [O][I] bytes, int4 [O][I/2] bytes) with f32
+    scales [O][I/G] to the f32 matrix [O][I]."""
+    q = _c(q, np.uint8)
+    scale = _c(scale, np.float32)
+    O, nb = q.shape
+    I = nb if fmt == FMT_INT8_ROW else 2 * nb
+    W = np.empty((O, I), np.float32)
+    if lib().orc_dequant_int(int(fmt), _ptr(q), _ptr(scale), O, I, _ptr(W)) != 0:
+        raise ValueError("orc_dequant_int rejected its arguments")
+    return W
+
+
 def dequant_fp8(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
     q = _c(q, np.uint8)
     scale = _c(scale, np.float32)
@@ -135,7 +169,8 @@ def dequant_nvfp4(q: np.ndarray, scale: np.ndarray, g: float) -> np.ndarray:
 @dataclass
 class Expert:
     """One expert's stored weights (numpy).  fp8: gu_s/dn_s are f32 block
-    scales; nvfp4: e4m3 scale bytes plus the f32 globals gu_g/dn_g."""
+    scales; nvfp4: e4m3 scale bytes plus the f32 globals gu_g/dn_g; integer
+    formats: f32 row or group scales."""
     gu_q: np.ndarray
     gu_s: np.ndarray
     dn_q: np.ndarray
@@ -156,7 +191,7 @@ class Layer:
                  experts: Optional[Dict[int, Expert]] = None, shared: Optional[Expert] = None):
         self.hidden, self.n_experts, self.top_k = int(hidden), int(n_experts), int(top_k)
         self.inter, self.shared_inter, self.fmt = int(inter), int(shared_inter), int(fmt)
-        sdt = np.float32 if fmt == FMT_FP8_B128 else np.uint8
+        sdt = np.uint8 if fmt == FMT_NVFP4 else np.float32
         self._keep = []
         self.router_w = _c(router_w, np.uint16)
         self.router_bias = _c(router_bias, np.float32)
@@ -225,7 +260,7 @@ def group(ids: np.ndarray, n_experts: int):
 
 
 def expert_apply(layer: Layer, expert: Expert, inter: int, x_row: np.ndarray) -> np.ndarray:
-    sdt = np.float32 if layer.fmt == FMT_FP8_B128 else np.uint8
+    sdt = np.uint8 if layer.fmt == FMT_NVFP4 else np.float32
     keep = []
     cx = layer._mk(expert, sdt)
     keep.append(cx)

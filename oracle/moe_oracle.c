@@ -85,6 +85,21 @@ float orc_e2m1_to_f32(uint8_t nib)
     return (float)(s ? -v : v);
 }
 
+/* Two's-complement 8-bit integer: bytes 0..127 are 0..127, 128..255 are
+ * -128..-1. */
+float orc_int8_to_f32(uint8_t c)
+{
+    int v = c;
+    return (float)(v >= 128 ? v - 256 : v);
+}
+
+/* Two's-complement 4-bit integer: nibbles 0..7 are 0..7, 8..15 are -8..-1. */
+float orc_int4_to_f32(uint8_t nib)
+{
+    int v = nib & 15;
+    return (float)(v >= 8 ? v - 16 : v);
+}
+
 /* ---------------------------------------------------------------- weights */
 
 /* fp8 block-128x128: scale array is [O/128][I/128], one f32 per block;
@@ -110,11 +125,37 @@ static float w_nvfp4(const uint8_t *q, const uint8_t *scale, float g, int I, int
     return (float)(code * sc * (double)g);
 }
 
+/* Integer experts (colibri PR: a per-row int4 checkpoint of Qwen3.6, an
+ * int4-g64 expert sidecar, int8 rows in its decode GEMV).  The layout is a
+ * reading: symmetric two's-complement codes; int4 two per byte with the even
+ * column in the low nibble; one f32 scale per G consecutive input columns of
+ * a row (G = the row length for the per-row formats, 64 for g64), scale
+ * array [O][I/G]; the scale multiplies. */
+static int int_group(int fmt, int I) { return fmt == ORC_FMT_INT4_G64 ? 64 : I; }
+
+static float w_int(int fmt, const uint8_t *q, const float *scale, int I, int o, int i)
+{
+    double code;
+    if (fmt == ORC_FMT_INT8_ROW) {
+        code = orc_int8_to_f32(q[(size_t)o * (size_t)I + (size_t)i]);
+    } else {
+        uint8_t byte = q[(size_t)o * (size_t)(I / 2) + (size_t)(i / 2)];
+        code = orc_int4_to_f32((i & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15));
+    }
+    const int G = int_group(fmt, I);
+    double sc = scale[(size_t)o * (size_t)(I / G) + (size_t)(i / G)];
+    return (float)(code * sc);
+}
+
+static int known_format(int fmt) { return fmt >= ORC_FMT_FP8_B128 && fmt <= ORC_FMT_INT4_G64; }
+
 static float weight(int fmt, const uint8_t *q, const void *s, float g, int I, int o, int i)
 {
     if (fmt == ORC_FMT_NVFP4)
         return w_nvfp4(q, (const uint8_t *)s, g, I, o, i);
-    return w_fp8(q, (const float *)s, I, o, i);
+    if (fmt == ORC_FMT_FP8_B128)
+        return w_fp8(q, (const float *)s, I, o, i);
+    return w_int(fmt, q, (const float *)s, I, o, i);
 }
 
 int orc_dequant_fp8(const uint8_t *q, const float *scale, int O, int I, float *W)
@@ -134,6 +175,20 @@ int orc_dequant_nvfp4(const uint8_t *q, const uint8_t *scale, float g, int O, in
     for (int o = 0; o < O; o++)
         for (int i = 0; i < I; i++)
             W[(size_t)o * I + i] = w_nvfp4(q, scale, g, I, o, i);
+    return 0;
+}
+
+int orc_dequant_int(int fmt, const uint8_t *q, const float *scale, int O, int I, float *W)
+{
+    if (!q || !scale || !W || O <= 0 || I <= 0)
+        return -1;
+    if (fmt != ORC_FMT_INT8_ROW && fmt != ORC_FMT_INT4_ROW && fmt != ORC_FMT_INT4_G64)
+        return -1;
+    if ((fmt != ORC_FMT_INT8_ROW && I % 2) || (fmt == ORC_FMT_INT4_G64 && I % 64))
+        return -1;
+    for (int o = 0; o < O; o++)
+        for (int i = 0; i < I; i++)
+            W[(size_t)o * I + i] = w_int(fmt, q, scale, I, o, i);
     return 0;
 }
 
@@ -268,7 +323,8 @@ static double silu(double t) { return t / (1.0 + exp(-t)); }
 int orc_expert_apply(const orc_layer *L, const orc_expert *X, int inter,
                      const uint16_t *x_row, double *d)
 {
-    if (!L || !X || !x_row || !d || !X->gu_q || !X->gu_s || !X->dn_q || !X->dn_s || inter <= 0)
+    if (!L || !X || !x_row || !d || !X->gu_q || !X->gu_s || !X->dn_q || !X->dn_s || inter <= 0 ||
+        !known_format(L->fmt))
         return -1;
     const int H = L->hidden, fmt = L->fmt;
     float *xf = (float *)malloc(sizeof(float) * (size_t)H);

@@ -30,6 +30,12 @@
  *                      row-major [O][I/2] bytes; one e4m3 scale per 16
  *                      consecutive input columns, array [O][I/16]; one f32
  *                      global scale per matrix; w = code*scale*global.
+ *   ORC_FMT_INT8_ROW : two's-complement int8 codes, row-major [O][I]; one f32
+ *                      scale per row, array [O]; w = code*scale.
+ *   ORC_FMT_INT4_ROW : two's-complement int4 codes, two per byte (low nibble =
+ *                      even column), [O][I/2] bytes; one f32 scale per row.
+ *   ORC_FMT_INT4_G64 : int4 codes as above; one f32 scale per 64 consecutive
+ *                      input columns of a row, array [O][I/64].
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -39,7 +45,7 @@
 extern "C" {
 #endif
 
-enum { ORC_FMT_FP8_B128 = 0, ORC_FMT_NVFP4 = 1 };
+enum { ORC_FMT_FP8_B128 = 0, ORC_FMT_NVFP4 = 1, ORC_FMT_INT8_ROW = 2, ORC_FMT_INT4_ROW = 3, ORC_FMT_INT4_G64 = 4 };
 
 typedef struct orc_expert {
     const uint8_t *gu_q;   /* gate|up codes, [2I][H] (fp8) or [2I][H/2] (nvfp4) */
@@ -68,6 +74,8 @@ float    orc_bf16_to_f32(uint16_t b);
 uint16_t orc_f32_to_bf16_rne(float f);
 float    orc_e4m3_to_f32(uint8_t code);
 float    orc_e2m1_to_f32(uint8_t nibble);
+float    orc_int8_to_f32(uint8_t code);
+float    orc_int4_to_f32(uint8_t nibble);
 
 void orc_set_threads(int n);
 int  orc_get_threads(void);
@@ -75,6 +83,9 @@ int  orc_get_threads(void);
 /* Dequantised f32 weight matrices (O x I), for tests of the format decoders. */
 int orc_dequant_fp8(const uint8_t *q, const float *scale, int O, int I, float *W);
 int orc_dequant_nvfp4(const uint8_t *q, const uint8_t *scale, float g, int O, int I, float *W);
+/* The integer formats (fmt = ORC_FMT_INT8_ROW, _INT4_ROW or _INT4_G64); scale
+ * is f32 [O][I/G] with G = I for the per-row formats and 64 for g64. */
+int orc_dequant_int(int fmt, const uint8_t *q, const float *scale, int O, int I, float *W);
 
 /* Router logits f32 [R][E]. */
 int orc_router_logits(const orc_layer *L, const uint16_t *x, int R, float *logits);

@@ -86,12 +86,13 @@ def _tiny():
     return wl, syn.make_layer_weights(wl, 0)
 
 
-def _textbook_layer(wl, W, x_bits, logits=None, residual=None):
+def _textbook_layer(wl, W, x_bits, logits=None, residual=None, deq=None):
     """Independent float64 formulation: numpy matmuls over weights decoded by
-    torch's e4m3 cast, scipy softmax, python sort."""
-    def deq(q, s):
-        v = torch.from_numpy(host(q)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
-        return (v * np.kron(host(s).astype(np.float64), np.ones((128, 128)))).astype(np.float32)
+    torch's e4m3 cast (or the given decoder), scipy softmax, python sort."""
+    if deq is None:
+        def deq(q, s):
+            v = torch.from_numpy(host(q)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+            return (v * np.kron(host(s).astype(np.float64), np.ones((128, 128)))).astype(np.float32)
 
     xf = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).double().numpy()
     if logits is None:
