@@ -29,6 +29,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FMT_DTYPE = {0: "fp8e4m3", 1: "nvfp4", 2: "int8", 3: "int4", 4: "int4"}
+FMT_NAME = {0: "fp8 e4m3 block-128", 1: "nvfp4", 2: "int8 per-row", 3: "int4 per-row", 4: "int4-g64"}
 METRIC = "us per MoE layer + effective weight GB/s (% of HBM peak), 35B-A3B shape, n=1"
 
 
@@ -407,10 +409,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3-w/bf16-x/f32-acc" if wl.fmt == syn.FMT_FP8_B128 else "nvfp4-w/bf16-x/f32-acc",
+        "dtype": FMT_DTYPE[wl.fmt] + "-w/bf16-x/f32-acc",
         "data": "synthetic (seeded; weights N(0,0.02) quantised, activations N(0,1) RMS-normalised)",
         "config": {"workload": f"{wl.name}: hidden {H}, {E} experts top-{k}, inter {I}, shared inter {Is}, "
-                               f"{'fp8 e4m3 block-128' if wl.fmt == 0 else 'nvfp4'} weights, "
+                               f"{FMT_NAME[wl.fmt]} weights, "
                                f"{rows} row(s), {layers} layers back to back",
                    "rows": rows, "layers": layers, "launch": best_mode,
                    "router": wl.router, "epilogue": "rmsnorm" if args.norm else None},

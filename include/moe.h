@@ -59,7 +59,7 @@ extern "C" {
 #endif
 
 #define MOE_API __attribute__((visibility("default")))
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 enum moe_status {
     MOE_OK = 0,
@@ -82,6 +82,16 @@ enum moe_weight_format {
      * global ("Inspecting Qwen3.5-397B-A17B-NVFP4", "The Architectural
      * Revelations": NVFP4 weights). */
     MOE_WFMT_NVFP4 = 1,
+    /* Integer experts (colibri PR: int8 rows in its decode GEMV, a per-row
+     * int4 checkpoint, an int4-g64 expert sidecar); the layouts are readings
+     * of those names: two's-complement codes, one f32 scale per group of G
+     * consecutive input columns of a row, array [out][in/G]; w = code * scale.
+     * Served by the GEMV arm (multi-row steps of any size) and the
+     * three-launch one-row path. */
+    MOE_WFMT_INT8_ROW = 2,      /* int8 codes [out][in] bytes; G = in (one scale per row) */
+    MOE_WFMT_INT4_ROW = 3,      /* int4 codes two per byte (even column in the low nibble),
+                                 * [out][in/2] bytes; G = in */
+    MOE_WFMT_INT4_G64 = 4,      /* int4 codes as above; G = 64 */
 };
 
 typedef struct moe_ctx moe_ctx;
@@ -89,12 +99,14 @@ typedef struct moe_ctx moe_ctx;
 /* One family of experts (the routed ones, or the single shared expert) stored
  * as per-expert slabs at a fixed byte stride.  Device pointers. */
 typedef struct moe_expert_weights {
-    const void *gate_up;        /* [2I][H] codes (fp8: 1 B each; nvfp4: H/2 B per row) */
-    const void *gate_up_scale;  /* fp8: f32 [2I/128][H/128]; nvfp4: e4m3 [2I][H/16] */
-    const float *gate_up_global;/* nvfp4: f32 per expert (stride 1 float); fp8: NULL */
-    const void *down;           /* [H][I] codes (fp8) or [H][I/2] bytes (nvfp4) */
-    const void *down_scale;     /* fp8: f32 [H/128][I/128]; nvfp4: e4m3 [H][I/16] */
-    const float *down_global;   /* nvfp4: f32 per expert; fp8: NULL */
+    const void *gate_up;        /* [2I][H] codes (fp8, int8: 1 B each; nvfp4, int4: H/2 B per row) */
+    const void *gate_up_scale;  /* fp8: f32 [2I/128][H/128]; nvfp4: e4m3 [2I][H/16];
+                                 * integer formats: f32 [2I][H/G] */
+    const float *gate_up_global;/* nvfp4: f32 per expert (stride 1 float); others: NULL */
+    const void *down;           /* [H][I] codes (fp8, int8) or [H][I/2] bytes (nvfp4, int4) */
+    const void *down_scale;     /* fp8: f32 [H/128][I/128]; nvfp4: e4m3 [H][I/16];
+                                 * integer formats: f32 [H][I/G] */
+    const float *down_global;   /* nvfp4: f32 per expert; others: NULL */
     int64_t gate_up_stride;     /* bytes from one expert's gate_up to the next */
     int64_t gate_up_scale_stride;
     int64_t down_stride;

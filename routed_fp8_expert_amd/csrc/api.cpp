@@ -90,7 +90,7 @@ int validate_family(const moe_expert_weights &f, int fmt, bool many) {
     if (!f.gate_up || !f.gate_up_scale || !f.down || !f.down_scale) return MOE_ERR_INVALID_ARG;
     if (fmt == MOE_WFMT_NVFP4 && (!f.gate_up_global || !f.down_global)) return MOE_ERR_INVALID_ARG;
     if (!aligned(f.gate_up, 16) || !aligned(f.down, 16)) return MOE_ERR_MISALIGNED;
-    const size_t salign = fmt == MOE_WFMT_FP8_E4M3_B128 ? 4 : 2;
+    const size_t salign = fmt == MOE_WFMT_NVFP4 ? 2 : 4;   // e4m3 byte pairs, else f32
     if (!aligned(f.gate_up_scale, salign) || !aligned(f.down_scale, salign)) return MOE_ERR_MISALIGNED;
     if (fmt == MOE_WFMT_NVFP4 && (!aligned(f.gate_up_global, 4) || !aligned(f.down_global, 4)))
         return MOE_ERR_MISALIGNED;
@@ -109,9 +109,9 @@ int validate_family(const moe_expert_weights &f, int fmt, bool many) {
 // routed and shared; at most 4 chunks per lane.
 bool down_shape_ok(const moe_layer_weights *w) {
     const int fmt = w->weight_format;
-    const int nch = (fmt == MOE_WFMT_FP8_E4M3_B128 ? w->inter : w->inter / 2) / 16;
+    const int nch = moe::fmt_row_bytes(fmt, w->inter) / 16;
     const int ie = std::max(w->inter, w->shared_inter);
-    const int nchmax = (fmt == MOE_WFMT_FP8_E4M3_B128 ? ie : ie / 2) / 16;
+    const int nchmax = moe::fmt_row_bytes(fmt, ie) / 16;
     const int lpr = nch >= 64 ? 64 : nch >= 32 ? 32 : nch >= 16 ? 16 : 8;
     return (nchmax + lpr - 1) / lpr <= 4;
 }
@@ -119,7 +119,7 @@ bool down_shape_ok(const moe_layer_weights *w) {
 int validate_weights(const moe_layer_weights *w) {
     if (!w) return MOE_ERR_INVALID_ARG;
     if (w->struct_size != sizeof(moe_layer_weights)) return MOE_ERR_INVALID_ARG;
-    if (w->weight_format != MOE_WFMT_FP8_E4M3_B128 && w->weight_format != MOE_WFMT_NVFP4)
+    if (w->weight_format < MOE_WFMT_FP8_E4M3_B128 || w->weight_format > MOE_WFMT_INT4_G64)
         return MOE_ERR_INVALID_ARG;
     const int H = w->hidden, E = w->n_experts, k = w->top_k, I = w->inter, Is = w->shared_inter;
     if (H <= 0 || E <= 0 || k <= 0 || I <= 0 || Is < 0) return MOE_ERR_INVALID_ARG;

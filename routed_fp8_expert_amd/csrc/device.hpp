@@ -125,6 +125,71 @@ __device__ __forceinline__ float dot8_e2m1_f32(uint32_t w, f32x4 h0, f32x4 h1, f
     return a;
 }
 
+// Two's-complement integer codes (the integer expert formats).  A
+// sign-extending bit-field extract and an int -> f32 convert give the exact
+// value; integers of at most 8 significant bits are exact in bf16, so the
+// upper half of the f32 is the bf16, and two of them pack into a pair.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+    return (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xffff0000u);
+}
+// int8 code in byte B of w.
+template <int B>
+__device__ __forceinline__ float i8_f32(uint32_t w) {
+    return (float)((int)(w << (24 - 8 * B)) >> 24);
+}
+// int4 code in nibble N of w (nibble 0 = bits 0..3).
+template <int N>
+__device__ __forceinline__ float i4_f32(uint32_t w) {
+    return (float)((int)(w << (28 - 4 * N)) >> 28);
+}
+
+// 16 int8 codes (one 16-byte chunk) . 16 bf16 activations (two 16-byte chunks).
+__device__ __forceinline__ float dot16_i8_bf16(u32x4 w, u32x4 xa, u32x4 xb) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+    float a = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a = dot2(as_bf16x2(pack_bf16_exact(i8_f32<0>(ws[q]), i8_f32<1>(ws[q]))), xs[2 * q], a);
+        a = dot2(as_bf16x2(pack_bf16_exact(i8_f32<2>(ws[q]), i8_f32<3>(ws[q]))), xs[2 * q + 1], a);
+    }
+    return a;
+}
+// 16 int8 codes . 16 f32 activations (four 16-byte chunks).
+__device__ __forceinline__ float dot16_i8_f32(u32x4 w, const f32x4 *h) {
+    float a = 0.0f;
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a = fmaf(i8_f32<0>(ws[q]), h[q].x, a);
+        a = fmaf(i8_f32<1>(ws[q]), h[q].y, a);
+        a = fmaf(i8_f32<2>(ws[q]), h[q].z, a);
+        a = fmaf(i8_f32<3>(ws[q]), h[q].w, a);
+    }
+    return a;
+}
+// 8 int4 codes (one dword, the even column in the low nibble) . 8 bf16
+// activations (one 16-byte chunk).
+__device__ __forceinline__ float dot8_i4_bf16(uint32_t w, u32x4 x, float a) {
+    a = dot2(as_bf16x2(pack_bf16_exact(i4_f32<0>(w), i4_f32<1>(w))), x.x, a);
+    a = dot2(as_bf16x2(pack_bf16_exact(i4_f32<2>(w), i4_f32<3>(w))), x.y, a);
+    a = dot2(as_bf16x2(pack_bf16_exact(i4_f32<4>(w), i4_f32<5>(w))), x.z, a);
+    a = dot2(as_bf16x2(pack_bf16_exact(i4_f32<6>(w), i4_f32<7>(w))), x.w, a);
+    return a;
+}
+// 8 int4 codes . 8 f32 activations (two 16-byte chunks).
+__device__ __forceinline__ float dot8_i4_f32(uint32_t w, f32x4 h0, f32x4 h1, float a) {
+    a = fmaf(i4_f32<0>(w), h0.x, a);
+    a = fmaf(i4_f32<1>(w), h0.y, a);
+    a = fmaf(i4_f32<2>(w), h0.z, a);
+    a = fmaf(i4_f32<3>(w), h0.w, a);
+    a = fmaf(i4_f32<4>(w), h1.x, a);
+    a = fmaf(i4_f32<5>(w), h1.y, a);
+    a = fmaf(i4_f32<6>(w), h1.z, a);
+    a = fmaf(i4_f32<7>(w), h1.w, a);
+    return a;
+}
+
 // 8 bf16 weights . 8 bf16 activations (one 16-byte chunk each).
 __device__ __forceinline__ float dot8_bf16(u32x4 w, u32x4 x, float a) {
     a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), a, false);

@@ -525,7 +525,20 @@ __global__ void k_decode_probe(int fmt, const uint8_t *codes, float *out, int n)
 
 static int routed_tasks(const FfnArgs &a) { return a.R == 1 ? a.k : a.max_routed_tasks; }
 static int n_tasks(const FfnArgs &a) { return routed_tasks(a) + (a.shared.inter > 0 && !a.shared_mfma ? 1 : 0); }
-static int gate_up_chunks(int fmt, int H) { return ((fmt == kFp8 ? H : H / 2) / 16 + kWave - 1) / kWave; }
+static int gate_up_chunks(int fmt, int H) { return (fmt_row_bytes(fmt, H) / 16 + kWave - 1) / kWave; }
+
+// One instantiation per weight format: FN<FMT>(args...).
+#define MOE_FMT_DISPATCH(FMT_VALUE, FN, ...)                                                      \
+    do {                                                                                          \
+        switch (FMT_VALUE) {                                                                      \
+            case kFp8: return FN<kFp8>(__VA_ARGS__);                                              \
+            case kNvfp4: return FN<kNvfp4>(__VA_ARGS__);                                          \
+            case kInt8Row: return FN<kInt8Row>(__VA_ARGS__);                                      \
+            case kInt4Row: return FN<kInt4Row>(__VA_ARGS__);                                      \
+            case kInt4G64: return FN<kInt4G64>(__VA_ARGS__);                                      \
+            default: return hipErrorInvalidValue;                                                 \
+        }                                                                                         \
+    } while (0)
 static int max_inter(const FfnArgs &a) { return a.routed.inter > a.shared.inter ? a.routed.inter : a.shared.inter; }
 
 #define MOE_CH_DISPATCH(CH_VALUE, LAUNCH)                                                             \
@@ -558,7 +571,7 @@ static hipError_t gate_up_fmt(const FfnArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_gate_up(const FfnArgs &a, hipStream_t st) {
-    return a.fmt == kFp8 ? gate_up_fmt<kFp8>(a, st) : gate_up_fmt<kNvfp4>(a, st);
+    MOE_FMT_DISPATCH(a.fmt, gate_up_fmt, a, st);
 }
 
 template <int FMT, int NCH, int NV>
@@ -594,7 +607,7 @@ static hipError_t lead_nch(const RouteArgs &r, const FfnArgs &a, hipStream_t st)
 }
 
 hipError_t launch_lead_r1(const RouteArgs &r, const FfnArgs &a, hipStream_t st) {
-    return a.fmt == kFp8 ? lead_nch<kFp8>(r, a, st) : lead_nch<kNvfp4>(r, a, st);
+    MOE_FMT_DISPATCH(a.fmt, lead_nch, r, a, st);
 }
 
 template <int FMT>
@@ -605,7 +618,7 @@ static hipError_t gate_up_r1_fmt(const FfnArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_gate_up_r1(const FfnArgs &a, hipStream_t st) {
-    return a.fmt == kFp8 ? gate_up_r1_fmt<kFp8>(a, st) : gate_up_r1_fmt<kNvfp4>(a, st);
+    MOE_FMT_DISPATCH(a.fmt, gate_up_r1_fmt, a, st);
 }
 
 constexpr size_t kMaxHLds = 64 * 1024;
@@ -660,10 +673,10 @@ static hipError_t down_grouped_fmt(const FfnArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_down_blend_r1(const FfnArgs &a, hipStream_t st) {
-    return a.fmt == kFp8 ? down_r1_fmt<kFp8>(a, st) : down_r1_fmt<kNvfp4>(a, st);
+    MOE_FMT_DISPATCH(a.fmt, down_r1_fmt, a, st);
 }
 hipError_t launch_down_grouped(const FfnArgs &a, hipStream_t st) {
-    return a.fmt == kFp8 ? down_grouped_fmt<kFp8>(a, st) : down_grouped_fmt<kNvfp4>(a, st);
+    MOE_FMT_DISPATCH(a.fmt, down_grouped_fmt, a, st);
 }
 hipError_t launch_blend(const FfnArgs &a, hipStream_t st) {
     if (a.norm_w)

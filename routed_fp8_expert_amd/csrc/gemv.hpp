@@ -10,7 +10,7 @@
 
 namespace moe {
 
-enum : int { kFp8 = 0, kNvfp4 = 1 };
+
 constexpr int kMaxSlots = 17;          // top_k <= 16, plus the shared expert
 constexpr int kPairsPerWave = 2;       // gate/up (i, I+i) row pairs per wave
 
@@ -249,39 +249,54 @@ __device__ __forceinline__ void stage_row(const uint16_t *src, int H, float *v) 
 
 // ------------------------------------------------------------------ weight chunks
 
-template <int FMT> __device__ __forceinline__ int row_bytes(int cols) { return FMT == kFp8 ? cols : cols / 2; }
-template <int FMT> constexpr int cols_per_chunk() { return FMT == kFp8 ? 16 : 32; }
+template <int FMT> __device__ __forceinline__ int row_bytes(int cols) { return fmt_row_bytes(FMT, cols); }
+template <int FMT> constexpr int cols_per_chunk() { return byte_codes(FMT) ? 16 : 32; }
 
 // Scale(s) of 16-byte chunk `c` of weight row `row` of a matrix with `cols`
 // columns.  fp8: one f32 per 128x128 block; nvfp4: two e4m3 bytes (two
-// 16-column groups).
+// 16-column groups); int8/int4 per row: the row's f32; int4-g64: the f32 of
+// the 64-column group holding the chunk's 32 columns.
 template <int FMT>
 __device__ __forceinline__ f32x2 chunk_scale(const uint8_t *s, int row, int cols, int c) {
-    if (FMT == kFp8) {
-        const float *sf = reinterpret_cast<const float *>(s);
+    const float *sf = reinterpret_cast<const float *>(s);
+    if constexpr (FMT == kFp8) {
         const float v = sf[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)];
         return f32x2{v, v};
-    } else {
+    } else if constexpr (FMT == kNvfp4) {
         const uint16_t b = *reinterpret_cast<const uint16_t *>(s + (size_t)row * (cols >> 4) + 2 * c);
         return f32x2{e4m3_f32(b, 0), e4m3_f32(b, 1)};
+    } else if constexpr (FMT == kInt4G64) {
+        const float v = sf[(size_t)row * (cols >> 6) + (c >> 1)];
+        return f32x2{v, v};
+    } else {
+        const float v = sf[row];
+        return f32x2{v, v};
     }
 }
 
 // 16-byte loads of activation per weight chunk: bf16 (gate/up) and f32 (down).
-template <int FMT> constexpr int x_quads() { return FMT == kFp8 ? 2 : 4; }
-template <int FMT> constexpr int h_quads() { return FMT == kFp8 ? 4 : 8; }
+template <int FMT> constexpr int x_quads() { return byte_codes(FMT) ? 2 : 4; }
+template <int FMT> constexpr int h_quads() { return byte_codes(FMT) ? 4 : 8; }
 
 // One 16-byte weight chunk . the chunk's bf16 activations (in registers).
 template <int FMT>
 __device__ __forceinline__ float chunk_dot_bf16(u32x4 w, f32x2 sc, const u32x4 (&x)[x_quads<FMT>()]) {
     if constexpr (FMT == kFp8) {
         return sc.x * dot16_e4m3_bf16(w, x[0], x[1]);
-    } else {
+    } else if constexpr (FMT == kInt8Row) {
+        return sc.x * dot16_i8_bf16(w, x[0], x[1]);
+    } else if constexpr (FMT == kNvfp4) {
         float a = dot8_e2m1_bf16(w.x, x[0], 0.0f);
         a = dot8_e2m1_bf16(w.y, x[1], a);
         float b = dot8_e2m1_bf16(w.z, x[2], 0.0f);
         b = dot8_e2m1_bf16(w.w, x[3], b);
         return sc.x * a + sc.y * b;
+    } else {
+        float a = dot8_i4_bf16(w.x, x[0], 0.0f);
+        a = dot8_i4_bf16(w.y, x[1], a);
+        a = dot8_i4_bf16(w.z, x[2], a);
+        a = dot8_i4_bf16(w.w, x[3], a);
+        return sc.x * a;
     }
 }
 template <int FMT>
@@ -302,12 +317,20 @@ template <int FMT>
 __device__ __forceinline__ float chunk_dot_f32(u32x4 w, f32x2 sc, const f32x4 (&h)[h_quads<FMT>()]) {
     if constexpr (FMT == kFp8) {
         return sc.x * dot16_e4m3_f32(w, h);
-    } else {
+    } else if constexpr (FMT == kInt8Row) {
+        return sc.x * dot16_i8_f32(w, h);
+    } else if constexpr (FMT == kNvfp4) {
         float a = dot8_e2m1_f32(w.x, h[0], h[1], 0.0f);
         a = dot8_e2m1_f32(w.y, h[2], h[3], a);
         float b = dot8_e2m1_f32(w.z, h[4], h[5], 0.0f);
         b = dot8_e2m1_f32(w.w, h[6], h[7], b);
         return sc.x * a + sc.y * b;
+    } else {
+        float a = dot8_i4_f32(w.x, h[0], h[1], 0.0f);
+        a = dot8_i4_f32(w.y, h[2], h[3], a);
+        a = dot8_i4_f32(w.z, h[4], h[5], a);
+        a = dot8_i4_f32(w.w, h[6], h[7], a);
+        return sc.x * a;
     }
 }
 // ... with the activations at hp (global or LDS).
@@ -332,7 +355,7 @@ template <int FMT, int CH, int P>
 struct GateUpRows {
     // fp8: the P gate rows (and the P up rows) sit in one 128-row scale
     // block (i0 is a multiple of P, which divides 128), so one scale per
-    // chunk serves each half; nvfp4 scales are per row.
+    // chunk serves each half; the other formats' scales are per row.
     static constexpr int NS = FMT == kFp8 ? 2 : 2 * P;
     static_assert(128 % P == 0, "pairs per wave must divide the scale block");
     u32x4 w[2 * P][CH];
@@ -532,9 +555,9 @@ struct DownRow {
 // host-side shape check agree on this rule): lanes cover the routed expert's
 // row, capped at the wave; chunks per lane cover the longer of the two rows.
 __host__ __device__ inline void down_lane_shape(int fmt, int inter, int shared_inter, int &lpr, int &ch) {
-    const int nch = (fmt == kFp8 ? inter : inter / 2) / 16;
+    const int nch = fmt_row_bytes(fmt, inter) / 16;
     const int ie = inter > shared_inter ? inter : shared_inter;
-    const int nchmax = (fmt == kFp8 ? ie : ie / 2) / 16;
+    const int nchmax = fmt_row_bytes(fmt, ie) / 16;
     lpr = nch >= 64 ? 64 : nch >= 32 ? 32 : nch >= 16 ? 16 : 8;
     ch = (nchmax + lpr - 1) / lpr;
 }

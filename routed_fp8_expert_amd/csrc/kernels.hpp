@@ -19,6 +19,12 @@ struct ExpertSet {
 constexpr int kReplicas = 8;   // one copy per XCD (workgroups map to XCDs by index)
 constexpr int kMfmaTileRows = 16;   // rows of an expert per matrix-core tile
 
+// Weight formats (the values of the C ABI's moe_weight_format).
+enum : int { kFp8 = 0, kNvfp4 = 1, kInt8Row = 2, kInt4Row = 3, kInt4G64 = 4 };
+// One code per byte (fp8, int8) or two (e2m1, int4).
+__host__ __device__ constexpr bool byte_codes(int fmt) { return fmt == kFp8 || fmt == kInt8Row; }
+__host__ __device__ constexpr int fmt_row_bytes(int fmt, int cols) { return byte_codes(fmt) ? cols : cols / 2; }
+
 enum MetaWord : int {
     kMetaGemvCount = 0,   // routed experts on the GEMV arm
     kMetaMfmaCount = 1,   // routed experts on the MFMA arm

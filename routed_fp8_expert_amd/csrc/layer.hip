@@ -144,7 +144,7 @@ __device__ __forceinline__ void block_topk(const RouteArgs &r, const float *lrep
 template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
 __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerGrid g) {
     // gate/up chunks per lane follow from the router's: H/1024 (fp8), H/2048 (nvfp4)
-    constexpr int CH = FMT == kFp8 ? (NCH + 1) / 2 : (NCH + 3) / 4;
+    constexpr int CH = byte_codes(FMT) ? (NCH + 1) / 2 : (NCH + 3) / 4;
     extern __shared__ f32x4 hlds4[];
     __shared__ unsigned ticket_s;
     __shared__ int ids_s[kMaxSlots];

@@ -43,7 +43,7 @@ def test_exports_match_headers(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     for status, text in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported shape"),
                          (-4, "workspace too small"), (-6, "device lost (sticky)")]:
         assert lib.strerror(status) == text
