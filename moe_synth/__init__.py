@@ -20,6 +20,8 @@ layers, 512 experts, 10 per token, NVFP4):
   a3b_i8, a3b_i4, a3b_i4g64   as a3b with int8 per-row, int4 per-row and
             int4-g64 experts (colibri PR: per-row int4 and int4-g64 experts)
   tiny_i4g64  as tiny with int4-g64 experts
+  a3b_f8bs, tiny_f8bs   as a3b / tiny with bf16 block scales (colibri PR: fp8
+            experts with BF16 128x128 block scales)
 """
 from __future__ import annotations
 
@@ -40,6 +42,7 @@ FMT_INT8_ROW = 2
 FMT_INT4_ROW = 3
 FMT_INT4_G64 = 4
 INT_FORMATS = (FMT_INT8_ROW, FMT_INT4_ROW, FMT_INT4_G64)
+FMT_FP8_B128_BF16S = 5
 
 
 @dataclass(frozen=True)
@@ -70,6 +73,8 @@ WORKLOADS: Dict[str, Workload] = {
     "a3b_i8": Workload("a3b_i8", 2048, 256, 8, 512, 512, FMT_INT8_ROW, 40, [1, 8]),
     "a3b_i4": Workload("a3b_i4", 2048, 256, 8, 512, 512, FMT_INT4_ROW, 40, [1, 8]),
     "a3b_i4g64": Workload("a3b_i4g64", 2048, 256, 8, 512, 512, FMT_INT4_G64, 40, [1, 8]),
+    "a3b_f8bs": Workload("a3b_f8bs", 2048, 256, 8, 512, 512, FMT_FP8_B128_BF16S, 40, [1, 8]),
+    "tiny_f8bs": Workload("tiny_f8bs", 256, 16, 2, 128, 128, FMT_FP8_B128_BF16S, 1, [1], "gemv", True, False),
     "tiny_i4g64": Workload("tiny_i4g64", 256, 16, 2, 128, 128, FMT_INT4_G64, 1, [1], "gemv", True, False),
 }
 
@@ -129,6 +134,19 @@ def quant_nvfp4(w: torch.Tensor):
     return packed, sc.view(torch.uint8).contiguous(), g.to(torch.float32).contiguous()
 
 
+def quant_fp8_b128_bf16s(w: torch.Tensor):
+    """As quant_fp8_b128 with the block scale rounded to bf16 first (the codes
+    are taken against the rounded scale).  Returns (codes u8, scales bf16
+    [..., O/128, I/128])."""
+    *lead, O, I = w.shape
+    b = w.reshape(*lead, O // 128, 128, I // 128, 128)
+    amax = b.abs().amax(dim=(-3, -1))
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).to(torch.bfloat16)
+    v = (b / scale.to(torch.float32)[..., :, None, :, None]).clamp(-FP8_MAX, FP8_MAX)
+    codes = v.to(torch.float8_e4m3fn).view(torch.uint8).reshape(*lead, O, I)
+    return codes.contiguous(), scale.contiguous()
+
+
 def quant_int(w: torch.Tensor, fmt: int):
     """Encode f32 weights [..., O, I] in an integer format: symmetric codes
     round(w / scale) clamped to +-qmax (127 for int8, 7 for int4), one f32
@@ -167,6 +185,9 @@ def _encode(w: torch.Tensor, fmt: int):
         return q, s, None
     if fmt in INT_FORMATS:
         q, s = quant_int(w, fmt)
+        return q, s, None
+    if fmt == FMT_FP8_B128_BF16S:
+        q, s = quant_fp8_b128_bf16s(w)
         return q, s, None
     return quant_nvfp4(w)
 
@@ -289,8 +310,9 @@ def effective_weight_bytes(wl: Workload, distinct_routed: int, router_gemv: bool
 
     def expert_bytes(inter):
         n = 2 * inter * H + H * inter          # weights of gate|up and down
-        if wl.fmt == FMT_FP8_B128:
-            return n + 4 * ((2 * inter // 128) * (H // 128) + (H // 128) * (inter // 128))
+        if wl.fmt in (FMT_FP8_B128, FMT_FP8_B128_BF16S):
+            sb = 4 if wl.fmt == FMT_FP8_B128 else 2
+            return n + sb * ((2 * inter // 128) * (H // 128) + (H // 128) * (inter // 128))
         if wl.fmt == FMT_INT8_ROW:
             return n + 4 * (2 * inter + H)
         if wl.fmt == FMT_INT4_ROW:

@@ -21,6 +21,7 @@ FMT_INT8_ROW = 2
 FMT_INT4_ROW = 3
 FMT_INT4_G64 = 4
 INT_FORMATS = (FMT_INT8_ROW, FMT_INT4_ROW, FMT_INT4_G64)
+FMT_FP8_B128_BF16S = 5
 
 _lib = None
 
@@ -56,6 +57,7 @@ def lib():
         L.orc_int4_to_f32.argtypes = [C.c_uint8]
         L.orc_int4_to_f32.restype = C.c_float
         L.orc_dequant_int.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
+        L.orc_dequant_fp8_bf16s.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
         L.orc_set_threads.argtypes = [C.c_int]
         L.orc_get_threads.restype = C.c_int
         L.orc_dequant_fp8.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
@@ -154,6 +156,17 @@ def dequant_fp8(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return W
 
 
+def dequant_fp8_bf16s(q: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """fp8 codes [O][I] with bf16 block scales (uint16 bit patterns) [O/128][I/128]."""
+    q = _c(q, np.uint8)
+    scale_bits = _c(scale_bits, np.uint16)
+    O, I = q.shape
+    W = np.empty((O, I), np.float32)
+    if lib().orc_dequant_fp8_bf16s(_ptr(q), _ptr(scale_bits), O, I, _ptr(W)) != 0:
+        raise ValueError("orc_dequant_fp8_bf16s rejected its arguments")
+    return W
+
+
 def dequant_nvfp4(q: np.ndarray, scale: np.ndarray, g: float) -> np.ndarray:
     q = _c(q, np.uint8)
     scale = _c(scale, np.uint8)
@@ -165,6 +178,11 @@ def dequant_nvfp4(q: np.ndarray, scale: np.ndarray, g: float) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ layers
+
+def _scale_dtype(fmt):
+    """Stored scale element type: e4m3 bytes (nvfp4), bf16 bits, else f32."""
+    return {FMT_NVFP4: np.uint8, FMT_FP8_B128_BF16S: np.uint16}.get(fmt, np.float32)
+
 
 @dataclass
 class Expert:
@@ -191,7 +209,7 @@ class Layer:
                  experts: Optional[Dict[int, Expert]] = None, shared: Optional[Expert] = None):
         self.hidden, self.n_experts, self.top_k = int(hidden), int(n_experts), int(top_k)
         self.inter, self.shared_inter, self.fmt = int(inter), int(shared_inter), int(fmt)
-        sdt = np.uint8 if fmt == FMT_NVFP4 else np.float32
+        sdt = _scale_dtype(fmt)
         self._keep = []
         self.router_w = _c(router_w, np.uint16)
         self.router_bias = _c(router_bias, np.float32)
@@ -260,7 +278,7 @@ def group(ids: np.ndarray, n_experts: int):
 
 
 def expert_apply(layer: Layer, expert: Expert, inter: int, x_row: np.ndarray) -> np.ndarray:
-    sdt = np.uint8 if layer.fmt == FMT_NVFP4 else np.float32
+    sdt = _scale_dtype(layer.fmt)
     keep = []
     cx = layer._mk(expert, sdt)
     keep.append(cx)

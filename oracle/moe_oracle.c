@@ -112,6 +112,15 @@ static float w_fp8(const uint8_t *q, const float *scale, int I, int o, int i)
     return (float)(code * sc);
 }
 
+/* fp8 block-128x128 with bf16 scales (colibri PR: a fixture of fp8 experts
+ * with BF16 128x128 block scales): the scale is a bf16, widened exactly. */
+static float w_fp8_bf16s(const uint8_t *q, const uint16_t *scale, int I, int o, int i)
+{
+    double code = orc_e4m3_to_f32(q[(size_t)o * I + i]);
+    double sc = orc_bf16_to_f32(scale[(size_t)(o / 128) * (size_t)(I / 128) + (size_t)(i / 128)]);
+    return (float)(code * sc);
+}
+
 /* NVFP4 ("Inspecting Qwen3.5-397B-A17B-NVFP4": NVIDIA's 4-bit float).  The
  * layout is a reading: two codes per byte, the even column in the low nibble;
  * one e4m3 scale per 16 consecutive columns of a row; one f32 global scale
@@ -147,7 +156,7 @@ static float w_int(int fmt, const uint8_t *q, const float *scale, int I, int o, 
     return (float)(code * sc);
 }
 
-static int known_format(int fmt) { return fmt >= ORC_FMT_FP8_B128 && fmt <= ORC_FMT_INT4_G64; }
+static int known_format(int fmt) { return fmt >= ORC_FMT_FP8_B128 && fmt <= ORC_FMT_FP8_B128_BF16S; }
 
 static float weight(int fmt, const uint8_t *q, const void *s, float g, int I, int o, int i)
 {
@@ -155,6 +164,8 @@ static float weight(int fmt, const uint8_t *q, const void *s, float g, int I, in
         return w_nvfp4(q, (const uint8_t *)s, g, I, o, i);
     if (fmt == ORC_FMT_FP8_B128)
         return w_fp8(q, (const float *)s, I, o, i);
+    if (fmt == ORC_FMT_FP8_B128_BF16S)
+        return w_fp8_bf16s(q, (const uint16_t *)s, I, o, i);
     return w_int(fmt, q, (const float *)s, I, o, i);
 }
 
@@ -175,6 +186,16 @@ int orc_dequant_nvfp4(const uint8_t *q, const uint8_t *scale, float g, int O, in
     for (int o = 0; o < O; o++)
         for (int i = 0; i < I; i++)
             W[(size_t)o * I + i] = w_nvfp4(q, scale, g, I, o, i);
+    return 0;
+}
+
+int orc_dequant_fp8_bf16s(const uint8_t *q, const uint16_t *scale, int O, int I, float *W)
+{
+    if (!q || !scale || !W || O <= 0 || I <= 0 || O % 128 || I % 128)
+        return -1;
+    for (int o = 0; o < O; o++)
+        for (int i = 0; i < I; i++)
+            W[(size_t)o * I + i] = w_fp8_bf16s(q, scale, I, o, i);
     return 0;
 }
 

@@ -36,6 +36,7 @@
  *                      even column), [O][I/2] bytes; one f32 scale per row.
  *   ORC_FMT_INT4_G64 : int4 codes as above; one f32 scale per 64 consecutive
  *                      input columns of a row, array [O][I/64].
+ *   ORC_FMT_FP8_B128_BF16S : as ORC_FMT_FP8_B128 with bf16 block scales.
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -45,7 +46,8 @@
 extern "C" {
 #endif
 
-enum { ORC_FMT_FP8_B128 = 0, ORC_FMT_NVFP4 = 1, ORC_FMT_INT8_ROW = 2, ORC_FMT_INT4_ROW = 3, ORC_FMT_INT4_G64 = 4 };
+enum { ORC_FMT_FP8_B128 = 0, ORC_FMT_NVFP4 = 1, ORC_FMT_INT8_ROW = 2, ORC_FMT_INT4_ROW = 3, ORC_FMT_INT4_G64 = 4,
+       ORC_FMT_FP8_B128_BF16S = 5 };
 
 typedef struct orc_expert {
     const uint8_t *gu_q;   /* gate|up codes, [2I][H] (fp8) or [2I][H/2] (nvfp4) */
@@ -86,6 +88,8 @@ int orc_dequant_nvfp4(const uint8_t *q, const uint8_t *scale, float g, int O, in
 /* The integer formats (fmt = ORC_FMT_INT8_ROW, _INT4_ROW or _INT4_G64); scale
  * is f32 [O][I/G] with G = I for the per-row formats and 64 for g64. */
 int orc_dequant_int(int fmt, const uint8_t *q, const float *scale, int O, int I, float *W);
+/* fp8 codes with bf16 block scales [O/128][I/128]. */
+int orc_dequant_fp8_bf16s(const uint8_t *q, const uint16_t *scale, int O, int I, float *W);
 
 /* Router logits f32 [R][E]. */
 int orc_router_logits(const orc_layer *L, const uint16_t *x, int R, float *logits);

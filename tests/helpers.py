@@ -16,7 +16,12 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 
 def host(t):
-    return None if t is None else t.detach().cpu().contiguous().numpy()
+    """Tensor -> numpy on the host (bf16 as its uint16 bit patterns)."""
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16:
+        return bits(t)
+    return t.detach().cpu().contiguous().numpy()
 
 
 def oracle_layer(orc, wl: syn.Workload, W: dict, experts=None):
