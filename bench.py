@@ -29,8 +29,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-FMT_DTYPE = {0: "fp8e4m3", 1: "nvfp4", 2: "int8", 3: "int4", 4: "int4"}
-FMT_NAME = {0: "fp8 e4m3 block-128", 1: "nvfp4", 2: "int8 per-row", 3: "int4 per-row", 4: "int4-g64"}
+FMT_DTYPE = {0: "fp8e4m3", 1: "nvfp4", 2: "int8", 3: "int4", 4: "int4", 5: "fp8e4m3"}
+FMT_NAME = {0: "fp8 e4m3 block-128", 1: "nvfp4", 2: "int8 per-row", 3: "int4 per-row", 4: "int4-g64",
+            5: "fp8 e4m3 block-128, bf16 scales"}
 METRIC = "us per MoE layer + effective weight GB/s (% of HBM peak), 35B-A3B shape, n=1"
 
 

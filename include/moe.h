@@ -92,6 +92,10 @@ enum moe_weight_format {
     MOE_WFMT_INT4_ROW = 3,      /* int4 codes two per byte (even column in the low nibble),
                                  * [out][in/2] bytes; G = in */
     MOE_WFMT_INT4_G64 = 4,      /* int4 codes as above; G = 64 */
+    /* As MOE_WFMT_FP8_E4M3_B128 with bf16 block scales [out/128][in/128]
+     * (colibri PR: fp8 experts with BF16 128x128 block scales).  GEMV arm and
+     * the three-launch one-row path. */
+    MOE_WFMT_FP8_E4M3_B128_BF16S = 5,
 };
 
 typedef struct moe_ctx moe_ctx;
@@ -100,11 +104,11 @@ typedef struct moe_ctx moe_ctx;
  * as per-expert slabs at a fixed byte stride.  Device pointers. */
 typedef struct moe_expert_weights {
     const void *gate_up;        /* [2I][H] codes (fp8, int8: 1 B each; nvfp4, int4: H/2 B per row) */
-    const void *gate_up_scale;  /* fp8: f32 [2I/128][H/128]; nvfp4: e4m3 [2I][H/16];
+    const void *gate_up_scale;  /* fp8: f32 (or bf16) [2I/128][H/128]; nvfp4: e4m3 [2I][H/16];
                                  * integer formats: f32 [2I][H/G] */
     const float *gate_up_global;/* nvfp4: f32 per expert (stride 1 float); others: NULL */
     const void *down;           /* [H][I] codes (fp8, int8) or [H][I/2] bytes (nvfp4, int4) */
-    const void *down_scale;     /* fp8: f32 [H/128][I/128]; nvfp4: e4m3 [H][I/16];
+    const void *down_scale;     /* fp8: f32 (or bf16) [H/128][I/128]; nvfp4: e4m3 [H][I/16];
                                  * integer formats: f32 [H][I/G] */
     const float *down_global;   /* nvfp4: f32 per expert; others: NULL */
     int64_t gate_up_stride;     /* bytes from one expert's gate_up to the next */

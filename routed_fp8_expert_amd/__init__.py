@@ -10,4 +10,5 @@ from .binding import (  # noqa: F401
     moe_dense_fp8, moe_expert_ffn, moe_layer_forward, moe_layer_forward_norm, moe_route, moe_workspace_bytes,
     strerror, workspace,
     KERNELS, MOE_WFMT_FP8_E4M3_B128, MOE_WFMT_NVFP4, MOE_WFMT_INT8_ROW, MOE_WFMT_INT4_ROW, MOE_WFMT_INT4_G64,
+    MOE_WFMT_FP8_E4M3_B128_BF16S,
 )

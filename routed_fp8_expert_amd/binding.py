@@ -29,6 +29,7 @@ MOE_WFMT_NVFP4 = 1
 MOE_WFMT_INT8_ROW = 2
 MOE_WFMT_INT4_ROW = 3
 MOE_WFMT_INT4_G64 = 4
+MOE_WFMT_FP8_E4M3_B128_BF16S = 5
 
 KERNELS = ["router", "topk", "group", "gate_up", "down", "blend", "mfma_gate_up", "mfma_down", "layer", "norm", "dense"]
 

@@ -90,7 +90,8 @@ int validate_family(const moe_expert_weights &f, int fmt, bool many) {
     if (!f.gate_up || !f.gate_up_scale || !f.down || !f.down_scale) return MOE_ERR_INVALID_ARG;
     if (fmt == MOE_WFMT_NVFP4 && (!f.gate_up_global || !f.down_global)) return MOE_ERR_INVALID_ARG;
     if (!aligned(f.gate_up, 16) || !aligned(f.down, 16)) return MOE_ERR_MISALIGNED;
-    const size_t salign = fmt == MOE_WFMT_NVFP4 ? 2 : 4;   // e4m3 byte pairs, else f32
+    // e4m3 byte pairs (nvfp4), bf16 (fp8 with bf16 scales), else f32
+    const size_t salign = fmt == MOE_WFMT_NVFP4 || fmt == MOE_WFMT_FP8_E4M3_B128_BF16S ? 2 : 4;
     if (!aligned(f.gate_up_scale, salign) || !aligned(f.down_scale, salign)) return MOE_ERR_MISALIGNED;
     if (fmt == MOE_WFMT_NVFP4 && (!aligned(f.gate_up_global, 4) || !aligned(f.down_global, 4)))
         return MOE_ERR_MISALIGNED;
@@ -119,7 +120,7 @@ bool down_shape_ok(const moe_layer_weights *w) {
 int validate_weights(const moe_layer_weights *w) {
     if (!w) return MOE_ERR_INVALID_ARG;
     if (w->struct_size != sizeof(moe_layer_weights)) return MOE_ERR_INVALID_ARG;
-    if (w->weight_format < MOE_WFMT_FP8_E4M3_B128 || w->weight_format > MOE_WFMT_INT4_G64)
+    if (w->weight_format < MOE_WFMT_FP8_E4M3_B128 || w->weight_format > MOE_WFMT_FP8_E4M3_B128_BF16S)
         return MOE_ERR_INVALID_ARG;
     const int H = w->hidden, E = w->n_experts, k = w->top_k, I = w->inter, Is = w->shared_inter;
     if (H <= 0 || E <= 0 || k <= 0 || I <= 0 || Is < 0) return MOE_ERR_INVALID_ARG;

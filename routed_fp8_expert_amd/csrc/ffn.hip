@@ -536,6 +536,7 @@ static int gate_up_chunks(int fmt, int H) { return (fmt_row_bytes(fmt, H) / 16 +
             case kInt8Row: return FN<kInt8Row>(__VA_ARGS__);                                      \
             case kInt4Row: return FN<kInt4Row>(__VA_ARGS__);                                      \
             case kInt4G64: return FN<kInt4G64>(__VA_ARGS__);                                      \
+            case kFp8Bf16s: return FN<kFp8Bf16s>(__VA_ARGS__);                                    \
             default: return hipErrorInvalidValue;                                                 \
         }                                                                                         \
     } while (0)

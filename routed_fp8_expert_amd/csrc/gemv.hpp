@@ -253,7 +253,7 @@ template <int FMT> __device__ __forceinline__ int row_bytes(int cols) { return f
 template <int FMT> constexpr int cols_per_chunk() { return byte_codes(FMT) ? 16 : 32; }
 
 // Scale(s) of 16-byte chunk `c` of weight row `row` of a matrix with `cols`
-// columns.  fp8: one f32 per 128x128 block; nvfp4: two e4m3 bytes (two
+// columns.  fp8: one f32 (or bf16) per 128x128 block; nvfp4: two e4m3 bytes (two
 // 16-column groups); int8/int4 per row: the row's f32; int4-g64: the f32 of
 // the 64-column group holding the chunk's 32 columns.
 template <int FMT>
@@ -261,6 +261,10 @@ __device__ __forceinline__ f32x2 chunk_scale(const uint8_t *s, int row, int cols
     const float *sf = reinterpret_cast<const float *>(s);
     if constexpr (FMT == kFp8) {
         const float v = sf[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)];
+        return f32x2{v, v};
+    } else if constexpr (FMT == kFp8Bf16s) {
+        const uint16_t *sb = reinterpret_cast<const uint16_t *>(s);
+        const float v = bf16_to_f32(sb[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)]);
         return f32x2{v, v};
     } else if constexpr (FMT == kNvfp4) {
         const uint16_t b = *reinterpret_cast<const uint16_t *>(s + (size_t)row * (cols >> 4) + 2 * c);
@@ -281,7 +285,7 @@ template <int FMT> constexpr int h_quads() { return byte_codes(FMT) ? 4 : 8; }
 // One 16-byte weight chunk . the chunk's bf16 activations (in registers).
 template <int FMT>
 __device__ __forceinline__ float chunk_dot_bf16(u32x4 w, f32x2 sc, const u32x4 (&x)[x_quads<FMT>()]) {
-    if constexpr (FMT == kFp8) {
+    if constexpr (fp8_block(FMT)) {
         return sc.x * dot16_e4m3_bf16(w, x[0], x[1]);
     } else if constexpr (FMT == kInt8Row) {
         return sc.x * dot16_i8_bf16(w, x[0], x[1]);
@@ -315,7 +319,7 @@ __device__ __forceinline__ float chunk_dot_bf16(u32x4 w, f32x2 sc, const uint16_
 // One 16-byte weight chunk . the chunk's f32 activations (in registers).
 template <int FMT>
 __device__ __forceinline__ float chunk_dot_f32(u32x4 w, f32x2 sc, const f32x4 (&h)[h_quads<FMT>()]) {
-    if constexpr (FMT == kFp8) {
+    if constexpr (fp8_block(FMT)) {
         return sc.x * dot16_e4m3_f32(w, h);
     } else if constexpr (FMT == kInt8Row) {
         return sc.x * dot16_i8_f32(w, h);
@@ -356,13 +360,13 @@ struct GateUpRows {
     // fp8: the P gate rows (and the P up rows) sit in one 128-row scale
     // block (i0 is a multiple of P, which divides 128), so one scale per
     // chunk serves each half; the other formats' scales are per row.
-    static constexpr int NS = FMT == kFp8 ? 2 : 2 * P;
+    static constexpr int NS = fp8_block(FMT) ? 2 : 2 * P;
     static_assert(128 % P == 0, "pairs per wave must divide the scale block");
     u32x4 w[2 * P][CH];
     f32x2 sc[NS][CH];
     float g;
 
-    __device__ __forceinline__ static constexpr int sidx(int q) { return FMT == kFp8 ? (q & 1) : q; }
+    __device__ __forceinline__ static constexpr int sidx(int q) { return fp8_block(FMT) ? (q & 1) : q; }
 
     __device__ __forceinline__ void load(const ExpertSet &X, int e, int i0, int H) {
         const int lane = threadIdx.x & (kWave - 1);

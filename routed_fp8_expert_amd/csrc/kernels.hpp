@@ -20,9 +20,11 @@ constexpr int kReplicas = 8;   // one copy per XCD (workgroups map to XCDs by in
 constexpr int kMfmaTileRows = 16;   // rows of an expert per matrix-core tile
 
 // Weight formats (the values of the C ABI's moe_weight_format).
-enum : int { kFp8 = 0, kNvfp4 = 1, kInt8Row = 2, kInt4Row = 3, kInt4G64 = 4 };
+enum : int { kFp8 = 0, kNvfp4 = 1, kInt8Row = 2, kInt4Row = 3, kInt4G64 = 4, kFp8Bf16s = 5 };
+// e4m3 codes with one scale per 128x128 block (f32 or bf16).
+__host__ __device__ constexpr bool fp8_block(int fmt) { return fmt == kFp8 || fmt == kFp8Bf16s; }
 // One code per byte (fp8, int8) or two (e2m1, int4).
-__host__ __device__ constexpr bool byte_codes(int fmt) { return fmt == kFp8 || fmt == kInt8Row; }
+__host__ __device__ constexpr bool byte_codes(int fmt) { return fp8_block(fmt) || fmt == kInt8Row; }
 __host__ __device__ constexpr int fmt_row_bytes(int fmt, int cols) { return byte_codes(fmt) ? cols : cols / 2; }
 
 enum MetaWord : int {

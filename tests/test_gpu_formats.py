@@ -1,5 +1,6 @@
-"""GPU parity of the integer expert formats (int8 per row, int4 per row,
-int4-g64) through the C ABI against the oracle on the same seeded inputs, at
+"""GPU parity of the other expert formats (int8 per row, int4 per row,
+int4-g64, fp8 with bf16 block scales) through the C ABI against the oracle on
+the same seeded inputs, at
 the layer's bar (ids and grouping bit-exact, y within 2e-2 * rms and 5e-3
 mean relative error).  They run on the GEMV arm and the three-launch one-row
 path; forcing the matrix-core arm leaves them on the GEMV arm, and three rows
@@ -72,7 +73,8 @@ def _inputs(orc, wl, W, layer, rows):
 CASES = [("tiny_i4g64", 0, r) for r in (1, 3, 17)] + \
         [("a3b_i8", 0, 1), ("a3b_i8", 1, 8), ("a3b_i8", 0, 33)] + \
         [("a3b_i4", 0, 1), ("a3b_i4", 0, 8)] + \
-        [("a3b_i4g64", 0, 1), ("a3b_i4g64", 1, 1), ("a3b_i4g64", 0, 8), ("a3b_i4g64", 0, 64)]
+        [("a3b_i4g64", 0, 1), ("a3b_i4g64", 1, 1), ("a3b_i4g64", 0, 8), ("a3b_i4g64", 0, 64)] + \
+        [("tiny_f8bs", 0, 1), ("tiny_f8bs", 0, 5), ("a3b_f8bs", 0, 1), ("a3b_f8bs", 0, 8), ("a3b_f8bs", 0, 64)]
 
 
 @pytest.mark.parametrize("name,layer,rows", CASES)
@@ -88,7 +90,7 @@ def test_int_format_layer(moe, ctx, orc, name, layer, rows):
     print(f"  max|err|/rms {stats[0]:.2e}, mean rel {stats[1]:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["a3b_i8", "a3b_i4g64"])
+@pytest.mark.parametrize("name", ["a3b_i8", "a3b_i4g64", "a3b_f8bs"])
 def test_int_formats_stay_on_gemv_arm_and_one_row_paths_agree(moe, orc, name):
     wl = syn.WORKLOADS[name]
     W = _weights(wl, 0)
@@ -113,7 +115,7 @@ def test_int_formats_stay_on_gemv_arm_and_one_row_paths_agree(moe, orc, name):
     assert np.array_equal(one[0], one[1])
 
 
-@pytest.mark.parametrize("name", ["a3b_i8", "a3b_i4", "a3b_i4g64"])
+@pytest.mark.parametrize("name", ["a3b_i8", "a3b_i4", "a3b_i4g64", "a3b_f8bs"])
 def test_int_format_batch_invariance(moe, ctx, orc, name):
     """Three rows in one call give the bits of three one-row calls."""
     wl = syn.WORKLOADS[name]
