@@ -231,7 +231,8 @@ def run_dense(args):
                    "arm": "matrix cores" if rows >= 32 else "gemv"},
         "kernels": {"dense": {"avg_us": round(kms / max(kn, 1) * 1e3, 3), "launches_per_step": kn // kt_steps}},
         "roofline": {"bound": "hbm", "kernel": "dense", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("dense", name, rows),
                      "algorithmic_bytes_per_launch": int(alg)},
         "cpu_baseline": cpu,
         "source_digest": source_digest(),
