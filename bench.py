@@ -337,7 +337,8 @@ def main():
     # rows per expert over the step (multi-row steps): the grouping's counts
     routing_stats = None
     if rows >= 2:
-        cnt = torch.stack([rt.expert_count.to(torch.int64) for rt in res.routing])   # [layers, E]
+        cnt = torch.stack([torch.bincount(rt.topk_ids.flatten().to(torch.int64), minlength=wl.n_experts)
+                           for rt in res.routing])   # [layers, E]
         routing_stats = {
             "distinct_experts_per_layer": round(float((cnt > 0).sum(1).float().mean()), 2),
             "zero_row_experts_per_layer": round(float((cnt == 0).sum(1).float().mean()), 2),

@@ -190,6 +190,12 @@ MOE_API int moe_ctx_set_force_arm(moe_ctx *ctx, int arm);
  * shared expert; routed gate/up; down and blend).
  * Also MOE_ONE_ROW_PATH=split in the environment.  Both give the same bits. */
 MOE_API int moe_ctx_set_one_row_path(moe_ctx *ctx, int path);
+/* Steps of 2 to `rows` rows (at the default arm choice) run without grouping:
+ * routing, then one GEMV per (row, slot) with the one-row kernels (the shared
+ * expert's gate/up once for all rows), down fused with the blend per row.
+ * Each row's result has the bits of a one-row call.  0 turns it off; the
+ * default is 8 (env MOE_FEW_ROWS).  MOE_ERR_INVALID_ARG for rows < 0. */
+MOE_API int moe_ctx_set_few_rows(moe_ctx *ctx, int rows);
 /* Device-side error word: kernels that meet an expert id outside [0, E)
  * skip it and set bit 0; a bounded wait that timed out sets bit 1.  Synchronises the ctx's device; clears the word
  * when `clear` is non-zero. */
@@ -231,7 +237,9 @@ MOE_API int moe_expert_ffn(moe_ctx *ctx, const moe_layer_weights *w, const void 
                            int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
 /* The whole layer: moe_route then moe_expert_ffn.  `routing` may be NULL,
- * in which case the routing arrays live in the workspace. */
+ * in which case the routing arrays live in the workspace; its grouping arrays
+ * (expert_count, expert_offset, perm) may be NULL too (all three or none), and
+ * are written only when given. */
 MOE_API int moe_layer_forward(moe_ctx *ctx, const moe_layer_weights *w, const void *x, int rows,
                               int64_t ldx, const float *logits_in, const moe_routing *routing,
                               void *y, void *residual, int64_t ldy, void *ws, size_t ws_bytes,

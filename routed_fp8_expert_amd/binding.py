@@ -95,6 +95,7 @@ def lib():
             "moe_ctx_set_mfma_min_rows": ([vp, i32], i32),
             "moe_ctx_set_force_arm": ([vp, i32], i32),
             "moe_ctx_set_one_row_path": ([vp, i32], i32),
+            "moe_ctx_set_few_rows": ([vp, i32], i32),
             "moe_ctx_device_errors": ([vp, C.POINTER(C.c_uint32), i32], i32),
             "moe_ctx_set_timing": ([vp, i32], i32),
             "moe_ctx_kernel_stats": ([vp, i32, C.POINTER(C.c_double), C.POINTER(i64)], i32),
@@ -198,6 +199,10 @@ def moe_ctx_set_one_row_path(ctx: Ctx, path: int) -> None:
     _check(lib().moe_ctx_set_one_row_path(ctx.handle, int(path)), "moe_ctx_set_one_row_path")
 
 
+def moe_ctx_set_few_rows(ctx: Ctx, rows: int) -> None:
+    _check(lib().moe_ctx_set_few_rows(ctx.handle, int(rows)), "moe_ctx_set_few_rows")
+
+
 def moe_ctx_device_errors(ctx: Ctx, clear: bool = True) -> int:
     v = C.c_uint32(0)
     _check(lib().moe_ctx_device_errors(ctx.handle, C.byref(v), int(clear)), "moe_ctx_device_errors")
@@ -267,14 +272,15 @@ class LayerWeights:
 class Routing:
     """Caller-owned routing arrays (moe_routing) as torch device tensors."""
 
-    def __init__(self, rows, n_experts, top_k, device, logits=False):
+    def __init__(self, rows, n_experts, top_k, device, logits=False, grouping=True):
         dev = torch.device(device)
         self.topk_ids = torch.empty((rows, top_k), dtype=torch.int32, device=dev)
         self.topk_w = torch.empty((rows, top_k), dtype=torch.float32, device=dev)
         self.shared_gate = torch.empty((rows,), dtype=torch.float32, device=dev)
-        self.expert_count = torch.empty((n_experts,), dtype=torch.int32, device=dev)
-        self.expert_offset = torch.empty((n_experts + 1,), dtype=torch.int32, device=dev)
-        self.perm = torch.empty((rows * top_k,), dtype=torch.int32, device=dev)
+        # grouping arrays: optional for moe_layer_forward (NULL when not asked for)
+        self.expert_count = torch.empty((n_experts,), dtype=torch.int32, device=dev) if grouping else None
+        self.expert_offset = torch.empty((n_experts + 1,), dtype=torch.int32, device=dev) if grouping else None
+        self.perm = torch.empty((rows * top_k,), dtype=torch.int32, device=dev) if grouping else None
         self.logits = (torch.empty((rows, n_experts), dtype=torch.float32, device=dev)
                        if logits else None)
         self.c = RoutingC(C.sizeof(RoutingC), _p(self.topk_ids), _p(self.topk_w),

@@ -26,6 +26,7 @@ enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, k
                       kSyncWords = 1024 + 40 * 64 };
 constexpr int kDenseMaxK = 8192;         // a wave's 64 lanes hold one scale per 128-wide block
 constexpr int kDenseMaxRows = 1 << 20;   // matrix-core grid rows stay far below 65535
+constexpr int kDefaultFewRows = 8;       // steps of 2..8 rows: one GEMV per row and slot (measured)
 constexpr int kDefaultMfmaMinRows = 4;   // rows per expert from which the MFMA arm pays (measured)
 constexpr int kMaxRows = 1024;
 constexpr int kMaxExperts = 1024;
@@ -47,6 +48,7 @@ struct moe_ctx {
     int status = MOE_OK;
     int64_t fault_countdown = 0;
     int mfma_min_rows = kDefaultMfmaMinRows;
+    int few_rows = kDefaultFewRows;
     int force_arm = 0;
     int one_row_path = 0;        // 0 = single launch where built, 1 = three launches
     uint32_t *words = nullptr;   // device: kSyncWords words
@@ -234,7 +236,9 @@ int check_routing(const moe_routing *r, int R, bool need_group) {
     if (!r || r->struct_size != sizeof(moe_routing)) return MOE_ERR_INVALID_ARG;
     if (R == 0) return MOE_OK;
     if (!r->topk_ids || !r->topk_w || !r->shared_gate) return MOE_ERR_INVALID_ARG;
-    if (need_group && R >= 2 && (!r->expert_count || !r->expert_offset || !r->perm)) return MOE_ERR_INVALID_ARG;
+    const int ngroup = (r->expert_count != nullptr) + (r->expert_offset != nullptr) + (r->perm != nullptr);
+    if (need_group && R >= 2 && ngroup != 3) return MOE_ERR_INVALID_ARG;
+    if (ngroup != 0 && ngroup != 3) return MOE_ERR_INVALID_ARG;   // all three grouping arrays or none
     const void *ps[] = {r->topk_ids, r->topk_w, r->shared_gate, r->expert_count, r->expert_offset, r->perm, r->logits};
     for (const void *p : ps)
         if (p && !aligned(p, 4)) return MOE_ERR_MISALIGNED;
@@ -316,7 +320,7 @@ moe::RouteArgs route_args(moe_ctx *c, const moe_layer_weights *w, const void *x,
     return a;
 }
 
-int do_route(moe_ctx *c, const moe::RouteArgs &a, bool plan, hipStream_t st) {
+int do_route(moe_ctx *c, const moe::RouteArgs &a, bool plan, hipStream_t st, bool group = true) {
     int rc;
     if (!a.logits_in) {
         rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_router(a, st); });
@@ -327,7 +331,7 @@ int do_route(moe_ctx *c, const moe::RouteArgs &a, bool plan, hipStream_t st) {
         rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, true, st); });
         if (rc) return rc;
     }
-    if (a.R >= 2) {
+    if (a.R >= 2 && group) {
         rc = launch(c, MOE_K_GROUP, st, [&] { return moe::launch_group(a, plan, st); });
         if (rc) return rc;
     }
@@ -412,6 +416,19 @@ int do_ffn(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
 
 // The whole one-row layer in three launches: router rows with the shared
 // expert's gate/up; the top-k inside the routed gate/up; down with the blend.
+// Steps of a few rows (2 .. few_rows, the default arm choice): no grouping;
+// the one-row gate/up and down+blend kernels over every (row, slot), the
+// shared expert's gate/up once for all rows.
+bool few_rows_path(const moe_ctx *c, int R) { return R >= 2 && c->force_arm == 0 && R <= c->few_rows; }
+
+int do_ffn_few(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
+    int rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up_r1(a, st); });
+    if (rc) return rc;
+    rc = launch(c, MOE_K_DOWN, st, [&] { return moe::launch_down_blend_r1(a, st); });
+    if (rc || !a.norm_w) return rc;
+    return launch(c, MOE_K_NORM, st, [&] { return moe::launch_rmsnorm(a, st); });
+}
+
 int do_layer_r1(moe_ctx *c, const moe::RouteArgs &r, moe::FfnArgs a, hipStream_t st) {
     if (c->one_row_path == 0 && moe::layer_r1_supported(r, a))
         return launch(c, MOE_K_LAYER, st, [&] { return moe::launch_layer_r1(r, a, c->words + kWordLayerSync, st); });
@@ -428,6 +445,11 @@ RoutingPtrs routing_ptrs(const moe_routing *r, void *ws, const Layout &L) {
     RoutingPtrs p{};
     if (r) {
         p = {r->topk_ids, r->topk_w, r->shared_gate, r->expert_count, r->expert_offset, r->perm, r->logits};
+        if (!p.counts || !p.offsets || !p.perm) {   // grouping arrays not asked for: the workspace's
+            p.counts = at<int32_t>(ws, L.counts);
+            p.offsets = at<int32_t>(ws, L.offsets);
+            p.perm = at<int32_t>(ws, L.perm);
+        }
     } else {
         p = {at<int32_t>(ws, L.ids), at<float>(ws, L.w),      at<float>(ws, L.s),      at<int32_t>(ws, L.counts),
              at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm), nullptr};
@@ -474,6 +496,7 @@ MOE_API int moe_ctx_create(int device, moe_ctx **out) {
     }
     if (const char *v = getenv("MOE_FAULT_AT")) c->fault_countdown = std::max<long long>(0, atoll(v));
     if (const char *v = getenv("MOE_MFMA_MIN_ROWS")) c->mfma_min_rows = std::max(0, atoi(v));
+    if (const char *v = getenv("MOE_FEW_ROWS")) c->few_rows = std::max(0, atoi(v));
     if (const char *v = getenv("MOE_ONE_ROW_PATH")) c->one_row_path = !strcmp(v, "split") ? 1 : 0;
     if (const char *v = getenv("MOE_FORCE_ARM")) {
         if (!strcmp(v, "gemv")) c->force_arm = 1;
@@ -513,6 +536,12 @@ MOE_API int moe_ctx_set_mfma_min_rows(moe_ctx *c, int rows) {
 MOE_API int moe_ctx_set_force_arm(moe_ctx *c, int arm) {
     if (!c || arm < 0 || arm > 2) return MOE_ERR_INVALID_ARG;
     c->force_arm = arm;
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_set_few_rows(moe_ctx *c, int rows) {
+    if (!c || rows < 0) return MOE_ERR_INVALID_ARG;
+    c->few_rows = rows;
     return MOE_OK;
 }
 
@@ -603,6 +632,7 @@ MOE_API int moe_expert_ffn(moe_ctx *c, const moe_layer_weights *w, const void *x
     const hipStream_t st = (hipStream_t)stream;
     const Layout L = make_layout(w, R);
     const RoutingPtrs rp = routing_ptrs(in, ws, L);
+    if (few_rows_path(c, R)) return do_ffn_few(c, ffn_args(c, w, x, R, ldx, rp, y, res, ldy, ws, L), st);
     if (R >= 2) {
         const moe::RouteArgs a = route_args(c, w, x, R, ldx, nullptr, rp, ws, L);
         rc = launch(c, MOE_K_GROUP, st, [&] { return moe::launch_plan(a, st); });
@@ -618,7 +648,7 @@ MOE_API int moe_layer_forward_norm(moe_ctx *c, const moe_layer_weights *w, const
     if (c->status) return MOE_ERR_DEVICE_LOST;
     int rc;
     if ((rc = validate_weights(w)) || (rc = validate_rows(w, R)) || (rc = check_x(w, x, R, ldx)) ||
-        (routing && (rc = check_routing(routing, R, true))) || (rc = check_out(w, y, res, R, ldy)) ||
+        (routing && (rc = check_routing(routing, R, false))) || (rc = check_out(w, y, res, R, ldy)) ||
         (rc = check_ws(w, R, ws, ws_bytes)) || (rc = check_norm(w, norm, y, res)))
         return rc;
     if (!logits_in && !w->router_w) return MOE_ERR_INVALID_ARG;
@@ -638,6 +668,13 @@ MOE_API int moe_layer_forward_norm(moe_ctx *c, const moe_layer_weights *w, const
         fa.ldn = norm->ldo;
     }
     if (R == 1) return do_layer_r1(c, ra, fa, st);
+    if (few_rows_path(c, R)) {
+        // grouping arrays are written only when the caller asked for them
+        const bool group = routing && routing->expert_count && routing->expert_offset && routing->perm;
+        rc = do_route(c, ra, false, st, group);
+        if (rc) return rc;
+        return do_ffn_few(c, fa, st);
+    }
     rc = do_route(c, ra, true, st);
     if (rc) return rc;
     return do_ffn(c, fa, st);

@@ -237,42 +237,60 @@ __global__ __launch_bounds__(256) void k_lead_r1(RouteArgs r, FfnArgs a) {
     sink_word(a.sink, warm);
 }
 
-// gate/up of the routed experts of a one-row layer.  Grid (slices, k): block
-// (b, j) takes slot j's expert from the published ids and its slice b; each
-// block also warms its share of that expert's down matrix.
+// gate/up of the routed experts of a one-row layer, and of a step of a few
+// rows without grouping.  Grid (slices, slots, R): block (b, j, r) takes slot
+// j of row r (its expert from the published ids, h row r*k + j) and its slice
+// b; each such block also warms its share of that expert's down matrix.  With
+// several rows slot k is the shared expert, run by the blocks of row 0 for
+// every row (weights loaded once; h rows R*k + r); at one row the lead kernel
+// runs it.
 template <int FMT, int CH>
 __global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
     const int wid = threadIdx.x >> 6;
-    const int slot = blockIdx.y;
-    const int e = a.ids[slot];
+    const int slot = blockIdx.y, r = blockIdx.z;
+    const int i0 = (blockIdx.x * 4 + wid) * P;
+    if (slot == a.k) {
+        const ExpertSet &X = a.shared;
+        if (r != 0 || i0 >= X.inter) return;
+        GateUpRows<FMT, CH, P> rows;
+        rows.load(X, 0, i0, a.H);
+        for (int rr = 0; rr < a.R; ++rr)
+            rows.apply(a.x + (size_t)rr * a.ldx, a.H, X.inter, i0, a.h + (size_t)(a.R * a.k + rr) * a.hstride);
+        return;
+    }
+    const int e = a.ids[(size_t)r * a.k + slot];
     if (e < 0 || e >= a.E) {
         if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, kErrBadExpertId);
         return;
     }
     const ExpertSet &X = a.routed;
-    const int i0 = (blockIdx.x * 4 + wid) * P;
     GateUpRows<FMT, CH, P> rows;
     if (i0 < X.inter) rows.load(X, e, i0, a.H);
     const uint32_t warm = warm_slice(X.dn + (size_t)e * X.dn_stride, (size_t)a.H * row_bytes<FMT>(X.inter),
                                      blockIdx.x, gridDim.x);
-    if (i0 < X.inter) rows.apply(a.x, a.H, X.inter, i0, a.h + (size_t)slot * a.hstride);
+    if (i0 < X.inter)
+        rows.apply(a.x + (size_t)r * a.ldx, a.H, X.inter, i0, a.h + ((size_t)r * a.k + slot) * a.hstride);
     sink_word(a.sink, warm);
 }
 
-// Down GEMV fused with the blend, one activation row.  A row group of LPR
-// lanes owns output element o; it loads row o of every slot's down matrix up
-// front (all k+1 experts' loads in flight), stages h in LDS (HLDS), then for
-// each slot in order reduces d_j and accumulates y = fma(w_j, d_j, y), then
-// fma(s, d_shared, y), and adds into the residual.
+// Down GEMV fused with the blend, for one row (blockIdx.y) of a one-row
+// layer or of a step of a few rows.  A row group of LPR lanes owns output
+// element o; it loads row o of every slot's down matrix up front (all k+1
+// experts' loads in flight), stages the row's h in LDS (HLDS), then for each
+// slot in order reduces d_j and accumulates y = fma(w_j, d_j, y), then
+// fma(s, d_shared, y), and adds into the residual.  Slot j's h is row r*k + j,
+// the shared expert's row R*k + r.
 template <int FMT, int LPR, int CH, bool HLDS>
 __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
     extern __shared__ f32x4 hlds4[];
     constexpr int RPW = kWave / LPR;
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+    const int r = blockIdx.y;
     const int sub = lane % LPR;
     const int o = (blockIdx.x * 4 + wid) * RPW + lane / LPR;
     const bool live = o < a.H;
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
+    auto hrow = [&](int j) { return j == a.k ? (size_t)a.R * a.k + r : (size_t)r * a.k + j; };
 
     DownRow<FMT, LPR, CH> rows[kMaxSlots];
     int es[kMaxSlots];
@@ -281,20 +299,22 @@ __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
         if (j < nslots) {
             const bool sh = j == a.k;
             const ExpertSet &X = sh ? a.shared : a.routed;
-            const int e = sh ? 0 : a.ids[j];
+            const int e = sh ? 0 : a.ids[(size_t)r * a.k + j];
             const bool ok = sh || (e >= 0 && e < a.E);
             es[j] = ok ? e : -1;
             rows[j].load(X, ok ? e : 0, o, sub, live && ok);
         }
     }
-    const float *hbase = a.h;
     if (HLDS) {
-        const int n4 = nslots * a.hstride / 4;
+        const int n4 = a.hstride / 4;
         const f32x4 *src = reinterpret_cast<const f32x4 *>(a.h);
-        for (int i = threadIdx.x; i < n4; i += 256) hlds4[i] = src[i];
+        for (int i = threadIdx.x; i < nslots * n4; i += 256) {
+            const int j = i / n4;
+            hlds4[i] = src[hrow(j) * n4 + (i - j * n4)];
+        }
         __syncthreads();
-        hbase = reinterpret_cast<const float *>(hlds4);
     }
+    const float *hl = reinterpret_cast<const float *>(hlds4);
     float y = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxSlots; ++j) {
@@ -305,12 +325,13 @@ __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
                 if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, kErrBadExpertId);
                 continue;
             }
-            float d = rows[j].dot(hbase + (size_t)j * a.hstride, X.inter, sub);
+            const float *hp = HLDS ? hl + (size_t)j * a.hstride : a.h + hrow(j) * a.hstride;
+            float d = rows[j].dot(hp, X.inter, sub);
             d *= global_scale<FMT>(X.dn_g, es[j]);
-            y = fmaf(sh ? a.s[0] : a.w[j], d, y);
+            y = fmaf(sh ? a.s[r] : a.w[(size_t)r * a.k + j], d, y);
         }
     }
-    if (live && sub == 0) store_out(a.y, a.res, a.ldy, 0, o, y);
+    if (live && sub == 0) store_out(a.y, a.res, a.ldy, r, o, y);
 }
 
 // Down GEMV for one expert of a multi-row step.  A row group of LPR lanes
@@ -613,7 +634,9 @@ hipError_t launch_lead_r1(const RouteArgs &r, const FfnArgs &a, hipStream_t st) 
 
 template <int FMT>
 static hipError_t gate_up_r1_fmt(const FfnArgs &a, hipStream_t st) {
-    dim3 grid((a.routed.inter + 4 * P - 1) / (4 * P), a.k), block(256);
+    const int inter = a.R > 1 ? max_inter(a) : a.routed.inter;
+    const int slots = a.k + (a.R > 1 && a.shared.inter > 0 ? 1 : 0);
+    dim3 grid((inter + 4 * P - 1) / (4 * P), slots, a.R), block(256);
     MOE_CH_DISPATCH(gate_up_chunks(FMT, a.H), hipLaunchKernelGGL((k_gate_up_r1<FMT, CH>), grid, block, 0, st, a));
     return hipGetLastError();
 }
@@ -648,7 +671,7 @@ static hipError_t down_r1_fmt(const FfnArgs &a, hipStream_t st) {
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
     const size_t hbytes = (size_t)nslots * a.hstride * 4;
     MOE_DOWN_DISPATCH({
-        dim3 grid((a.H + rows_per_block - 1) / rows_per_block), block(256);
+        dim3 grid((a.H + rows_per_block - 1) / rows_per_block, a.R), block(256);
         if (hbytes <= kMaxHLds)
             hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, true>), grid, block, hbytes, st, a);
         else

@@ -42,7 +42,7 @@ class Resident:
             self.residual0.append(syn.make_residual(wl, l, rows, self.device))
             self.y.append(torch.empty((rows, wl.hidden), dtype=torch.bfloat16, device=self.device)
                           if keep_y else None)
-            self.routing.append(B.Routing(rows, wl.n_experts, wl.top_k, self.device, logits=True)
+            self.routing.append(B.Routing(rows, wl.n_experts, wl.top_k, self.device, logits=True, grouping=False)
                                 if with_routing else None)
         self.residual = [r.clone() for r in self.residual0]
         self.ws = B.workspace(self.lw[0], rows, self.device)

@@ -137,12 +137,20 @@ def test_bad_ids_are_skipped_and_flagged(moe, tiny):
     moe.moe_expert_ffn(ctx, lw, x, rt, y, None, ws)
     assert moe.moe_ctx_device_errors(ctx) & 1
     assert torch.all(torch.isfinite(y.float()))
-    # multi-row: a corrupt permutation is caught, not followed
+    # multi-row, grouped path: a corrupt permutation is caught, not followed
     lw2, x2, y2, rt2, ws2 = _setup(moe, wl, W, rows=4)
     moe.moe_route(ctx, lw2, x2, rt2, ws2)
     rt2.perm.fill_(1 << 20)
+    moe.moe_ctx_set_few_rows(ctx, 0)
     moe.moe_expert_ffn(ctx, lw2, x2, rt2, y2, None, ws2)
     assert moe.moe_ctx_device_errors(ctx) & 1
+    # multi-row, few-rows path (no grouping read): a bad id is skipped and flagged
+    moe.moe_ctx_set_few_rows(ctx, 8)
+    moe.moe_route(ctx, lw2, x2, rt2, ws2)
+    rt2.topk_ids[2, 1] = -3
+    moe.moe_expert_ffn(ctx, lw2, x2, rt2, y2, None, ws2)
+    assert moe.moe_ctx_device_errors(ctx) & 1
+    assert torch.all(torch.isfinite(y2.float()))
     assert moe.moe_ctx_status(ctx) == 0
     ctx.close()
 
