@@ -27,6 +27,7 @@ enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, k
 constexpr int kDenseMaxK = 8192;         // a wave's 64 lanes hold one scale per 128-wide block
 constexpr int kDenseMaxRows = 1 << 20;   // matrix-core grid rows stay far below 65535
 constexpr int kDefaultFewRows = 8;       // steps of 2..8 rows: one GEMV per row and slot (measured)
+constexpr int kFusedTopkRows = 4;        // few-rows steps up to 4 rows select in the gate/up blocks (measured)
 constexpr int kDefaultMfmaMinRows = 4;   // rows per expert from which the MFMA arm pays (measured)
 constexpr int kMaxRows = 1024;
 constexpr int kMaxExperts = 1024;
@@ -320,7 +321,7 @@ moe::RouteArgs route_args(moe_ctx *c, const moe_layer_weights *w, const void *x,
     return a;
 }
 
-int do_route(moe_ctx *c, const moe::RouteArgs &a, bool plan, hipStream_t st, bool group = true) {
+int do_route(moe_ctx *c, const moe::RouteArgs &a, bool plan, hipStream_t st) {
     int rc;
     if (!a.logits_in) {
         rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_router(a, st); });
@@ -331,7 +332,7 @@ int do_route(moe_ctx *c, const moe::RouteArgs &a, bool plan, hipStream_t st, boo
         rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, true, st); });
         if (rc) return rc;
     }
-    if (a.R >= 2 && group) {
+    if (a.R >= 2) {
         rc = launch(c, MOE_K_GROUP, st, [&] { return moe::launch_group(a, plan, st); });
         if (rc) return rc;
     }
@@ -669,11 +670,32 @@ MOE_API int moe_layer_forward_norm(moe_ctx *c, const moe_layer_weights *w, const
     }
     if (R == 1) return do_layer_r1(c, ra, fa, st);
     if (few_rows_path(c, R)) {
-        // grouping arrays are written only when the caller asked for them
-        const bool group = routing && routing->expert_count && routing->expert_offset && routing->perm;
-        rc = do_route(c, ra, false, st, group);
+        // the router GEMV (unless logits are given); the gate/up blocks take
+        // their rows' top-k and publish the routing; the grouping arrays are
+        // written only when the caller asked for them
+        if (R <= kFusedTopkRows) {
+            if (!logits_in) {
+                rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_router(ra, st); });
+                if (rc) return rc;
+            }
+            fa.topk_src = logits_in ? logits_in : ra.logits;
+            fa.wsg = static_cast<const uint16_t *>(w->shared_gate_w);
+            fa.s_mode = !w->shared_gate_w ? 2 : logits_in ? 1 : 0;
+        } else {
+            // beyond it every gate/up block redoing the selection costs more
+            // than the top-k launch it saves
+            if (!logits_in) {
+                rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_router(ra, st); });
+                if (rc) return rc;
+            }
+            rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(ra, logits_in != nullptr, st); });
+            if (rc) return rc;
+        }
+        rc = do_ffn_few(c, fa, st);
         if (rc) return rc;
-        return do_ffn_few(c, fa, st);
+        const bool group = routing && routing->expert_count && routing->expert_offset && routing->perm;
+        if (!group) return MOE_OK;
+        return launch(c, MOE_K_GROUP, st, [&] { return moe::launch_group(ra, false, st); });
     }
     rc = do_route(c, ra, true, st);
     if (rc) return rc;

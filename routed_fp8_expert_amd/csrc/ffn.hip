@@ -244,11 +244,37 @@ __global__ __launch_bounds__(256) void k_lead_r1(RouteArgs r, FfnArgs a) {
 // several rows slot k is the shared expert, run by the blocks of row 0 for
 // every row (weights loaded once; h rows R*k + r); at one row the lead kernel
 // runs it.
-template <int FMT, int CH>
+//
+// With topk_src set (steps of a few rows), the routed blocks take row r's
+// top-k themselves (wave 0, from the logits in memory) instead of reading
+// published ids; block (0, 0, r) publishes the row's ids and weights and its
+// shared gate (s_mode).
+template <int FMT, int CH, int NV>
 __global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
-    const int wid = threadIdx.x >> 6;
+    __shared__ int e_s;
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
     const int slot = blockIdx.y, r = blockIdx.z;
     const int i0 = (blockIdx.x * 4 + wid) * P;
+    if (a.topk_src && slot < a.k) {
+        const bool publish = blockIdx.x == 0 && slot == 0;
+        if (wid == 0) {
+            int my_e;
+            float my_w;
+            topk_wave<NV>(a.topk_src + (size_t)r * a.E, a.E, a.k, false, my_e, my_w);
+            const int es = __builtin_amdgcn_readlane(my_e, slot);
+            if (lane == 0) e_s = es;
+            // the routing arrays are the caller's (writable); the other
+            // expert kernels only read them, hence the const views
+            if (publish && lane < a.k) {
+                const_cast<int32_t *>(a.ids)[(size_t)r * a.k + lane] = my_e;
+                const_cast<float *>(a.w)[(size_t)r * a.k + lane] = my_w;
+            }
+        } else if (wid == 1 && publish && a.s_mode != 0) {
+            const float s = a.s_mode == 1 ? sigmoid(dot_bf16_row_stream(a.wsg, a.x + (size_t)r * a.ldx, a.H)) : 1.0f;
+            if (lane == 0) const_cast<float *>(a.s)[r] = s;
+        }
+        __syncthreads();
+    }
     if (slot == a.k) {
         const ExpertSet &X = a.shared;
         if (r != 0 || i0 >= X.inter) return;
@@ -258,7 +284,7 @@ __global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
             rows.apply(a.x + (size_t)rr * a.ldx, a.H, X.inter, i0, a.h + (size_t)(a.R * a.k + rr) * a.hstride);
         return;
     }
-    const int e = a.ids[(size_t)r * a.k + slot];
+    const int e = a.topk_src ? e_s : a.ids[(size_t)r * a.k + slot];
     if (e < 0 || e >= a.E) {
         if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, kErrBadExpertId);
         return;
@@ -637,7 +663,14 @@ static hipError_t gate_up_r1_fmt(const FfnArgs &a, hipStream_t st) {
     const int inter = a.R > 1 ? max_inter(a) : a.routed.inter;
     const int slots = a.k + (a.R > 1 && a.shared.inter > 0 ? 1 : 0);
     dim3 grid((inter + 4 * P - 1) / (4 * P), slots, a.R), block(256);
-    MOE_CH_DISPATCH(gate_up_chunks(FMT, a.H), hipLaunchKernelGGL((k_gate_up_r1<FMT, CH>), grid, block, 0, st, a));
+    // the in-kernel top-k holds NV logits a lane: 4 up to 256 experts, 8, 16
+    const int nv = topk_nv(a.E);
+    if (nv <= 4)
+        MOE_CH_DISPATCH(gate_up_chunks(FMT, a.H), hipLaunchKernelGGL((k_gate_up_r1<FMT, CH, 4>), grid, block, 0, st, a));
+    else if (nv <= 8)
+        MOE_CH_DISPATCH(gate_up_chunks(FMT, a.H), hipLaunchKernelGGL((k_gate_up_r1<FMT, CH, 8>), grid, block, 0, st, a));
+    else
+        MOE_CH_DISPATCH(gate_up_chunks(FMT, a.H), hipLaunchKernelGGL((k_gate_up_r1<FMT, CH, 16>), grid, block, 0, st, a));
     return hipGetLastError();
 }
 

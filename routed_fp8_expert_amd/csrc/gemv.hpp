@@ -52,6 +52,29 @@ __device__ __forceinline__ float dot_bf16_row(const u32x4 (&wv)[NCH], const uint
     return group_sum<kWave>(acc);
 }
 
+// x_r . w with the bits of load_bf16_row<16> + dot_bf16_row<16> (the same
+// lane-strided chunks in the same order, the same wave sum), four chunks per
+// lane in flight instead of sixteen held in registers.
+__device__ __forceinline__ float dot_bf16_row_stream(const uint16_t *wrow, const uint16_t *xr, int H) {
+    const int lane = threadIdx.x & (kWave - 1), nch = H >> 3;
+    float acc = 0.0f;
+#pragma unroll
+    for (int t0 = 0; t0 < 16; t0 += 4) {
+        if (kWave * t0 >= nch) break;
+        u32x4 wv[4], xv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = lane + kWave * (t0 + t), cc = c < nch ? c : nch - 1;
+            wv[t] = ld16_stream(wrow + (size_t)cc * 8);
+            xv[t] = ld16(xr + (size_t)cc * 8);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (lane + kWave * (t0 + t) < nch) acc = dot8_bf16(wv[t], xv[t], acc);
+    }
+    return group_sum<kWave>(acc);
+}
+
 // ------------------------------------------------------------------ top-k
 
 __device__ __forceinline__ float ld_agent(const float *p) {

@@ -71,6 +71,10 @@ struct FfnArgs {
     float norm_eps;
     uint16_t *norm_out;         // bf16 [R][ldn]
     int64_t ldn;
+    // few-rows steps: the gate/up blocks take their row's top-k themselves
+    const float *topk_src;      // logits [R][E] to select from; null = ids already published
+    const uint16_t *wsg;        // shared-gate vector (s_mode 1)
+    int s_mode;                 // 0: s written by the router, 1: s = sigmoid(x . wsg), 2: s = 1
 };
 
 // Dense fp8 block-128 projection y = x . dequant(W)^T.

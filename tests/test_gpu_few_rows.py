@@ -67,6 +67,23 @@ def test_few_rows_path_equals_grouped_path(moe, orc, name, rows):
     check_layer(orc, wl, W, x, li, res0, yf, rf, tf, what=f"{name} R{rows} few")
 
 
+@pytest.mark.parametrize("logits", [True, False])
+def test_few_rows_ungated_shared_expert(moe, orc, logits):
+    """No shared-gate vector: s = 1 on both paths (given logits or the router)."""
+    wl = syn.WORKLOADS["tiny"]
+    W = dict(syn.make_layer_weights(wl, 0, "cuda"))
+    W["shared_gate_w"] = None
+    x, _ = tie_free_x(orc, wl, W, 0, 4, device="cuda")
+    li = syn.make_logits_in(syn.WORKLOADS["a3b_multi"], 0, 4, "cuda")[:, :wl.n_experts].contiguous() if logits else None
+    res0 = syn.make_residual(wl, 0, 4, "cuda")
+    yf, rf, tf = _forward(moe, 8, wl, W, x, li, res0)
+    yg, rg, tg = _forward(moe, 0, wl, W, x, li, res0)
+    assert np.array_equal(bits(yf), bits(yg))
+    assert bool(torch.all(tf.shared_gate == 1.0)) and torch.equal(tf.topk_ids, tg.topk_ids)
+    orc.set_threads(oracle_threads())
+    check_layer(orc, wl, W, x, li, res0, yf, rf, tf, what=f"tiny ungated few logits={logits}")
+
+
 def test_grouping_arrays_optional(moe, orc):
     wl = syn.WORKLOADS["a3b_multi"]
     W = syn.make_layer_weights(wl, 1, "cuda")
