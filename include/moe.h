@@ -193,8 +193,10 @@ MOE_API int moe_ctx_set_one_row_path(moe_ctx *ctx, int path);
 /* Steps of 2 to `rows` rows (at the default arm choice) run without grouping:
  * routing, then one GEMV per (row, slot) with the one-row kernels (the shared
  * expert's gate/up once for all rows), down fused with the blend per row.
- * Each row's result has the bits of a one-row call.  0 turns it off; the
- * default is 8 (env MOE_FEW_ROWS).  MOE_ERR_INVALID_ARG for rows < 0. */
+ * Each row's result has the bits of a one-row call.  0 turns it off; -1 (the
+ * default; env MOE_FEW_ROWS) chooses: 8 rows where a row's k+1 intermediate
+ * vectors take at most 32 KB (the 35B-A3B shape), else 0 (the 397B-A17B shape
+ * measured faster grouped).  MOE_ERR_INVALID_ARG for rows < -1. */
 MOE_API int moe_ctx_set_few_rows(moe_ctx *ctx, int rows);
 /* Device-side error word: kernels that meet an expert id outside [0, E)
  * skip it and set bit 0; a bounded wait that timed out sets bit 1.  Synchronises the ctx's device; clears the word

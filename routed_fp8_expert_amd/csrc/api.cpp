@@ -27,6 +27,8 @@ enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, k
 constexpr int kDenseMaxK = 8192;         // a wave's 64 lanes hold one scale per 128-wide block
 constexpr int kDenseMaxRows = 1 << 20;   // matrix-core grid rows stay far below 65535
 constexpr int kDefaultFewRows = 8;       // steps of 2..8 rows: one GEMV per row and slot (measured)
+constexpr int kFewRowsAuto = -1;         // ctx default: kDefaultFewRows where the per-row h fits kFewRowsHBytes
+constexpr size_t kFewRowsHBytes = 32 * 1024;
 constexpr int kFusedTopkRows = 4;        // few-rows steps up to 4 rows select in the gate/up blocks (measured)
 constexpr int kDefaultMfmaMinRows = 4;   // rows per expert from which the MFMA arm pays (measured)
 constexpr int kMaxRows = 1024;
@@ -49,7 +51,7 @@ struct moe_ctx {
     int status = MOE_OK;
     int64_t fault_countdown = 0;
     int mfma_min_rows = kDefaultMfmaMinRows;
-    int few_rows = kDefaultFewRows;
+    int few_rows = kFewRowsAuto;
     int force_arm = 0;
     int one_row_path = 0;        // 0 = single launch where built, 1 = three launches
     uint32_t *words = nullptr;   // device: kSyncWords words
@@ -420,7 +422,18 @@ int do_ffn(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
 // Steps of a few rows (2 .. few_rows, the default arm choice): no grouping;
 // the one-row gate/up and down+blend kernels over every (row, slot), the
 // shared expert's gate/up once for all rows.
-bool few_rows_path(const moe_ctx *c, int R) { return R >= 2 && c->force_arm == 0 && R <= c->few_rows; }
+// The automatic choice: the few-rows down kernel stages a row's k+1 h vectors
+// in every workgroup; where they exceed 32 KB (the 397B-A17B shape: 45 KB) the
+// grouped path measured faster at every row count.
+bool few_rows_path(const moe_ctx *c, const moe_layer_weights *w, int R) {
+    if (R < 2 || c->force_arm != 0) return false;
+    int lim = c->few_rows;
+    if (lim == kFewRowsAuto) {
+        const size_t h = (size_t)(w->top_k + 1) * (size_t)std::max(w->inter, w->shared_inter) * 4;
+        lim = h <= kFewRowsHBytes ? kDefaultFewRows : 0;
+    }
+    return R <= lim;
+}
 
 int do_ffn_few(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
     int rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up_r1(a, st); });
@@ -497,7 +510,7 @@ MOE_API int moe_ctx_create(int device, moe_ctx **out) {
     }
     if (const char *v = getenv("MOE_FAULT_AT")) c->fault_countdown = std::max<long long>(0, atoll(v));
     if (const char *v = getenv("MOE_MFMA_MIN_ROWS")) c->mfma_min_rows = std::max(0, atoi(v));
-    if (const char *v = getenv("MOE_FEW_ROWS")) c->few_rows = std::max(0, atoi(v));
+    if (const char *v = getenv("MOE_FEW_ROWS")) c->few_rows = std::max(kFewRowsAuto, atoi(v));
     if (const char *v = getenv("MOE_ONE_ROW_PATH")) c->one_row_path = !strcmp(v, "split") ? 1 : 0;
     if (const char *v = getenv("MOE_FORCE_ARM")) {
         if (!strcmp(v, "gemv")) c->force_arm = 1;
@@ -541,7 +554,7 @@ MOE_API int moe_ctx_set_force_arm(moe_ctx *c, int arm) {
 }
 
 MOE_API int moe_ctx_set_few_rows(moe_ctx *c, int rows) {
-    if (!c || rows < 0) return MOE_ERR_INVALID_ARG;
+    if (!c || rows < kFewRowsAuto) return MOE_ERR_INVALID_ARG;
     c->few_rows = rows;
     return MOE_OK;
 }
@@ -633,7 +646,7 @@ MOE_API int moe_expert_ffn(moe_ctx *c, const moe_layer_weights *w, const void *x
     const hipStream_t st = (hipStream_t)stream;
     const Layout L = make_layout(w, R);
     const RoutingPtrs rp = routing_ptrs(in, ws, L);
-    if (few_rows_path(c, R)) return do_ffn_few(c, ffn_args(c, w, x, R, ldx, rp, y, res, ldy, ws, L), st);
+    if (few_rows_path(c, w, R)) return do_ffn_few(c, ffn_args(c, w, x, R, ldx, rp, y, res, ldy, ws, L), st);
     if (R >= 2) {
         const moe::RouteArgs a = route_args(c, w, x, R, ldx, nullptr, rp, ws, L);
         rc = launch(c, MOE_K_GROUP, st, [&] { return moe::launch_plan(a, st); });
@@ -669,7 +682,7 @@ MOE_API int moe_layer_forward_norm(moe_ctx *c, const moe_layer_weights *w, const
         fa.ldn = norm->ldo;
     }
     if (R == 1) return do_layer_r1(c, ra, fa, st);
-    if (few_rows_path(c, R)) {
+    if (few_rows_path(c, w, R)) {
         // the router GEMV (unless logits are given); the gate/up blocks take
         // their rows' top-k and publish the routing; the grouping arrays are
         // written only when the caller asked for them

@@ -122,11 +122,12 @@ def test_expert_ffn_on_both_paths(moe, orc):
     assert np.array_equal(out[0], out[1])
 
 
-def test_few_rows_knob_rejects_negative(moe):
+def test_few_rows_knob_rejects_below_auto(moe):
     c = moe.Ctx(0)
     with pytest.raises(moe.MoeError):
-        moe.moe_ctx_set_few_rows(c, -1)
+        moe.moe_ctx_set_few_rows(c, -2)
     moe.moe_ctx_set_few_rows(c, 0)
+    moe.moe_ctx_set_few_rows(c, -1)
     c.close()
 
 
