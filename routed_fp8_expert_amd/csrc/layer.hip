@@ -371,7 +371,9 @@ static bool layer_resident(const RouteArgs &r, const FfnArgs &a) {
 }
 
 // The shapes the single launch is built for: the tiny layer (H 256, E 16,
-// I 128) and the 35B-A3B layer (H 2048, E 256, I 512, fp8).  KS: the most
+// I 128) and the 35B-A3B layer (H 2048, E 256, I 512) in fp8 and in the
+// other expert formats (int8 and int4 per row, int4-g64, fp8 with bf16
+// scales; int4 rows of 512 codes take 16 lanes a row in down).  KS: the most
 // slots (routed + shared) an instantiation holds; HS: the intermediate size
 // of every slot (routed and shared alike).  Other shapes, and any launch
 // whose workgroups do not all fit on the device at once (the 397B-A17B
@@ -379,7 +381,11 @@ static bool layer_resident(const RouteArgs &r, const FfnArgs &a) {
 // slower than the three launches), take the three-launch path.
 #define MOE_LAYER_SHAPES(X)             \
     X(kFp8, 1, 1, 8, 1, 17, 128)        \
-    X(kFp8, 4, 4, 32, 1, 9, 512)
+    X(kFp8, 4, 4, 32, 1, 9, 512)        \
+    X(kFp8Bf16s, 4, 4, 32, 1, 9, 512)   \
+    X(kInt8Row, 4, 4, 32, 1, 9, 512)    \
+    X(kInt4Row, 4, 4, 16, 1, 9, 512)    \
+    X(kInt4G64, 4, 4, 16, 1, 9, 512)
 
 bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
