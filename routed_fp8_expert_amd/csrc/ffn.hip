@@ -331,12 +331,28 @@ __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
             rows[j].load(X, ok ? e : 0, o, sub, live && ok);
         }
     }
+    // 32-code chunks (e2m1, int4): h staged in chunk-quad order per slot
+    // (DownRow::dot_perm), the quad of slot j starting at element c*CPC + f
+    // going to quad (f/4)*(I_j/CPC) + c, so the lanes of a row group read
+    // consecutive quads, not quads 128 bytes apart (LDS bank conflicts);
+    // measured faster there, slower for 16-code chunks, which keep the plain
+    // layout
+    constexpr bool PERM = !byte_codes(FMT);
     if (HLDS) {
+        constexpr int CPC = cols_per_chunk<FMT>();
         const int n4 = a.hstride / 4;
         const f32x4 *src = reinterpret_cast<const f32x4 *>(a.h);
         for (int i = threadIdx.x; i < nslots * n4; i += 256) {
-            const int j = i / n4;
-            hlds4[i] = src[hrow(j) * n4 + (i - j * n4)];
+            const int j = i / n4, q4 = i - j * n4;
+            if (!PERM) {
+                hlds4[i] = src[hrow(j) * n4 + q4];
+                continue;
+            }
+            const int ij = j == a.k ? a.shared.inter : a.routed.inter;
+            if (4 * q4 < ij) {
+                const int c = (4 * q4) / CPC, f = (4 * q4) % CPC;
+                hlds4[j * n4 + (f >> 2) * (ij / CPC) + c] = src[hrow(j) * n4 + q4];
+            }
         }
         __syncthreads();
     }
@@ -351,8 +367,9 @@ __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
                 if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, kErrBadExpertId);
                 continue;
             }
-            const float *hp = HLDS ? hl + (size_t)j * a.hstride : a.h + hrow(j) * a.hstride;
-            float d = rows[j].dot(hp, X.inter, sub);
+            float d = !HLDS ? rows[j].dot(a.h + hrow(j) * a.hstride, X.inter, sub)
+                      : PERM ? rows[j].dot_perm(hl + (size_t)j * a.hstride, X.inter, sub)
+                             : rows[j].dot(hl + (size_t)j * a.hstride, X.inter, sub);
             d *= global_scale<FMT>(X.dn_g, es[j]);
             y = fmaf(sh ? a.s[r] : a.w[(size_t)r * a.k + j], d, y);
         }
