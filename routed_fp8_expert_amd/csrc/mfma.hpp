@@ -12,7 +12,9 @@
 //
 // Work unit: an expert's 16-row tile by 16 gate (+ 16 up) columns (gate/up)
 // or 32 output columns (down) per wave, over all of K, with the next K
-// block's loads in flight while one is multiplied; no cross-wave reduction.
+// block's loads in flight while one is multiplied; the activation (or h)
+// tile staged through LDS for the workgroup's four waves; no cross-wave
+// reduction.
 // The units run as the leading workgroups of the grouped gate/up and down
 // launches (ffn.hip), beside the GEMV arm's.  Operand layout of the
 // 16x16x32 MFMA: A[i][k] in lane i + 16*(k/8) element k%8, B[k][j] in lane
@@ -101,31 +103,41 @@ __device__ __forceinline__ int mtile_entry(const MTile &m, int i, int nk) {
 
 constexpr int kMfmaWaves = 4;    // waves per workgroup; each owns its own columns over all of K
 
-// Per-lane operands of one 128-wide K block of the gate/up tile: the gate
-// and up weight chunks (16 codes each, two 64-wide halves) and the lane's
-// row of activations for the same k (two 8-value pieces per half).
+// Activation tiles go through LDS.  A fragment load straight from memory
+// (16 rows x 64 bytes per instruction, the rows H elements apart) runs at
+// about a third of the rate of whole-row pieces (measured on MI355X: ~37
+// against ~120 GB/s per compute unit from L2), and the workgroup's four
+// waves read the same tile; so the workgroup loads each 128-wide K block of
+// the tile once, 16 bytes a thread in whole 256-byte row pieces, into a
+// double-buffered LDS tile whose rows are padded so that the fragment reads
+// of 16 lanes hit distinct banks.
+constexpr int kXRow = 128 + 8;   // bf16 per staged activation row (8 of padding)
+constexpr int kHRow = 128 + 4;   // f32 per staged h row (4 of padding)
+
+// The gate and up weight chunks of one 128-wide K block (16 codes each, two
+// 64-wide halves).
 struct GuStage {
-    u32x4 g[2], u[2], x[2][2];
+    u32x4 g[2], u[2];
 };
 
-__device__ __forceinline__ void gu_load(GuStage &s, const uint8_t *wg, const uint8_t *wu, const uint16_t *xr,
-                                        bool rv, int kb, int grp) {
+__device__ __forceinline__ void gu_load(GuStage &s, const uint8_t *wg, const uint8_t *wu, int kb, int grp) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int k0 = kb * 128 + c * 64 + grp * 16;
         s.g[c] = ld16_stream(wg + k0);
         s.u[c] = ld16_stream(wu + k0);
-        s.x[c][0] = rv ? ld16(xr + k0) : u32x4{0u, 0u, 0u, 0u};
-        s.x[c][1] = rv ? ld16(xr + k0 + 8) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
-// acc += scale * (X_tile . W^T) over one K block, gate and up.
-__device__ __forceinline__ void gu_step(const GuStage &s, float sg, float su, f32x4 &accg, f32x4 &accu) {
+// acc += scale * (X_tile . W^T) over one K block, gate and up; the lane's
+// activation fragments (row col, k = c*64 + grp*16 .. +15) from the LDS tile.
+__device__ __forceinline__ void gu_step(const GuStage &s, const uint16_t (*xs)[kXRow], int col, int grp, float sg,
+                                        float su, f32x4 &accg, f32x4 &accu) {
     f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        const bf16x8 x0 = as_bf16x8(s.x[c][0]), x1 = as_bf16x8(s.x[c][1]);
+        const u32x4 *xp = reinterpret_cast<const u32x4 *>(&xs[col][c * 64 + grp * 16]);
+        const bf16x8 x0 = as_bf16x8(xp[0]), x1 = as_bf16x8(xp[1]);
         tg = mfma(x0, e4m3x8_bf16(s.g[c].x, s.g[c].y), tg);
         tg = mfma(x1, e4m3x8_bf16(s.g[c].z, s.g[c].w), tg);
         tu = mfma(x0, e4m3x8_bf16(s.u[c].x, s.u[c].y), tu);
@@ -140,20 +152,25 @@ __device__ __forceinline__ void gu_step(const GuStage &s, float sg, float su, f3
 
 // h = silu(X_tile . Wg^T) * (X_tile . Wu^T) for a 16-row tile and 16 gate
 // columns (+ the 16 matching up columns) per wave, all of K; two K blocks of
-// loads are in flight while one is multiplied.
+// weight loads in flight, the next K block of activations staged while one
+// is multiplied.
 __device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int tile) {
+    __shared__ uint16_t xs[2][kTileRows][kXRow];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
     const MTile t = resolve_mtile(a, tile);
     if (!t.valid) return;
     const ExpertSet &X = t.X;
     const int I = X.inter, H = a.H, nk = a.R * a.k;
+    // I is a multiple of 128, so a workgroup's 64 columns are all in range or
+    // all past it: the exit is uniform (the waves share the barriers below)
+    if (bx * kMfmaWaves * 16 >= I) return;
     const int n0 = (bx * kMfmaWaves + wid) * 16;
-    if (n0 >= I) return;
     const int col = lane & 15, grp = lane >> 4;
     const int nkb = H >> 7;
-    const int ent = mtile_entry(t, col, nk);
-    const bool rv = ent >= 0;
-    const uint16_t *xr = a.x + (size_t)(rv ? (ent < nk ? ent / a.k : ent - nk) : 0) * a.ldx;
+    // this thread's staging piece: 16 bytes (8 values) of tile row threadIdx/16
+    const int srow = threadIdx.x >> 4, spiece = threadIdx.x & 15;
+    const int sent = mtile_entry(t, srow, nk);   // rows without an entry stage row 0 (results dropped)
+    const uint16_t *sx = a.x + (size_t)(sent >= 0 ? (sent < nk ? sent / a.k : sent - nk) : 0) * a.ldx + spiece * 8;
     int oent[4];   // entries of the output rows this lane holds (D layout), loaded early
 #pragma unroll
     for (int i = 0; i < 4; ++i) oent[i] = mtile_entry(t, 4 * grp + i, nk);
@@ -166,14 +183,25 @@ __device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int 
 
     f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
     GuStage s0, s1;
-    gu_load(s0, wg, wu, xr, rv, 0, grp);
-    if (nkb > 1) gu_load(s1, wg, wu, xr, rv, 1, grp);
+    gu_load(s0, wg, wu, 0, grp);
+    if (nkb > 1) gu_load(s1, wg, wu, 1, grp);
+    *reinterpret_cast<u32x4 *>(&xs[0][srow][spiece * 8]) = ld16(sx);
+    __syncthreads();
+    // one K block: the next block's activations loaded, this block multiplied
+    // from LDS, the next block stored into the other buffer, a barrier
+    auto step = [&](int kb, const GuStage &s) {
+        u32x4 xn = {0u, 0u, 0u, 0u};
+        if (kb + 1 < nkb) xn = ld16(sx + (kb + 1) * 128);
+        gu_step(s, xs[kb & 1], col, grp, readlane(sgl, kb), readlane(sul, kb), accg, accu);
+        if (kb + 1 < nkb) *reinterpret_cast<u32x4 *>(&xs[(kb + 1) & 1][srow][spiece * 8]) = xn;
+        __syncthreads();
+    };
     for (int kb = 0; kb < nkb; kb += 2) {
-        gu_step(s0, readlane(sgl, kb), readlane(sul, kb), accg, accu);
-        if (kb + 2 < nkb) gu_load(s0, wg, wu, xr, rv, kb + 2, grp);
+        step(kb, s0);
+        if (kb + 2 < nkb) gu_load(s0, wg, wu, kb + 2, grp);
         if (kb + 1 < nkb) {
-            gu_step(s1, readlane(sgl, kb + 1), readlane(sul, kb + 1), accg, accu);
-            if (kb + 3 < nkb) gu_load(s1, wg, wu, xr, rv, kb + 3, grp);
+            step(kb + 1, s1);
+            if (kb + 3 < nkb) gu_load(s1, wg, wu, kb + 3, grp);
         }
     }
     // D[i][j]: lane holds column j = col, rows 4*grp .. 4*grp+3
@@ -186,38 +214,39 @@ __device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int 
 
 // ------------------------------------------------------------------ down
 
-// Per-lane operands of one 128-wide K block of the down tile: the weight
-// chunks of the wave's two 16-column tiles and the lane's row of h (f32).
+// The weight chunks of one 128-wide K block of the down tile: the wave's two
+// 16-column tiles, two 64-wide halves.
 struct DnStage {
     u32x4 w[2][2];
-    f32x4 h[2][4];
 };
 
-__device__ __forceinline__ void dn_load(DnStage &s, const uint8_t *const (&wd)[2], const float *hr, bool rv, int kb,
-                                        int grp) {
+__device__ __forceinline__ void dn_load(DnStage &s, const uint8_t *const (&wd)[2], int kb, int grp) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int k0 = kb * 128 + c * 64 + grp * 16;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) s.w[nt][c] = ld16_stream(wd[nt] + k0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            s.h[c][q] = rv ? *reinterpret_cast<const f32x4 *>(hr + k0 + 4 * q) : f32x4{0, 0, 0, 0};
     }
 }
 
-// acc[nt] += scale[nt] * (h_tile . W^T) over one K block; h enters as
-// hi + lo bf16.
-__device__ __forceinline__ void dn_step(const DnStage &s, const float (&sc)[2], f32x4 (&acc)[2]) {
+// acc[nt] += scale[nt] * (h_tile . W^T) over one K block; the lane's h
+// (row col, k = c*64 + grp*16 .. +15) from the LDS tile enters as hi + lo
+// bf16.
+__device__ __forceinline__ void dn_step(const DnStage &s, const float (*hs)[kHRow], int col, int grp,
+                                        const float (&sc)[2], f32x4 (&acc)[2]) {
     f32x4 td[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+        const f32x4 *hp = reinterpret_cast<const f32x4 *>(&hs[col][c * 64 + grp * 16]);
+        f32x4 h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = hp[q];
         bf16x8 hi0, lo0, hi1, lo1;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float v0 = s.h[c][q][i], v1 = s.h[c][q + 2][i];
+                const float v0 = h[q][i], v1 = h[q + 2][i];
                 const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1;
                 hi0[q * 4 + i] = b0;
                 lo0[q * 4 + i] = (__bf16)(v0 - (float)b0);
@@ -240,20 +269,27 @@ __device__ __forceinline__ void dn_step(const DnStage &s, const float (&sc)[2], 
 }
 
 // D = h_tile . W_dn^T for a 16-row tile and 32 output columns per wave (two
-// 16-column tiles), all of K = I; two K blocks of loads in flight.
+// 16-column tiles), all of K = I; two K blocks of weight loads in flight, the
+// next K block of h staged in LDS (two 16-byte loads a thread, whole
+// 256-byte row pieces) while one is multiplied.
 __device__ __forceinline__ void mfma_down_unit(const FfnArgs &a, int bx, int tile) {
+    __shared__ float hs[2][kTileRows][kHRow];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
     const MTile t = resolve_mtile(a, tile);
     if (!t.valid) return;
     const ExpertSet &X = t.X;
     const int I = X.inter, H = a.H, nk = a.R * a.k;
+    // H is a multiple of 128: a workgroup's 128 columns are all in range or
+    // all past it (uniform exit; the waves share the barriers below)
+    if (bx * kMfmaWaves * 32 >= H) return;
     const int n0 = (bx * kMfmaWaves + wid) * 32;
-    if (n0 >= H) return;
     const int col = lane & 15, grp = lane >> 4;
     const int nkb = I >> 7;
-    const int ent = mtile_entry(t, col, nk);
-    const bool rv = ent >= 0;
-    const float *hr = a.h + (size_t)(rv ? ent : 0) * a.hstride;
+    // staging: thread t loads values 4*(t%16) .. +3 and 64 + 4*(t%16) .. +3 of
+    // the K block for tile row t/16
+    const int srow = threadIdx.x >> 4, spiece = threadIdx.x & 15;
+    const int sent = mtile_entry(t, srow, nk);   // rows without an entry stage entry 0's h (results dropped)
+    const float *sh = a.h + (size_t)(sent >= 0 ? sent : 0) * a.hstride + spiece * 4;
     int oent[4];   // entries of the output rows this lane holds (D layout), loaded early
 #pragma unroll
     for (int i = 0; i < 4; ++i) oent[i] = mtile_entry(t, 4 * grp + i, nk);
@@ -267,18 +303,31 @@ __device__ __forceinline__ void mfma_down_unit(const FfnArgs &a, int bx, int til
     }
     f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
     DnStage s0, s1;
-    dn_load(s0, wd, hr, rv, 0, grp);
-    if (nkb > 1) dn_load(s1, wd, hr, rv, 1, grp);
-    for (int kb = 0; kb < nkb; kb += 2) {
-        {
-            const float sc[2] = {readlane(sl[0], kb), readlane(sl[1], kb)};
-            dn_step(s0, sc, acc);
-        }
-        if (kb + 2 < nkb) dn_load(s0, wd, hr, rv, kb + 2, grp);
+    dn_load(s0, wd, 0, grp);
+    if (nkb > 1) dn_load(s1, wd, 1, grp);
+    *reinterpret_cast<f32x4 *>(&hs[0][srow][spiece * 4]) = *reinterpret_cast<const f32x4 *>(sh);
+    *reinterpret_cast<f32x4 *>(&hs[0][srow][64 + spiece * 4]) = *reinterpret_cast<const f32x4 *>(sh + 64);
+    __syncthreads();
+    auto step = [&](int kb, const DnStage &s) {
+        f32x4 hn0 = {0, 0, 0, 0}, hn1 = {0, 0, 0, 0};
         if (kb + 1 < nkb) {
-            const float sc[2] = {readlane(sl[0], kb + 1), readlane(sl[1], kb + 1)};
-            dn_step(s1, sc, acc);
-            if (kb + 3 < nkb) dn_load(s1, wd, hr, rv, kb + 3, grp);
+            hn0 = *reinterpret_cast<const f32x4 *>(sh + (kb + 1) * 128);
+            hn1 = *reinterpret_cast<const f32x4 *>(sh + (kb + 1) * 128 + 64);
+        }
+        const float sc[2] = {readlane(sl[0], kb), readlane(sl[1], kb)};
+        dn_step(s, hs[kb & 1], col, grp, sc, acc);
+        if (kb + 1 < nkb) {
+            *reinterpret_cast<f32x4 *>(&hs[(kb + 1) & 1][srow][spiece * 4]) = hn0;
+            *reinterpret_cast<f32x4 *>(&hs[(kb + 1) & 1][srow][64 + spiece * 4]) = hn1;
+        }
+        __syncthreads();
+    };
+    for (int kb = 0; kb < nkb; kb += 2) {
+        step(kb, s0);
+        if (kb + 2 < nkb) dn_load(s0, wd, kb + 2, grp);
+        if (kb + 1 < nkb) {
+            step(kb + 1, s1);
+            if (kb + 3 < nkb) dn_load(s1, wd, kb + 3, grp);
         }
     }
 #pragma unroll
