@@ -89,43 +89,55 @@ __global__ __launch_bounds__(256) void k_dense_gemv(DenseArgs a) {
 // leaves its partial tiles in LDS.  Every 8 tiles (128 rows) the partials are
 // summed over the K slices in slice order and rounded once.  A row's result
 // depends on nothing but the row, so any row count gives the same bits for it.
+// A tile's activations for this wave's K slice, as loaded: block b, load i
+// holds rows 4i + lane/16 of the tile, values 8*(lane%16) .. +7 of the
+// block (whole 256-byte row pieces; fragment-shaped loads, 16 rows x 64
+// bytes each, run at about a third of the rate from L2).
 template <int KBMAX>
 struct DenseXs {
-    u32x4 v[KBMAX][2][2];   // [K block][64-wide half][8-value piece]
+    u32x4 v[KBMAX][4];
 };
+
+constexpr int kDXRow = 128 + 8;   // bf16 per row of a wave's staged K block (8 of padding)
 
 template <int KBMAX>
 __device__ __forceinline__ void dense_load_x(DenseXs<KBMAX> &xs, const DenseArgs &a, int rt, int kb0, int nkb,
-                                             int col, int grp) {
-    const int ra = rt * 16 + col;
-    const uint16_t *xr = a.x + (size_t)(ra < a.R ? ra : 0) * a.ldx;   // rows past R: row 0, results dropped
+                                             int lane) {
+    const int piece = lane & 15;
 #pragma unroll
     for (int b = 0; b < KBMAX; ++b) {
         const int kb = kb0 + b < nkb ? kb0 + b : nkb - 1;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int k0 = kb * 128 + c * 64 + grp * 16;
-            xs.v[b][c][0] = ld16(xr + k0);
-            xs.v[b][c][1] = ld16(xr + k0 + 8);
+        for (int i = 0; i < 4; ++i) {
+            const int ra = rt * 16 + i * 4 + (lane >> 4);
+            const uint16_t *xr = a.x + (size_t)(ra < a.R ? ra : 0) * a.ldx;   // rows past R: row 0, results dropped
+            xs.v[b][i] = ld16(xr + kb * 128 + piece * 8);
         }
     }
 }
 
-// This wave's K-slice products for one tile; nmine is wave-uniform.
+// This wave's K-slice products for one tile; nmine is wave-uniform.  Each
+// K block goes through the wave's LDS block (rows padded: the fragment
+// reads of 16 lanes hit distinct banks) into MFMA fragments.
 template <int CT, int KBMAX>
 __device__ __forceinline__ void dense_products(f32x4 (&acc)[CT], const u32x4 (&w)[KBMAX][CT][2], float sl,
-                                               const DenseXs<KBMAX> &cur, int nmine) {
+                                               const DenseXs<KBMAX> &cur, int nmine, uint16_t *xw, int lane) {
+    const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int b = 0; b < KBMAX; ++b) {
         if (b < nmine) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4 *>(xw + (i * 4 + (lane >> 4)) * kDXRow + (lane & 15) * 8) = cur.v[b][i];
             f32x4 td[CT];
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) td[ct] = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const bf16x8 xa = as_bf16x8(cur.v[b][c][0]), xb = as_bf16x8(cur.v[b][c][1]);
+                const u32x4 *xp = reinterpret_cast<const u32x4 *>(xw + col * kDXRow + c * 64 + grp * 16);
+                const bf16x8 xa = as_bf16x8(xp[0]), xb = as_bf16x8(xp[1]);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     u32x4 q = w[b][ct][c];
@@ -152,7 +164,7 @@ template <int CT, int KS, int RS, int KBMAX, int D>
 __global__ __launch_bounds__(KS * RS * 64) void k_dense_mfma(DenseArgs a) {
     static_assert((kDenseChunkTiles / RS) % D == 0, "the activation ring turns whole within a chunk");
     constexpr int NT = KS * RS * 64;
-    extern __shared__ float part[];   // [kDenseChunkTiles][KS][CT][256]
+    extern __shared__ float part[];   // [kDenseChunkTiles][KS][CT][256], then the waves' [16][kDXRow] bf16 blocks
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ks = wid % KS, rg = wid / KS;
@@ -160,6 +172,7 @@ __global__ __launch_bounds__(KS * RS * 64) void k_dense_mfma(DenseArgs a) {
     const int n0 = blockIdx.x * (16 * CT);
     const int nkb = a.K >> 7;
     const int kb0 = ks * nkb / KS, nmine = (ks + 1) * nkb / KS - kb0;   // nmine <= KBMAX (host)
+    uint16_t *xw = reinterpret_cast<uint16_t *>(part + kDenseChunkTiles * KS * CT * 256) + wid * 16 * kDXRow;
 
     u32x4 w[KBMAX][CT][2];
 #pragma unroll
@@ -179,17 +192,17 @@ __global__ __launch_bounds__(KS * RS * 64) void k_dense_mfma(DenseArgs a) {
     DenseXs<KBMAX> xb[D];
 #pragma unroll
     for (int d = 0; d + 1 < D; ++d)
-        if (rg + d * RS < nrt) dense_load_x(xb[d], a, rg + d * RS, kb0, nkb, col, grp);
+        if (rg + d * RS < nrt) dense_load_x(xb[d], a, rg + d * RS, kb0, nkb, lane);
     for (int t0 = 0; t0 < nrt; t0 += kDenseChunkTiles) {
 #pragma unroll
         for (int j = 0; j < kDenseChunkTiles / RS; ++j) {
             const int t = t0 + rg + j * RS;
             if (t < nrt) {
-                if (D == 1) dense_load_x(xb[0], a, t, kb0, nkb, col, grp);   // no ring: this tile now
+                if (D == 1) dense_load_x(xb[0], a, t, kb0, nkb, lane);   // no ring: this tile now
                 f32x4 acc[CT];
-                dense_products<CT, KBMAX>(acc, w, sl, xb[j % D], nmine);
+                dense_products<CT, KBMAX>(acc, w, sl, xb[j % D], nmine, xw, lane);
                 const int tn = t + (D - 1) * RS;
-                if (D > 1 && tn < nrt) dense_load_x(xb[(j + D - 1) % D], a, tn, kb0, nkb, col, grp);
+                if (D > 1 && tn < nrt) dense_load_x(xb[(j + D - 1) % D], a, tn, kb0, nkb, lane);
                 float *pp = part + ((j * RS + rg) * KS + ks) * CT * 256;
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
@@ -226,7 +239,8 @@ static void dense_gemv_launch(const DenseArgs &a, hipStream_t st) {
 
 template <int CT, int KS, int RS, int KBMAX, int D>
 static void dense_mfma_launch(const DenseArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)kDenseChunkTiles * KS * CT * 256 * sizeof(float);
+    const size_t lds = (size_t)kDenseChunkTiles * KS * CT * 256 * sizeof(float) +
+                       (size_t)KS * RS * 16 * kDXRow * sizeof(uint16_t);
     hipLaunchKernelGGL((k_dense_mfma<CT, KS, RS, KBMAX, D>), dim3(a.N / (16 * CT)), dim3(KS * RS * 64), lds, st, a);
 }
 
