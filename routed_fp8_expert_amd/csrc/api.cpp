@@ -177,7 +177,7 @@ Layout make_layout(const moe_layer_weights *w, int R) {
     L.meta = take(moe::kMetaWords * 4);
     L.gemv = take(E * 4);
     L.mfma = take(E * 4);
-    L.tiles = take((E + 1) * 4);
+    L.tiles = take(2 * (E + 1) * 4);   // two row-tile prefixes (down, gate/up tiles)
     L.h = take(ne * hs * 4);
     L.dbuf = take(R >= 2 ? ne * H * 4 : 0);
     // replicas for the single-launch one-row layer
@@ -393,11 +393,15 @@ moe::FfnArgs ffn_args(moe_ctx *c, const moe_layer_weights *w, const void *x, int
     const int thr = R >= 2 ? mfma_threshold(c, w, R) : 0;
     a.shared_mfma = thr > 0 && w->shared_inter > 0 && R >= thr;
     a.mfma_max_tiles = 0;
+    a.mfma_gu_max_tiles = 0;
     if (thr > 0) {
-        // sum over MFMA experts of ceil(rows/32) <= R*k/32 + (number of such experts)
+        // sum over MFMA experts of ceil(rows/T) <= R*k/T + (number of such experts)
         const int rk = R * w->top_k;
-        constexpr int T = moe::kMfmaTileRows;
-        a.mfma_max_tiles = (rk + T - 1) / T + std::min(w->n_experts, rk / thr) + (a.shared_mfma ? (R + T - 1) / T : 0);
+        auto bound = [&](int T) {
+            return (rk + T - 1) / T + std::min(w->n_experts, rk / thr) + (a.shared_mfma ? (R + T - 1) / T : 0);
+        };
+        a.mfma_max_tiles = bound(moe::kMfmaTileRows);
+        a.mfma_gu_max_tiles = bound(moe::kMfmaGuTileRows);
     }
     return a;
 }

@@ -621,7 +621,7 @@ static hipError_t gate_up_fmt(const FfnArgs &a, hipStream_t st) {
     const int pm = ch <= 2 ? 4 : P;        // 4 pairs per wave while the registers allow
     const int gx = (max_inter(a) + 4 * pm - 1) / (4 * pm);
     const int nmx = mfma_gate_up_groups(max_inter(a));
-    const int nm = FMT == kFp8 && a.mfma_max_tiles > 0 ? nmx * a.mfma_max_tiles : 0;
+    const int nm = FMT == kFp8 && a.mfma_gu_max_tiles > 0 ? nmx * a.mfma_gu_max_tiles : 0;
     const long long nb = nm + (long long)gx * n_tasks(a);
     if (nb == 0) return hipSuccess;
     dim3 grid((unsigned)nb), block(256);

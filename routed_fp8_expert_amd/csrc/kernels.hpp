@@ -17,7 +17,8 @@ struct ExpertSet {
 // Per-step bookkeeping written by the grouping kernel, read by the expert
 // kernels (int32 words in the workspace).
 constexpr int kReplicas = 8;   // one copy per XCD (workgroups map to XCDs by index)
-constexpr int kMfmaTileRows = 16;   // rows of an expert per matrix-core tile
+constexpr int kMfmaTileRows = 16;   // rows of an expert per matrix-core tile (down)
+constexpr int kMfmaGuTileRows = 64; // rows of an expert per gate/up matrix-core tile
 
 // Weight formats (the values of the C ABI's moe_weight_format).
 enum : int { kFp8 = 0, kNvfp4 = 1, kInt8Row = 2, kInt4Row = 3, kInt4G64 = 4, kFp8Bf16s = 5 };
@@ -31,6 +32,7 @@ enum MetaWord : int {
     kMetaGemvCount = 0,   // routed experts on the GEMV arm
     kMetaMfmaCount = 1,   // routed experts on the MFMA arm
     kMetaMfmaTiles = 2,   // MFMA row tiles (routed)
+    kMetaMfmaGuTiles = 3, // gate/up MFMA row tiles of kMfmaGuTileRows (routed)
     kMetaWords = 16
 };
 
@@ -61,6 +63,7 @@ struct FfnArgs {
     uint32_t *err;
     int max_routed_tasks;       // grid bound on routed experts for R >= 2
     int mfma_max_tiles;         // grid bound on MFMA row tiles (0 = MFMA arm off)
+    int mfma_gu_max_tiles;      // grid bound on gate/up MFMA row tiles
     int shared_mfma;            // the shared expert's rows go to the MFMA arm
     uint32_t *sink;             // word the cache-warming reads fold into
     // single-launch one-row layer: per-XCD replicas of values crossing workgroups

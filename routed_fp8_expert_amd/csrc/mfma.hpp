@@ -10,11 +10,12 @@
 // as a bf16 pair hi + lo (hi = bf16(h), lo = bf16(h - hi)), two MFMAs, so h
 // keeps about 16 significant bits.
 //
-// Work unit: an expert's 16-row tile by 16 gate (+ 16 up) columns (gate/up)
-// or 32 output columns (down) per wave, over all of K, with the next K
-// block's loads in flight while one is multiplied; the activation (or h)
-// tile staged through LDS for the workgroup's four waves; no cross-wave
-// reduction.
+// Work unit: an expert's 64-row tile by 16 gate (+ 16 up) columns per wave
+// (gate/up; each K block's weight codes are converted once and multiplied
+// into up to four 16-row subtiles) or a 16-row tile by 32 output columns per
+// wave (down), over all of K, with the next K block's loads in flight while
+// one is multiplied; the activation (or h) tile staged through LDS for the
+// workgroup's four waves; no cross-wave reduction.
 // The units run as the leading workgroups of the grouped gate/up and down
 // launches (ffn.hip), beside the GEMV arm's.  Operand layout of the
 // 16x16x32 MFMA: A[i][k] in lane i + 16*(k/8) element k%8, B[k][j] in lane
@@ -44,8 +45,9 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The tile a workgroup row (blockIdx.y) covers: an expert of the MFMA list
-// and 16 of its rows, or 16 rows of the shared expert.
+// The tile a unit covers: an expert of the MFMA list and TR of its rows, or
+// TR rows of the shared expert.  TR selects the tile prefix: kMfmaTileRows
+// (down) at mfma_tiles[0 ..], kMfmaGuTileRows (gate/up) at mfma_tiles[E+1 ..].
 struct MTile {
     ExpertSet X;           // the expert family (a copy: no pointer into the kernel arguments)
     int e, row0, n;           // expert, first row within the expert, rows in the tile
@@ -54,16 +56,19 @@ struct MTile {
     bool valid;
 };
 
+template <int TR>
 __device__ __forceinline__ MTile resolve_mtile(const FfnArgs &a, int t) {
+    static_assert(TR == kMfmaTileRows || TR == kMfmaGuTileRows, "a planned tile height");
     MTile m{a.routed, 0, 0, 0, nullptr, 0, false};
     const int nk = a.R * a.k;
-    const int n_routed = a.meta[kMetaMfmaTiles];
+    const int n_routed = a.meta[TR == kMfmaTileRows ? kMetaMfmaTiles : kMetaMfmaGuTiles];
+    const int32_t *prefix = TR == kMfmaTileRows ? a.mfma_tiles : a.mfma_tiles + a.E + 1;
     if (t < n_routed) {
         // the expert whose tile range holds t (prefix over the MFMA list)
         int lo = 0, hi = a.meta[kMetaMfmaCount] - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (a.mfma_tiles[mid] <= t) lo = mid;
+            if (prefix[mid] <= t) lo = mid;
             else hi = mid - 1;
         }
         const int e = a.mfma_list[lo];
@@ -71,18 +76,18 @@ __device__ __forceinline__ MTile resolve_mtile(const FfnArgs &a, int t) {
         const int cnt = a.counts[e], off = a.offsets[e];
         if (cnt < 0 || off < 0 || off + cnt > nk) return m;
         m.e = e;
-        m.row0 = (t - a.mfma_tiles[lo]) * kTileRows;
-        m.n = min(kTileRows, cnt - m.row0);
+        m.row0 = (t - prefix[lo]) * TR;
+        m.n = min(TR, cnt - m.row0);
         m.list = a.perm + off + m.row0;
         m.valid = m.n > 0;
         return m;
     }
     if (!a.shared_mfma) return m;
     const int ts = t - n_routed;
-    if (ts * kTileRows >= a.R) return m;
+    if (ts * TR >= a.R) return m;
     m.X = a.shared;
-    m.row0 = ts * kTileRows;
-    m.n = min(kTileRows, a.R - m.row0);
+    m.row0 = ts * TR;
+    m.n = min(TR, a.R - m.row0);
     m.first = nk + m.row0;
     m.valid = true;
     return m;
@@ -129,51 +134,81 @@ __device__ __forceinline__ void gu_load(GuStage &s, const uint8_t *wg, const uin
     }
 }
 
-// acc += scale * (X_tile . W^T) over one K block, gate and up; the lane's
-// activation fragments (row col, k = c*64 + grp*16 .. +15) from the LDS tile.
+constexpr int kGuSub = kMfmaGuTileRows / 16;   // 16-row subtiles of a gate/up tile
+
+// acc[q] += scale * (X_q . W^T) over one K block, gate and up, for the
+// tile's first nsub 16-row subtiles q (nsub is the same for the whole
+// workgroup): the block's codes are converted once and multiplied into every
+// subtile.  The lane's activation fragments (row 16q + col, k = c*64 +
+// grp*16 .. +15) come from the LDS tile.  Per subtile the MFMA chain is the
+// one a lone 16-row tile takes, so a row's result does not depend on its
+// subtile.
 __device__ __forceinline__ void gu_step(const GuStage &s, const uint16_t (*xs)[kXRow], int col, int grp, float sg,
-                                        float su, f32x4 &accg, f32x4 &accu) {
-    f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
+                                        float su, int nsub, f32x4 (&accg)[kGuSub], f32x4 (&accu)[kGuSub]) {
+    f32x4 tg[kGuSub], tu[kGuSub];
+#pragma unroll
+    for (int q = 0; q < kGuSub; ++q) tg[q] = tu[q] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        const u32x4 *xp = reinterpret_cast<const u32x4 *>(&xs[col][c * 64 + grp * 16]);
-        const bf16x8 x0 = as_bf16x8(xp[0]), x1 = as_bf16x8(xp[1]);
-        tg = mfma(x0, e4m3x8_bf16(s.g[c].x, s.g[c].y), tg);
-        tg = mfma(x1, e4m3x8_bf16(s.g[c].z, s.g[c].w), tg);
-        tu = mfma(x0, e4m3x8_bf16(s.u[c].x, s.u[c].y), tu);
-        tu = mfma(x1, e4m3x8_bf16(s.u[c].z, s.u[c].w), tu);
+        const bf16x8 g0 = e4m3x8_bf16(s.g[c].x, s.g[c].y), g1 = e4m3x8_bf16(s.g[c].z, s.g[c].w);
+        const bf16x8 u0 = e4m3x8_bf16(s.u[c].x, s.u[c].y), u1 = e4m3x8_bf16(s.u[c].z, s.u[c].w);
+#pragma unroll
+        for (int q = 0; q < kGuSub; ++q) {
+            if (q < nsub) {
+                const u32x4 *xp = reinterpret_cast<const u32x4 *>(&xs[q * 16 + col][c * 64 + grp * 16]);
+                const bf16x8 x0 = as_bf16x8(xp[0]), x1 = as_bf16x8(xp[1]);
+                tg[q] = mfma(x0, g0, tg[q]);
+                tg[q] = mfma(x1, g1, tg[q]);
+                tu[q] = mfma(x0, u0, tu[q]);
+                tu[q] = mfma(x1, u1, tu[q]);
+            }
+        }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        accg[i] = fmaf(sg, tg[i], accg[i]);
-        accu[i] = fmaf(su, tu[i], accu[i]);
+    for (int q = 0; q < kGuSub; ++q) {
+        if (q < nsub) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                accg[q][i] = fmaf(sg, tg[q][i], accg[q][i]);
+                accu[q][i] = fmaf(su, tu[q][i], accu[q][i]);
+            }
+        }
     }
 }
 
-// h = silu(X_tile . Wg^T) * (X_tile . Wu^T) for a 16-row tile and 16 gate
-// columns (+ the 16 matching up columns) per wave, all of K; two K blocks of
-// weight loads in flight, the next K block of activations staged while one
-// is multiplied.
+// h = silu(X_tile . Wg^T) * (X_tile . Wu^T) for a tile of up to 64 rows and
+// 16 gate columns (+ the 16 matching up columns) per wave, all of K; two K
+// blocks of weight loads in flight, the next K block of activations staged
+// while one is multiplied.  The weights are read once per 64 rows: an
+// expert's gate/up matrix is the bulk of what a unit loads.
 __device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int tile) {
-    __shared__ uint16_t xs[2][kTileRows][kXRow];
+    __shared__ uint16_t xs[2][kMfmaGuTileRows][kXRow];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-    const MTile t = resolve_mtile(a, tile);
+    const MTile t = resolve_mtile<kMfmaGuTileRows>(a, tile);
     if (!t.valid) return;
     const ExpertSet &X = t.X;
     const int I = X.inter, H = a.H, nk = a.R * a.k;
     // I is a multiple of 128, so a workgroup's 64 columns are all in range or
     // all past it: the exit is uniform (the waves share the barriers below)
     if (bx * kMfmaWaves * 16 >= I) return;
+    const int nsub = (t.n + 15) >> 4;   // 1 .. kGuSub
     const int n0 = (bx * kMfmaWaves + wid) * 16;
     const int col = lane & 15, grp = lane >> 4;
     const int nkb = H >> 7;
-    // this thread's staging piece: 16 bytes (8 values) of tile row threadIdx/16
+    // this thread's staging pieces: 16 bytes (8 values) of tile rows
+    // threadIdx/16 + 16q; rows without an entry stage row 0 (results dropped)
     const int srow = threadIdx.x >> 4, spiece = threadIdx.x & 15;
-    const int sent = mtile_entry(t, srow, nk);   // rows without an entry stage row 0 (results dropped)
-    const uint16_t *sx = a.x + (size_t)(sent >= 0 ? (sent < nk ? sent / a.k : sent - nk) : 0) * a.ldx + spiece * 8;
-    int oent[4];   // entries of the output rows this lane holds (D layout), loaded early
+    const uint16_t *sx0 = a.x + spiece * 8;
+    int srx[kGuSub];   // activation row of each staged tile row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) oent[i] = mtile_entry(t, 4 * grp + i, nk);
+    for (int q = 0; q < kGuSub; ++q) {
+        srx[q] = 0;
+        if (q < nsub) {
+            const int sent = mtile_entry(t, srow + 16 * q, nk);
+            srx[q] = sent >= 0 ? (sent < nk ? sent / a.k : sent - nk) : 0;
+        }
+    }
+    auto xrow = [&](int q) { return sx0 + (size_t)srx[q] * a.ldx; };
     const uint8_t *wg = X.gu + (size_t)t.e * X.gu_stride + (size_t)(n0 + col) * H;
     const uint8_t *wu = X.gu + (size_t)t.e * X.gu_stride + (size_t)(I + n0 + col) * H;
     // the K block's scales, lane j holding block j (H <= 8192: at most 64)
@@ -181,19 +216,28 @@ __device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int 
     const float sgl = lane < nkb ? sbase[(size_t)(n0 >> 7) * nkb + lane] : 0.0f;
     const float sul = lane < nkb ? sbase[(size_t)((I + n0) >> 7) * nkb + lane] : 0.0f;
 
-    f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+    f32x4 accg[kGuSub], accu[kGuSub];
+#pragma unroll
+    for (int q = 0; q < kGuSub; ++q) accg[q] = accu[q] = f32x4{0, 0, 0, 0};
     GuStage s0, s1;
     gu_load(s0, wg, wu, 0, grp);
     if (nkb > 1) gu_load(s1, wg, wu, 1, grp);
-    *reinterpret_cast<u32x4 *>(&xs[0][srow][spiece * 8]) = ld16(sx);
+#pragma unroll
+    for (int q = 0; q < kGuSub; ++q)
+        if (q < nsub) *reinterpret_cast<u32x4 *>(&xs[0][srow + 16 * q][spiece * 8]) = ld16(xrow(q));
     __syncthreads();
     // one K block: the next block's activations loaded, this block multiplied
     // from LDS, the next block stored into the other buffer, a barrier
     auto step = [&](int kb, const GuStage &s) {
-        u32x4 xn = {0u, 0u, 0u, 0u};
-        if (kb + 1 < nkb) xn = ld16(sx + (kb + 1) * 128);
-        gu_step(s, xs[kb & 1], col, grp, readlane(sgl, kb), readlane(sul, kb), accg, accu);
-        if (kb + 1 < nkb) *reinterpret_cast<u32x4 *>(&xs[(kb + 1) & 1][srow][spiece * 8]) = xn;
+        const bool more = kb + 1 < nkb;
+        u32x4 xn[kGuSub];
+#pragma unroll
+        for (int q = 0; q < kGuSub; ++q)
+            if (more && q < nsub) xn[q] = ld16(xrow(q) + (kb + 1) * 128);
+        gu_step(s, xs[kb & 1], col, grp, readlane(sgl, kb), readlane(sul, kb), nsub, accg, accu);
+#pragma unroll
+        for (int q = 0; q < kGuSub; ++q)
+            if (more && q < nsub) *reinterpret_cast<u32x4 *>(&xs[(kb + 1) & 1][srow + 16 * q][spiece * 8]) = xn[q];
         __syncthreads();
     };
     for (int kb = 0; kb < nkb; kb += 2) {
@@ -204,11 +248,17 @@ __device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int 
             if (kb + 3 < nkb) gu_load(s1, wg, wu, kb + 3, grp);
         }
     }
-    // D[i][j]: lane holds column j = col, rows 4*grp .. 4*grp+3
+    // D[i][j]: lane holds column j = col, rows 16q + 4*grp .. +3
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = oent[i];
-        if (e >= 0) a.h[(size_t)e * a.hstride + n0 + col] = silu_mul(accg[i], accu[i]);
+    for (int q = 0; q < kGuSub; ++q) {
+        if (q < nsub) {
+            int oent[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oent[i] = mtile_entry(t, 16 * q + 4 * grp + i, nk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (oent[i] >= 0) a.h[(size_t)oent[i] * a.hstride + n0 + col] = silu_mul(accg[q][i], accu[q][i]);
+        }
     }
 }
 
@@ -275,7 +325,7 @@ __device__ __forceinline__ void dn_step(const DnStage &s, const float (*hs)[kHRo
 __device__ __forceinline__ void mfma_down_unit(const FfnArgs &a, int bx, int tile) {
     __shared__ float hs[2][kTileRows][kHRow];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-    const MTile t = resolve_mtile(a, tile);
+    const MTile t = resolve_mtile<kMfmaTileRows>(a, tile);
     if (!t.valid) return;
     const ExpertSet &X = t.X;
     const int I = X.inter, H = a.H, nk = a.R * a.k;

@@ -117,27 +117,39 @@ __device__ int block_excl_scan(int v, int *wave_tot, int *total) {
 }
 
 // Splits the touched experts into the GEMV-arm list and the MFMA-arm list
-// (rows >= threshold), both ascending, and the MFMA row-tile prefix.  Thread
-// e of a 1024-thread block holds expert e's row count c.
+// (rows >= threshold), both ascending, and the MFMA row-tile prefixes: of
+// kMfmaTileRows-row tiles at mfma_tiles[0 .. n], of kMfmaGuTileRows-row
+// tiles at mfma_tiles[E+1 .. E+1+n].  Thread e of a 1024-thread block holds
+// expert e's row count c.
 __device__ void plan_lists(const RouteArgs &a, int e, int c, int *wave_tot) {
     const int E = a.E;
     const bool mf = e < E && c > 0 && a.mfma_min_rows > 0 && c >= a.mfma_min_rows;
     const bool gv = e < E && c > 0 && !mf;
-    int n_gemv, n_mfma, n_tiles;
+    int n_gemv, n_mfma, n_tiles, n_gu_tiles;
     const int pg = block_excl_scan(gv ? 1 : 0, wave_tot, &n_gemv);
     const int pm = block_excl_scan(mf ? 1 : 0, wave_tot, &n_mfma);
     const int tiles = mf ? (c + kMfmaTileRows - 1) / kMfmaTileRows : 0;
-    const int pt = block_excl_scan(tiles, wave_tot, &n_tiles);
+    const int gu_tiles = mf ? (c + kMfmaGuTileRows - 1) / kMfmaGuTileRows : 0;
+    // both tile counts in one scan: the down tiles in the low 16 bits (their
+    // total is at most R*k/16 + E < 2^16), the gate/up tiles above
+    const int packed = block_excl_scan(tiles | (gu_tiles << 16), wave_tot, &n_tiles);
+    const int pt = packed & 0xFFFF, pgt = packed >> 16;
+    n_gu_tiles = n_tiles >> 16;
+    n_tiles &= 0xFFFF;
+    int32_t *gu_prefix = a.mfma_tiles + E + 1;
     if (gv) a.gemv_list[pg] = e;
     if (mf) {
         a.mfma_list[pm] = e;
         a.mfma_tiles[pm] = pt;
+        gu_prefix[pm] = pgt;
     }
     if (threadIdx.x == 0) {
         a.meta[kMetaGemvCount] = n_gemv;
         a.meta[kMetaMfmaCount] = n_mfma;
         a.meta[kMetaMfmaTiles] = n_tiles;
+        a.meta[kMetaMfmaGuTiles] = n_gu_tiles;
         a.mfma_tiles[n_mfma] = n_tiles;
+        gu_prefix[n_mfma] = n_gu_tiles;
     }
 }
 
