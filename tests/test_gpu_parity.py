@@ -251,6 +251,57 @@ def test_mfma_arm_forced_for_every_expert(moe, ctx, orc, rows):
         moe.moe_ctx_set_force_arm(ctx, 0)
 
 
+def _logits_with_counts(E, k, R, counts, seed):
+    """Given router logits under which expert e (a key of `counts`) is chosen
+    by exactly counts[e] rows: each listed expert takes the rows with the
+    fewest choices so far, every row is then filled to k distinct experts
+    from the unlisted ones in turn (1-3 rows each), and a row's chosen
+    experts get distinct logits well above all others (tie-free)."""
+    rng = np.random.default_rng(seed)
+    chosen = [[] for _ in range(R)]
+    for e, c in counts.items():
+        load = np.array([len(ch) for ch in chosen])
+        for r in np.argsort(load, kind="stable")[:c]:
+            chosen[r].append(e)
+    fill = [e for e in range(E) if e not in counts]
+    nxt = 0
+    for r in range(R):
+        assert len(chosen[r]) <= k
+        while len(chosen[r]) < k:
+            e = fill[nxt % len(fill)]
+            nxt += 1
+            if e not in chosen[r]:
+                chosen[r].append(e)
+    li = rng.normal(0.0, 1.0, size=(R, E)).astype(np.float32)
+    for r in range(R):
+        top = 10.0 + rng.permutation(k).astype(np.float32) * 0.37 + rng.uniform(0, 0.1, k).astype(np.float32)
+        li[r, chosen[r]] = top
+    return li
+
+
+@pytest.mark.parametrize("rows,counts", [
+    (160, {3: 4, 7: 16, 9: 17, 11: 31, 12: 32, 13: 33, 20: 48, 21: 63, 22: 64, 23: 65, 30: 100, 31: 129,
+           40: 160}),
+    (512, {0: 512, 1: 300, 2: 257, 3: 129, 4: 64, 5: 63, 6: 16, 7: 4}),
+])
+def test_mfma_tile_shapes(moe, ctx, orc, rows, counts):
+    """Experts whose row counts give gate/up tiles of 1 to 4 16-row subtiles
+    (ragged last subtiles, several tiles per expert, an expert on every row)
+    and down tiles with ragged tails, against the oracle."""
+    wl = syn.WORKLOADS["a3b_multi"]
+    W = syn.make_layer_weights(wl, 6, "cuda")
+    x = syn.make_x(wl, 6, rows, 0, "cuda")
+    li = torch.from_numpy(_logits_with_counts(wl.n_experts, wl.top_k, rows, counts, 60 + rows)).cuda()
+    _say(f"{wl.name}: given counts, rows {rows}")
+    y, res, rt, res0 = _run(moe, ctx, wl, W, x, li, layer=6)
+    assert moe.moe_ctx_status(ctx) == 0 and moe.moe_ctx_device_errors(ctx) == 0
+    got = rt.expert_count.cpu().numpy()
+    for e, c in counts.items():
+        assert got[e] == c, (e, got[e], c)
+    sample = None if rows <= 160 else list(range(0, rows, 37)) + [rows - 1]
+    check_layer(orc, wl, W, x, li, res0, y, res, rt, rows=sample, what=f"counts R{rows}")
+
+
 def test_gemv_arm_only_at_64_rows(moe, ctx, orc):
     moe.moe_ctx_set_force_arm(ctx, 1)
     try:
