@@ -252,14 +252,29 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     __syncthreads();
     const float *hbase = reinterpret_cast<const float *>(hlds4);
     float y = 0.0f;
+    if (has_shared && k == KS - 1) {
+        // every slot present (the instantiated shape): no per-slot branches,
+        // so the slots' LDS reads and lane reductions overlap; the same dots
+        // and the same blend order as below
+        float d[KS];
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-        if (j < nslots) {
-            const bool sh = j == k;
-            const ExpertSet &X = sh ? a.shared : a.routed;
-            float d = rows[j].dot_perm(hbase + (size_t)j * HS, X.inter, sub);
-            d *= global_scale<FMT>(X.dn_g, sh ? 0 : ids_s[j]);
-            y = fmaf(sh ? s_gate : w_s[j], d, y);
+        for (int j = 0; j < KS; ++j) {
+            const ExpertSet &X = j == KS - 1 ? a.shared : a.routed;
+            d[j] = rows[j].dot_perm(hbase + (size_t)j * HS, X.inter, sub);
+            d[j] *= global_scale<FMT>(X.dn_g, j == KS - 1 ? 0 : ids_s[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < KS; ++j) y = fmaf(j == KS - 1 ? s_gate : w_s[j], d[j], y);
+    } else {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            if (j < nslots) {
+                const bool sh = j == k;
+                const ExpertSet &X = sh ? a.shared : a.routed;
+                float d = rows[j].dot_perm(hbase + (size_t)j * HS, X.inter, sub);
+                d *= global_scale<FMT>(X.dn_g, sh ? 0 : ids_s[j]);
+                y = fmaf(sh ? s_gate : w_s[j], d, y);
+            }
         }
     }
     if (live && sub == 0) {
