@@ -134,15 +134,23 @@ __device__ __forceinline__ void gate_up_gemv_unit(const FfnArgs &a, int bx, int 
     const int i0 = (bx * 4 + wid) * PM;
     if (i0 >= X.inter) return;
     using Rows = GateUpRows<FMT, CH, PM>;
+    const int nk = a.R * a.k;
+    // the first entry's activation loads go out before the weight loads
+    // (which are converted as they arrive, so waited for at once): the
+    // activations then travel with the weights instead of after them
+    int mine = lane < min(kWave, t.n) ? task_entry(t, lane, nk) : -1;
+    int ec = readlane(mine, 0);
+    u32x4 xc[CH][XQ], xn[CH][XQ];
+    if (ec >= 0) Rows::load_x(a.x + (size_t)entry_row(a, ec) * a.ldx, a.H, xc);
     Rows rows;
     rows.load(X, t.e, i0, a.H);
-    const int nk = a.R * a.k;
-    u32x4 xc[CH][XQ], xn[CH][XQ];
     for (int n0 = 0; n0 < t.n; n0 += kWave) {
         const int cnt = min(kWave, t.n - n0);
-        const int mine = lane < cnt ? task_entry(t, n0 + lane, nk) : -1;
-        int ec = readlane(mine, 0);
-        if (ec >= 0) Rows::load_x(a.x + (size_t)entry_row(a, ec) * a.ldx, a.H, xc);
+        if (n0 > 0) {
+            mine = lane < cnt ? task_entry(t, n0 + lane, nk) : -1;
+            ec = readlane(mine, 0);
+            if (ec >= 0) Rows::load_x(a.x + (size_t)entry_row(a, ec) * a.ldx, a.H, xc);
+        }
         for (int j = 0; j < cnt; ++j) {
             const int en = j + 1 < cnt ? readlane(mine, j + 1) : -1;
             if (en >= 0) Rows::load_x(a.x + (size_t)entry_row(a, en) * a.ldx, a.H, xn);
@@ -394,19 +402,25 @@ __device__ __forceinline__ void down_gemv_unit(const FfnArgs &a, int bx, int tas
     const int sub = lane % LPR;
     const int o0 = wave_row0 + (lane / LPR) * RPL;
     using Row = DownRow<FMT, LPR, CH>;
+    const int nk = a.R * a.k;
+    // the first entry's h loads before the weight loads (as in the gate/up unit)
+    int mine = lane < min(kWave, t.n) ? task_entry(t, lane, nk) : -1;
+    int ec = readlane(mine, 0);
+    f32x4 hc[CH][HQ], hn[CH][HQ];
+    if (ec >= 0) Row::load_h(a.h + (size_t)ec * a.hstride, X.inter, sub, hc);
     Row rows[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) rows[i].template load<true>(X, t.e, o0 + i, sub, o0 + i < a.H);
     const float g = global_scale<FMT>(X.dn_g, t.e);
     const int orow = o0 + sub / SPAN;
     const bool writer = sub % SPAN == 0 && orow < a.H;
-    const int nk = a.R * a.k;
-    f32x4 hc[CH][HQ], hn[CH][HQ];
     for (int n0 = 0; n0 < t.n; n0 += kWave) {
         const int cnt = min(kWave, t.n - n0);
-        const int mine = lane < cnt ? task_entry(t, n0 + lane, nk) : -1;
-        int ec = readlane(mine, 0);
-        if (ec >= 0) Row::load_h(a.h + (size_t)ec * a.hstride, X.inter, sub, hc);
+        if (n0 > 0) {
+            mine = lane < cnt ? task_entry(t, n0 + lane, nk) : -1;
+            ec = readlane(mine, 0);
+            if (ec >= 0) Row::load_h(a.h + (size_t)ec * a.hstride, X.inter, sub, hc);
+        }
         for (int j = 0; j < cnt; ++j) {
             const int en = j + 1 < cnt ? readlane(mine, j + 1) : -1;
             if (en >= 0) Row::load_h(a.h + (size_t)en * a.hstride, X.inter, sub, hn);
