@@ -313,15 +313,17 @@ __global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
 // experts' loads in flight), stages the row's h in LDS (HLDS), then for each
 // slot in order reduces d_j and accumulates y = fma(w_j, d_j, y), then
 // fma(s, d_shared, y), and adds into the residual.  Slot j's h is row r*k + j,
-// the shared expert's row R*k + r.
+// the shared expert's row R*k + r.  kDownR1Waves waves a workgroup: the
+// row's h is staged once for that many waves' output elements.
+constexpr int kDownR1Waves = 8;
 template <int FMT, int LPR, int CH, bool HLDS>
-__global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
+__global__ __launch_bounds__(kDownR1Waves * kWave) void k_down_r1(FfnArgs a) {
     extern __shared__ f32x4 hlds4[];
     constexpr int RPW = kWave / LPR;
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
     const int r = blockIdx.y;
     const int sub = lane % LPR;
-    const int o = (blockIdx.x * 4 + wid) * RPW + lane / LPR;
+    const int o = (blockIdx.x * kDownR1Waves + wid) * RPW + lane / LPR;
     const bool live = o < a.H;
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
     auto hrow = [&](int j) { return j == a.k ? (size_t)a.R * a.k + r : (size_t)r * a.k + j; };
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256) void k_down_r1(FfnArgs a) {
         constexpr int CPC = cols_per_chunk<FMT>();
         const int n4 = a.hstride / 4;
         const f32x4 *src = reinterpret_cast<const f32x4 *>(a.h);
-        for (int i = threadIdx.x; i < nslots * n4; i += 256) {
+        for (int i = threadIdx.x; i < nslots * n4; i += kDownR1Waves * kWave) {
             const int j = i / n4, q4 = i - j * n4;
             if (!PERM) {
                 hlds4[i] = src[hrow(j) * n4 + q4];
@@ -735,7 +737,9 @@ static hipError_t down_r1_fmt(const FfnArgs &a, hipStream_t st) {
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
     const size_t hbytes = (size_t)nslots * a.hstride * 4;
     MOE_DOWN_DISPATCH({
-        dim3 grid((a.H + rows_per_block - 1) / rows_per_block, a.R), block(256);
+        const int rpb = kDownR1Waves * (kWave / LPR);
+        dim3 grid((a.H + rpb - 1) / rpb, a.R), block(kDownR1Waves * kWave);
+        (void)rows_per_block;
         if (hbytes <= kMaxHLds)
             hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, true>), grid, block, hbytes, st, a);
         else
