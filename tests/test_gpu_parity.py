@@ -198,6 +198,39 @@ def test_top_k_extremes(moe, ctx, orc, k):
         assert torch.all(rt.topk_w == 1.0)
 
 
+ODD_SHAPES = {
+    # hidden 3 K blocks, 100 experts (not a multiple of the wave), shared
+    # intermediate half the routed one
+    "h384_e100": dict(hidden=384, n_experts=100, top_k=6, inter=256, shared_inter=128),
+    # hidden 9 K blocks (odd), 200 experts, shared intermediate three times the
+    # routed one (3 K blocks in its down projection)
+    "h1152_e200": dict(hidden=1152, n_experts=200, top_k=3, inter=128, shared_inter=384),
+}
+
+
+@pytest.mark.parametrize("shape", list(ODD_SHAPES))
+@pytest.mark.parametrize("rows", [1, 5, 40])
+def test_odd_shapes(moe, ctx, orc, shape, rows):
+    """Shapes away from the models': expert counts that do not fill the top-k
+    lanes, shared and routed intermediates that differ, odd K-block counts;
+    one row (three-launch path), a few rows and a matrix-core step."""
+    import dataclasses
+    wl = dataclasses.replace(syn.WORKLOADS["tiny"], name=f"odd_{shape}", **ODD_SHAPES[shape])
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    li = None
+    if rows <= 8:
+        x, _ = tie_free_x(orc, wl, W, 0, rows, device="cuda")
+    else:
+        # many rows of 100+ experts: given logits (compared as the same f32
+        # values on both sides), the router GEMV skipped
+        x = syn.make_x(wl, 0, rows, 0, "cuda")
+        li = syn.make_logits_in(dataclasses.replace(wl, router="uniform"), 0, rows, "cuda")
+    _say(f"{wl.name}: rows {rows}")
+    y, res, rt, res0 = _run(moe, ctx, wl, W, x, li)
+    assert moe.moe_ctx_status(ctx) == 0 and moe.moe_ctx_device_errors(ctx) == 0
+    check_layer(orc, wl, W, x, li, res0, y, res, rt, what=f"{shape} R{rows}")
+
+
 def test_padded_leading_dimensions(moe, ctx, orc):
     from routed_fp8_expert_amd.workload import layer_weights
     wl = syn.WORKLOADS["tiny"]
