@@ -208,14 +208,18 @@ ODD_SHAPES = {
 }
 
 
-@pytest.mark.parametrize("shape", list(ODD_SHAPES))
+ODD_CASES = [(shape, 0) for shape in ODD_SHAPES] + [("h384_e100", f) for f in (1, 2, 3, 4, 5)]
+
+
+@pytest.mark.parametrize("shape,fmt", ODD_CASES)
 @pytest.mark.parametrize("rows", [1, 5, 40])
-def test_odd_shapes(moe, ctx, orc, shape, rows):
+def test_odd_shapes(moe, ctx, orc, shape, fmt, rows):
     """Shapes away from the models': expert counts that do not fill the top-k
     lanes, shared and routed intermediates that differ, odd K-block counts;
-    one row (three-launch path), a few rows and a matrix-core step."""
+    one row (three-launch path), a few rows and a matrix-core step (fp8), in
+    every weight format."""
     import dataclasses
-    wl = dataclasses.replace(syn.WORKLOADS["tiny"], name=f"odd_{shape}", **ODD_SHAPES[shape])
+    wl = dataclasses.replace(syn.WORKLOADS["tiny"], name=f"odd_{shape}", fmt=fmt, **ODD_SHAPES[shape])
     W = syn.make_layer_weights(wl, 0, "cuda")
     li = None
     if rows <= 8:
@@ -228,7 +232,7 @@ def test_odd_shapes(moe, ctx, orc, shape, rows):
     _say(f"{wl.name}: rows {rows}")
     y, res, rt, res0 = _run(moe, ctx, wl, W, x, li)
     assert moe.moe_ctx_status(ctx) == 0 and moe.moe_ctx_device_errors(ctx) == 0
-    check_layer(orc, wl, W, x, li, res0, y, res, rt, what=f"{shape} R{rows}")
+    check_layer(orc, wl, W, x, li, res0, y, res, rt, what=f"{shape} fmt {fmt} R{rows}")
 
 
 def test_padded_leading_dimensions(moe, ctx, orc):
