@@ -228,7 +228,7 @@ def run_dense(args):
         "config": {"workload": f"dense {name}: y[{rows},{n}] = x[{rows},{k}] . W^T, fp8 e4m3 block-128 weights, "
                                f"{copies} resident copies in turn",
                    "rows": rows, "copies": copies,
-                   "arm": "matrix cores" if rows >= 32 else "gemv"},
+                   "arm": "matrix cores" if rows >= 8 else "gemv"},
         "kernels": {"dense": {"avg_us": round(kms / max(kn, 1) * 1e3, 3), "launches_per_step": kn // kt_steps}},
         "roofline": {"bound": "hbm", "kernel": "dense", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

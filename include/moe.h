@@ -175,8 +175,8 @@ MOE_API int moe_ctx_status(const moe_ctx *ctx);
  * the ctx becomes lost and the call returns MOE_ERR_DEVICE_LOST.  n <= 0
  * disables it. */
 MOE_API int moe_ctx_set_fault_at(moe_ctx *ctx, int64_t n);
-/* Rows per expert at and above which (with a step of at least 32 rows) an
- * expert of an fp8 layer takes the MFMA grouped-GEMM arm (default 4); 0
+/* Rows per expert at and above which (in a grouped step of at least 9 rows)
+ * an expert of an fp8 layer takes the MFMA grouped-GEMM arm (default 4); 0
  * restores the default.  The shared expert takes it when the step has that
  * many rows.  NVFP4 layers always use the GEMV arm. */
 MOE_API int moe_ctx_set_mfma_min_rows(moe_ctx *ctx, int rows);

@@ -31,6 +31,12 @@ constexpr int kFewRowsAuto = -1;         // ctx default: kDefaultFewRows where t
 constexpr size_t kFewRowsHBytes = 32 * 1024;
 constexpr int kFusedTopkRows = 4;        // few-rows steps up to 4 rows select in the gate/up blocks (measured)
 constexpr int kDefaultMfmaMinRows = 4;   // rows per expert from which the MFMA arm pays (measured)
+// Step rows from which the MFMA arm runs: where the few-rows path ends (up to
+// 8 rows by default; the grouped path below keeps GEMV-only bits there).
+// Measured against 32: 12 rows 84.1 -> 67.2 us, 16 rows 102.0 -> 78.5, 24
+// rows 135.7 -> 98.2 (the shared expert's rows leave one long GEMV task); at
+// 4 rows it was slower.
+constexpr int kMfmaStepRows = 9;
 constexpr int kMaxRows = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
@@ -281,12 +287,12 @@ int check_ws(const moe_layer_weights *w, int R, const void *ws, size_t ws_bytes)
     return MOE_OK;
 }
 
-// The MFMA arm serves fp8 layers in steps of at least 32 rows (any multi-row
-// step when forced), for experts with at least the threshold's rows.
+// The MFMA arm serves fp8 layers in steps of at least kMfmaStepRows rows (any
+// multi-row step when forced), for experts with at least the threshold's rows.
 bool mfma_enabled(const moe_ctx *c, const moe_layer_weights *w, int R) {
     if (w->weight_format != MOE_WFMT_FP8_E4M3_B128 || c->force_arm == 1) return false;
     if (c->force_arm == 2) return R >= 2;
-    return R >= 32 && c->mfma_min_rows > 0;
+    return R >= kMfmaStepRows && c->mfma_min_rows > 0;
 }
 int mfma_threshold(const moe_ctx *c, const moe_layer_weights *w, int R) {
     if (!mfma_enabled(c, w, R)) return 0;
