@@ -63,9 +63,11 @@ def _check(orc, q, s, x, y, sel):
 
 
 CASES = [
-    ("small_384x640", r) for r in (1, 3, 7, 8, 17, 33, 64, 128)
+    # 129 and 300 rows: the matrix-core arm's second and third 128-row chunk,
+    # the last one ragged
+    ("small_384x640", r) for r in (1, 3, 7, 8, 17, 33, 64, 128, 129, 300)
 ] + [
-    ("up_4096x2048", r) for r in (1, 5, 7, 8, 31, 64, 128)
+    ("up_4096x2048", r) for r in (1, 5, 7, 8, 31, 64, 128, 200)
 ] + [
     ("down_2048x4096", r) for r in (1, 7, 8, 32, 128)
 ] + [
