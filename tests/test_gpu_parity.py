@@ -111,7 +111,9 @@ def test_a3b_one_row(moe, ctx, orc, layer):
     _layer(moe, ctx, orc, syn.WORKLOADS["a3b"], layer, 1)
 
 
-@pytest.mark.parametrize("rows", [2, 4, 8, 16, 32, 64])
+# 9 rows: the first grouped step with the matrix-core arm (8 and fewer take
+# the few-rows path)
+@pytest.mark.parametrize("rows", [2, 4, 8, 9, 12, 16, 32, 64])
 def test_a3b_multi_row(moe, ctx, orc, rows):
     wl = syn.WORKLOADS["a3b_multi"]
     for layer in (0, 1):
