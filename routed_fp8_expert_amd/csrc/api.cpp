@@ -22,7 +22,7 @@ namespace {
 
 // ctx words: the router ticket, the error word and the warming sink on their
 // own lines, then the single-launch layer's synchronisation lines.
-enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, kWordLayerSync = 1024,
+enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, kWordGroupTicket = 192, kWordLayerSync = 1024,
                       kSyncWords = 1024 + 40 * 64 };
 constexpr int kDenseMaxK = 8192;         // a wave's 64 lanes hold one scale per 128-wide block
 constexpr int kDenseMaxRows = 1 << 20;   // matrix-core grid rows stay far below 65535
@@ -326,6 +326,7 @@ moe::RouteArgs route_args(moe_ctx *c, const moe_layer_weights *w, const void *x,
     a.mfma_min_rows = mfma_threshold(c, w, R);
     a.err = c->words + kWordError;
     a.ticket = c->words + kWordRouterTicket;
+    a.group_ticket = c->words + kWordGroupTicket;
     return a;
 }
 
@@ -334,17 +335,11 @@ int do_route(moe_ctx *c, const moe::RouteArgs &a, bool plan, hipStream_t st) {
     if (!a.logits_in) {
         rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_router(a, st); });
         if (rc) return rc;
-        rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, false, st); });
-        if (rc) return rc;
-    } else {
-        rc = launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, true, st); });
-        if (rc) return rc;
     }
-    if (a.R >= 2) {
-        rc = launch(c, MOE_K_GROUP, st, [&] { return moe::launch_group(a, plan, st); });
-        if (rc) return rc;
-    }
-    return MOE_OK;
+    const bool compute_s = a.logits_in != nullptr;   // else the router launch made it
+    // a multi-row step's top-k and grouping share one launch
+    if (a.R >= 2) return launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk_group(a, compute_s, plan, st); });
+    return launch(c, MOE_K_TOPK, st, [&] { return moe::launch_topk(a, compute_s, st); });
 }
 
 moe::ExpertSet expert_set(const moe_expert_weights &f, int inter) {

@@ -48,6 +48,7 @@ struct RouteArgs {
     int mfma_min_rows;          // experts with count >= this go to the MFMA arm (0 = never)
     uint32_t *err;
     unsigned *ticket;           // ctx word: router workgroups done (one-row lead kernel)
+    unsigned *group_ticket;     // ctx word: top-k workgroups done (fused top-k + grouping)
 };
 
 struct FfnArgs {
@@ -93,6 +94,7 @@ struct DenseArgs {
 hipError_t launch_router(const RouteArgs &a, hipStream_t st);
 hipError_t launch_topk(const RouteArgs &a, bool compute_s, hipStream_t st);
 hipError_t launch_group(const RouteArgs &a, bool plan, hipStream_t st);
+hipError_t launch_topk_group(const RouteArgs &a, bool compute_s, bool plan, hipStream_t st);
 hipError_t launch_plan(const RouteArgs &a, hipStream_t st);
 size_t group_lds_bytes(int E, int R);
 

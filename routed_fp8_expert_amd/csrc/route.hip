@@ -171,18 +171,18 @@ __global__ __launch_bounds__(1024) void k_plan(RouteArgs a) {
 // Grouping by expert: a bitmap of rows per expert (rows ascending), counts
 // by popcount, an exclusive scan for the offsets, and each (row, slot) placed
 // at offset + (rows before it that chose the same expert).  With `do_plan`
-// it also writes the arm lists.  One 1024-thread workgroup.
-__global__ __launch_bounds__(1024) void k_group(RouteArgs a, int do_plan) {
-    extern __shared__ uint32_t bm[];          // [E][W]
-    __shared__ int wave_tot[40];
-    __shared__ int soff[1024];
+// it also writes the arm lists.  One 1024-thread workgroup; COHERENT reads
+// the ids at agent scope (written by other workgroups of the same launch).
+template <bool COHERENT>
+__device__ void group_rows(const RouteArgs &a, int do_plan, uint32_t *bm, int *wave_tot, int *soff) {
     const int tid = threadIdx.x;
     const int R = a.R, E = a.E, k = a.k, W = (R + 31) >> 5;
     const int n = R * k;
+    auto id_at = [&](int i) { return COHERENT ? ld_agent(a.ids + i) : a.ids[i]; };
     for (int i = tid; i < E * W; i += 1024) bm[i] = 0u;
     __syncthreads();
     for (int i = tid; i < n; i += 1024) {
-        const int e = a.ids[i];
+        const int e = id_at(i);
         const int r = i / k;
         if (e >= 0 && e < E)
             atomicOr(&bm[e * W + (r >> 5)], 1u << (r & 31));
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(1024) void k_group(RouteArgs a, int do_plan) {
     if (do_plan) plan_lists(a, e, c, wave_tot);
     __syncthreads();
     for (int i = tid; i < n; i += 1024) {
-        const int ee = a.ids[i];
+        const int ee = id_at(i);
         if (ee < 0 || ee >= E) continue;
         const int r = i / k;
         const uint32_t *row = bm + ee * W;
@@ -213,6 +213,53 @@ __global__ __launch_bounds__(1024) void k_group(RouteArgs a, int do_plan) {
         for (int q = 0; q < (r >> 5); ++q) rank += __popc(row[q]);
         a.perm[soff[ee] + rank] = i;
     }
+}
+
+__global__ __launch_bounds__(1024) void k_group(RouteArgs a, int do_plan) {
+    extern __shared__ uint32_t bm[];          // [E][W]
+    __shared__ int wave_tot[40];
+    __shared__ int soff[1024];
+    group_rows<false>(a, do_plan, bm, wave_tot, soff);
+}
+
+// Top-k of a grouped step and its grouping in one launch: one wave a row, 16
+// rows a workgroup (ids and weights stored write-through), then each
+// workgroup counts itself done once its stores have completed, and the last
+// one to do so groups the step (reading the ids at agent scope) and resets
+// the count for the next call.  No workgroup waits on another.
+template <int NV>
+__global__ __launch_bounds__(1024) void k_topk_group(RouteArgs a, int s_mode, int do_plan) {
+    extern __shared__ uint32_t bm[];          // [E][W], the grouping's
+    __shared__ int wave_tot[40];
+    __shared__ int soff[1024];
+    __shared__ unsigned ticket_s;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = blockIdx.x * 16 + (threadIdx.x >> 6);
+    if (r < a.R) {
+        const float *l = a.logits_in ? a.logits_in + (size_t)r * a.E : a.logits + (size_t)r * a.E;
+        int e;
+        float w;
+        topk_wave<NV>(l, a.E, a.k, false, e, w);
+        if (lane < a.k) {
+            st_agent(a.ids + (size_t)r * a.k + lane, e);
+            st_agent(a.w + (size_t)r * a.k + lane, w);
+        }
+        if (s_mode == 1) {
+            // chunks in order, the wave sum last: the bits of the one-row router
+            const float d = dot_bf16_row_stream(a.wsg, a.x + (size_t)r * a.ldx, a.H);
+            if (lane == 0) a.s[r] = sigmoid(d);
+        } else if (s_mode == 2 && lane == 0) {
+            a.s[r] = 1.0f;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        ticket_s = __hip_atomic_fetch_add(a.group_ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket_s != gridDim.x - 1) return;
+    if (threadIdx.x == 0) __hip_atomic_store(a.group_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    group_rows<true>(a, do_plan, bm, wave_tot, soff);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -265,6 +312,20 @@ hipError_t launch_topk(const RouteArgs &a, bool compute_s, hipStream_t st) {
 
 hipError_t launch_group(const RouteArgs &a, bool plan, hipStream_t st) {
     hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), group_lds_bytes(a.E, a.R), st, a, (int)plan);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_group(const RouteArgs &a, bool compute_s, bool plan, hipStream_t st) {
+    const int s_mode = a.wsg ? (compute_s ? 1 : 0) : 2;
+    dim3 grid((a.R + 15) / 16), block(1024);
+    const size_t lds = group_lds_bytes(a.E, a.R);
+    switch (topk_nv(a.E)) {
+        case 1: hipLaunchKernelGGL(k_topk_group<1>, grid, block, lds, st, a, s_mode, (int)plan); break;
+        case 2: hipLaunchKernelGGL(k_topk_group<2>, grid, block, lds, st, a, s_mode, (int)plan); break;
+        case 4: hipLaunchKernelGGL(k_topk_group<4>, grid, block, lds, st, a, s_mode, (int)plan); break;
+        case 8: hipLaunchKernelGGL(k_topk_group<8>, grid, block, lds, st, a, s_mode, (int)plan); break;
+        default: hipLaunchKernelGGL(k_topk_group<16>, grid, block, lds, st, a, s_mode, (int)plan); break;
+    }
     return hipGetLastError();
 }
 
