@@ -16,7 +16,9 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["route.hip", "ffn.hip", "layer.hip", "dense.hip", "api.cpp"]
+# every .hip file of csrc/ (the expert kernels compile one weight format per
+# file, in parallel) and the C ABI
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")) + ["api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -48,7 +50,8 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(srcs)))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
     if verbose:
