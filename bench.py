@@ -94,49 +94,146 @@ def counter_traffic(kernel: str, workload: str, rows: int):
     return int(kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in kv else None
 
 
-def cpu_baseline(wl, res, budget_s: float):
+def cpu_threads():
+    """Threads the oracle may use: every CPU of this process's affinity mask,
+    capped by OMP_NUM_THREADS where the environment sets it (a shared GPU machine
+    grants each GPU a share of its CPUs that way)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_info() -> dict:
+    """Seed, sources and software versions of the run."""
+    import subprocess
+    import torch
+    import moe_synth as syn
+    rev = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        rev = r.stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"seed": syn.BASE_SEED, "git_revision": rev, "source_digest": source_digest(), "rocm": rocm,
+            "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "gpu": torch.cuda.get_device_name(0) if torch.cuda.is_available() else None}
+
+
+def verify_layer(moe, oracle, L, wl, res, ctx, stream, n, x, li, logits):
+    """Layer n once more on the GPU with y written (a fresh copy of its
+    residual; outside the timed region), checked against the oracle layer L:
+    ids bit-exact, weights within 1e-5, y within max|err| <= 2e-2 * rms(y)
+    and sum|err| / sum|y| <= 5e-3.  A layer whose oracle logits put two of the
+    k+1 largest within 1e-4 of each other (where a different summation order
+    may legitimately swap them) is reported as a near tie, not compared."""
+    import numpy as np
+    import torch
+    from oracle.layers import bits, min_top_gap
+    gap = min_top_gap(logits, wl.top_k)
+    if gap < 1e-4:
+        return {"layer": res.layer_ids[n], "near_tie": round(gap, 8)}
+    ref = oracle.layer_forward(L, x, logits_in=li, residual=bits(res.residual0[n]))
+    rows = res.rows
+    y = torch.empty((rows, wl.hidden), dtype=torch.bfloat16, device=res.device)
+    rt = moe.Routing(rows, wl.n_experts, wl.top_k, res.device)
+    resid = res.residual0[n].clone()
+    moe.moe_layer_forward(ctx, res.lw[n], res.x[n], y, resid, res.ws, logits_in=res.logits_in[n],
+                          routing=rt, stream=stream)
+    torch.cuda.synchronize()
+    ids_ok = bool(np.array_equal(rt.topk_ids.cpu().numpy(), ref["ids"]))
+    w_err = float(np.max(np.abs(rt.topk_w.cpu().numpy() - ref["w"])))
+    g = y.float().cpu().numpy().astype(np.float64)
+    o = ref["y"].astype(np.float64)
+    rms = float(np.sqrt(np.mean(o * o)))
+    err = np.abs(g - o)
+    max_rel = float(err.max() / max(rms, 1e-300))
+    mean_rel = float(err.sum() / max(np.abs(o).sum(), 1e-300))
+    ok = ids_ok and w_err <= 1e-5 and max_rel <= 2e-2 and mean_rel <= 5e-3 and bool(np.all(np.isfinite(g)))
+    return {"layer": res.layer_ids[n], "ok": ok, "ids_equal": ids_ok, "w_max_err": w_err,
+            "y_max_err_over_rms": max_rel, "y_mean_rel_err": mean_rel}
+
+
+def cpu_baseline(wl, res, budget_s: float, moe, ctx, stream):
     """The CPU oracle on the same layers (touched experts copied to the host
-    outside the timing), layer by layer until the time budget is spent."""
+    outside the timing), layer by layer until the time budget is spent; each
+    layer it runs is also the parity check of that layer's GPU result
+    (verify_layer)."""
     import numpy as np
     import oracle
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from helpers import bits, host, oracle_layer
+    from oracle.layers import bits, host, oracle_layer, router_only_layer
+    import moe_synth as syn
 
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = cpu_threads()
     oracle.set_threads(threads)
     done_layers, t_total, bytes_total = 0, 0.0, 0
-    import moe_synth as syn
+    checks = []
     for n in range(len(res.layer_ids)):
-        ids = res.routing[n].topk_ids.cpu().numpy()
-        L = oracle_layer(oracle, wl, res.W[n], experts=np.unique(ids))
         x = bits(res.x[n])
         li = host(res.logits_in[n])
+        logits = li if li is not None else oracle.router_logits(router_only_layer(oracle, wl, res.W[n]), x)
+        ids_orc, _ = oracle.topk_softmax(logits, wl.top_k)
+        ids_gpu = res.routing[n].topk_ids.cpu().numpy()
+        # touched experts to the host (outside the timing): the oracle's own
+        # choice, and the GPU's (they differ only on a near tie)
+        L = oracle_layer(oracle, wl, res.W[n], experts=np.union1d(ids_orc, ids_gpu))
         t0 = time.perf_counter()
         oracle.layer_forward(L, x, logits_in=li)
         t_total += time.perf_counter() - t0
         done_layers += 1
-        bytes_total += syn.effective_weight_bytes(wl, int(np.unique(ids).size), li is None)
+        bytes_total += syn.effective_weight_bytes(wl, int(np.unique(ids_orc).size), li is None)
+        checks.append(verify_layer(moe, oracle, L, wl, res, ctx, stream, n, x, li, logits))
+        if n == 0:
+            first = (L, x, li)
         if t_total >= budget_s:
             break
     # the first layer again on one thread
     oracle.set_threads(1)
-    ids = res.routing[0].topk_ids.cpu().numpy()
-    L = oracle_layer(oracle, wl, res.W[0], experts=np.unique(ids))
-    x, li = bits(res.x[0]), host(res.logits_in[0])
+    L, x, li = first
     t0 = time.perf_counter()
     oracle.layer_forward(L, x, logits_in=li)
     t_one = time.perf_counter() - t0
     oracle.set_threads(threads)
-    return {
+    compared = [c for c in checks if "ok" in c]
+    parity = {
+        "layers_compared": len(compared),
+        "layers_near_tie": len(checks) - len(compared),
+        "ok": all(c["ok"] for c in compared) and len(compared) > 0,
+        "worst_y_max_err_over_rms": max((c.get("y_max_err_over_rms", 0.0) for c in compared), default=None),
+        "worst_y_mean_rel_err": max((c.get("y_mean_rel_err", 0.0) for c in compared), default=None),
+        "failed": [c for c in compared if not c["ok"]][:4],
+    }
+    cpu = {
         "value": round(bytes_total / t_total / 1e9, 4),
         "unit": "GB/s",
         "us_per_layer": round(t_total / done_layers * 1e6, 1),
         "cores": threads,
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{done_layers} of {len(res.layer_ids)} layers of the same workload, one pass each, "
                   f"{threads} OpenMP threads, f64 arithmetic; layer 0 once more on 1 thread",
         "single_thread_us_per_layer": round(t_one * 1e6, 1),
     }
+    return cpu, parity
 
 
 def run_dense(args):
@@ -197,7 +294,7 @@ def run_dense(args):
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        threads = cpu_threads()
         oracle.set_threads(threads)
         qh, sh = q.cpu().numpy(), s.cpu().numpy()
         xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
@@ -207,7 +304,8 @@ def run_dense(args):
             done += 1
         t = (time.perf_counter() - t0) / done
         cpu = {"value": round(alg / t / 1e9, 4), "unit": "GB/s", "us_per_projection": round(t * 1e6, 1),
-               "cores": threads, "kind": "oracle",
+               "cores": threads, "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+               "kind": "oracle",
                "sample": f"{done} projections of the same shape and rows, {threads} OpenMP threads, f64"}
     line = {
         "metric": f"us per dense fp8 block-128 projection {n}x{k} + weight GB/s (% of HBM peak), {rows} row(s)",
@@ -273,7 +371,11 @@ def main():
     layers = args.layers if args.layers is not None else wl.layers
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    res = Resident(wl, rows, layers, device=dev, keep_y=False, norm=args.norm)
+    progress = None
+    if args.profile_steps is not None:
+        def progress(msg):
+            print(msg, file=sys.stderr, flush=True)
+    res = Resident(wl, rows, layers, device=dev, keep_y=False, norm=args.norm, progress=progress)
     ctx = moe.Ctx(0)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -283,10 +385,16 @@ def main():
 
     if args.profile_steps is not None:
         with torch.cuda.stream(stream):
-            for _ in range(args.profile_steps):
+            for i in range(args.profile_steps):
                 step()
-        torch.cuda.synchronize()
-        print(json.dumps({"profile_steps": args.profile_steps, "workload": wl.name, "rows": rows}))
+                torch.cuda.synchronize()
+                print(f"profiled step {i + 1} of {args.profile_steps}", file=sys.stderr, flush=True)
+        errors = moe.moe_ctx_device_errors(ctx, clear=False)
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": wl.name, "rows": rows,
+                          "device_errors": errors}))
+        ctx.close()
+        if errors:
+            sys.exit(1)
         return
 
     results = {}
@@ -325,6 +433,7 @@ def main():
     if args.launch in ("graph", "both"):
         results["graph"], spans_by_mode["graph"] = time_graph()
     assert moe.moe_ctx_status(ctx) == 0
+    device_errors = moe.moe_ctx_device_errors(ctx, clear=False)
     best_mode = min(results, key=results.get)
     ms_per_step = results[best_mode]
 
@@ -366,6 +475,7 @@ def main():
         if n:
             kernels[name] = {"avg_us": round(ms / n * 1e3, 3), "launches_per_step": n // kt_steps}
     moe.moe_ctx_set_timing(ctx, False)
+    device_errors |= moe.moe_ctx_device_errors(ctx, clear=False)
 
     # Algorithmic bytes of one layer: the effective weight bytes plus the
     # activations read (x) and the residual read and written.
@@ -394,9 +504,10 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                     "algorithmic_bytes_per_launch": int(layer_bytes)}
 
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, res, args.cpu_seconds)
+        cpu, parity = cpu_baseline(wl, res, args.cpu_seconds, moe, ctx, stream)
+        device_errors |= moe.moe_ctx_device_errors(ctx, clear=False)
 
     line = {
         "metric": METRIC,
@@ -425,10 +536,20 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "source_digest": source_digest(),
+        "parity": parity,
+        "device_errors": device_errors,
+        "run": run_info(),
     }
-    print(json.dumps(line), flush=True)
     ctx.close()
+    if device_errors or (parity is not None and not parity["ok"]):
+        # a timed run whose kernels flagged an error, or whose checked layers
+        # differ from the oracle, measured something other than the layer
+        print(json.dumps({"error": "the timed layers are not valid: "
+                          + (f"device error word {device_errors:#x}" if device_errors else "parity check failed"),
+                          "metric": METRIC, "device_errors": device_errors, "parity": parity,
+                          "config": line["config"], "run": line["run"]}), flush=True)
+        sys.exit(1)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

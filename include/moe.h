@@ -22,9 +22,10 @@
  * Conventions
  *  - Every pointer argument marked "device" is a device address on the ctx's
  *    GPU; "host" pointers are read during the call only.  The caller owns
- *    every buffer.  The library allocates no device memory during a call: it
- *    uses the caller's workspace and a few KB of synchronisation words the ctx
- *    allocates at creation.
+ *    every buffer.  The library allocates no device memory: a call uses the
+ *    caller's workspace, and a ctx's synchronisation words (10 KB) are a slot
+ *    of a fixed pool in the library's static device memory (64 ctxs per
+ *    device at once).
  *  - Calls are asynchronous: success (MOE_OK) means the work is enqueued on
  *    `stream` (an opaque hipStream_t; NULL = the device's null stream).  No
  *    call synchronises with the host.
@@ -59,7 +60,7 @@ extern "C" {
 #endif
 
 #define MOE_API __attribute__((visibility("default")))
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 enum moe_status {
     MOE_OK = 0,
@@ -69,6 +70,7 @@ enum moe_status {
     MOE_ERR_WORKSPACE_TOO_SMALL = -4,
     MOE_ERR_HIP = -5,               /* a HIP call failed; the ctx is now lost */
     MOE_ERR_DEVICE_LOST = -6,       /* sticky: an earlier HIP error or injected fault */
+    MOE_ERR_TOO_MANY_CTX = -7,      /* every ctx slot of the device is in use */
 };
 
 enum moe_weight_format {
@@ -163,8 +165,11 @@ enum moe_kernel_id {
 MOE_API int moe_abi_version(void);
 MOE_API const char *moe_strerror(int status);
 
-/* Create a ctx on HIP device `device`.  Allocates the ctx's synchronisation
- * words (a few KB) on that device.  Reads MOE_FAULT_AT (see
+/* Create a ctx on HIP device `device`.  Takes a free slot of synchronisation
+ * words from the library's static pool on that device and zeroes it
+ * (synchronously; MOE_ERR_TOO_MANY_CTX when all 64 are in use); allocates no
+ * device memory.  moe_ctx_destroy waits for the device to finish before it
+ * returns the slot.  Reads MOE_FAULT_AT (see
  * moe_ctx_set_fault_at), MOE_FORCE_ARM ("gemv" or "mfma") and
  * MOE_MFMA_MIN_ROWS from the environment. */
 MOE_API int moe_ctx_create(int device, moe_ctx **out);
@@ -199,9 +204,19 @@ MOE_API int moe_ctx_set_one_row_path(moe_ctx *ctx, int path);
  * measured faster grouped).  MOE_ERR_INVALID_ARG for rows < -1. */
 MOE_API int moe_ctx_set_few_rows(moe_ctx *ctx, int rows);
 /* Device-side error word: kernels that meet an expert id outside [0, E)
- * skip it and set bit 0; a bounded wait that timed out sets bit 1.  Synchronises the ctx's device; clears the word
- * when `clear` is non-zero. */
+ * skip it and set bit 0; a wait of the one-launch layer that reached the
+ * ctx's wait limit sets bit 1 (the layer's output is then invalid, and the
+ * ctx's synchronisation words may be left inconsistent, so later one-launch
+ * layers on it are invalid too until the word is cleared).  Synchronises the
+ * ctx's device and reads the word into *flags; with `clear` non-zero it
+ * zeroes the word and, when bit 1 was set, the synchronisation words. */
 MOE_API int moe_ctx_device_errors(moe_ctx *ctx, uint32_t *flags, int clear);
+/* Wait limit of the one-launch layer: a workgroup waiting for another one
+ * gives up after `us` microseconds of the device's constant clock (measured
+ * from its first poll; 0 = a single poll) and sets bit 1 of the device error
+ * word.  us < 0 restores the default, 10000 (10 ms); values above 60 s are
+ * taken as 60 s.  Normal waits last a few microseconds. */
+MOE_API int moe_ctx_set_wait_limit(moe_ctx *ctx, int64_t us);
 /* Per-kernel timing with HIP events on the launch stream (diagnostics;
  * adds an event pair around every launch while enabled).  enable != 0
  * starts (and resets) it; stats synchronise on the recorded events. */

@@ -23,6 +23,7 @@ MOE_ERR_MISALIGNED = -3
 MOE_ERR_WORKSPACE_TOO_SMALL = -4
 MOE_ERR_HIP = -5
 MOE_ERR_DEVICE_LOST = -6
+MOE_ERR_TOO_MANY_CTX = -7
 
 MOE_WFMT_FP8_E4M3_B128 = 0
 MOE_WFMT_NVFP4 = 1
@@ -97,6 +98,7 @@ def lib():
             "moe_ctx_set_one_row_path": ([vp, i32], i32),
             "moe_ctx_set_few_rows": ([vp, i32], i32),
             "moe_ctx_device_errors": ([vp, C.POINTER(C.c_uint32), i32], i32),
+            "moe_ctx_set_wait_limit": ([vp, i64], i32),
             "moe_ctx_set_timing": ([vp, i32], i32),
             "moe_ctx_kernel_stats": ([vp, i32, C.POINTER(C.c_double), C.POINTER(i64)], i32),
             "moe_workspace_bytes": ([C.POINTER(LayerWeightsC), i32], sz),
@@ -207,6 +209,10 @@ def moe_ctx_device_errors(ctx: Ctx, clear: bool = True) -> int:
     v = C.c_uint32(0)
     _check(lib().moe_ctx_device_errors(ctx.handle, C.byref(v), int(clear)), "moe_ctx_device_errors")
     return int(v.value)
+
+
+def moe_ctx_set_wait_limit(ctx: Ctx, us: int) -> None:
+    _check(lib().moe_ctx_set_wait_limit(ctx.handle, int(us)), "moe_ctx_set_wait_limit")
 
 
 def moe_ctx_set_timing(ctx: Ctx, enable: bool) -> None:

@@ -20,10 +20,16 @@
 
 namespace {
 
-// ctx words: the router ticket, the error word and the warming sink on their
-// own lines, then the single-launch layer's synchronisation lines.
-enum SyncWord : int { kWordRouterTicket = 0, kWordError = 64, kWordSink = 128, kWordGroupTicket = 192, kWordLayerSync = 1024,
-                      kSyncWords = 1024 + 40 * 64 };
+// ctx words (kernels.hpp): tickets, the error word, the warming sink and the
+// single-launch layer's synchronisation lines, from the ctx pool.
+using moe::kCtxWords;
+using moe::kLayerSyncWords;
+using moe::kWordError;
+using moe::kWordGroupTicket;
+using moe::kWordLayerSync;
+using moe::kWordRouterTicket;
+using moe::kWordSink;
+constexpr int64_t kDefaultWaitUs = 10000;   // a one-launch layer's wait gives up after 10 ms
 constexpr int kDenseMaxK = 8192;         // a wave's 64 lanes hold one scale per 128-wide block
 constexpr int kDenseMaxRows = 1 << 20;   // matrix-core grid rows stay far below 65535
 constexpr int kDefaultFewRows = 8;       // steps of 2..8 rows: one GEMV per row and slot (measured)
@@ -40,6 +46,7 @@ constexpr int kMfmaStepRows = 9;
 constexpr int kMaxRows = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
+static_assert(kMaxTopK == moe::kMaxTopK, "top-k limit");
 constexpr int kMaxHidden = 8192;
 constexpr int kMaxInter = 4096;
 constexpr size_t kMaxGroupWords = 8192;   // grouping bitmap: 32 KB of LDS
@@ -60,7 +67,10 @@ struct moe_ctx {
     int few_rows = kFewRowsAuto;
     int force_arm = 0;
     int one_row_path = 0;        // 0 = single launch where built, 1 = three launches
-    uint32_t *words = nullptr;   // device: kSyncWords words
+    uint32_t *words = nullptr;   // device: kCtxWords words of the ctx pool
+    int slot = -1;               // the pool slot holding them
+    int64_t clock_khz = 100000;  // the device's constant clock (s_memrealtime)
+    int64_t wait_us = kDefaultWaitUs;
     bool timing = false;
     std::vector<TimingRecord> recs;
     std::vector<hipEvent_t> spare;
@@ -448,9 +458,14 @@ int do_ffn_few(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
     return launch(c, MOE_K_NORM, st, [&] { return moe::launch_rmsnorm(a, st); });
 }
 
+// A wait's deadline in ticks of the device's constant clock.
+uint64_t wait_ticks(const moe_ctx *c) { return (uint64_t)c->wait_us * (uint64_t)c->clock_khz / 1000u; }
+
 int do_layer_r1(moe_ctx *c, const moe::RouteArgs &r, moe::FfnArgs a, hipStream_t st) {
     if (c->one_row_path == 0 && moe::layer_r1_supported(r, a))
-        return launch(c, MOE_K_LAYER, st, [&] { return moe::launch_layer_r1(r, a, c->words + kWordLayerSync, st); });
+        return launch(c, MOE_K_LAYER, st, [&] {
+            return moe::launch_layer_r1(r, a, c->words + kWordLayerSync, wait_ticks(c), st);
+        });
     int rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_lead_r1(r, a, st); });
     if (rc) return rc;
     rc = launch(c, MOE_K_GATE_UP, st, [&] { return moe::launch_gate_up_r1(a, st); });
@@ -493,6 +508,7 @@ MOE_API const char *moe_strerror(int status) {
         case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case MOE_ERR_HIP: return "HIP error (ctx lost)";
         case MOE_ERR_DEVICE_LOST: return "device lost (sticky)";
+        case MOE_ERR_TOO_MANY_CTX: return "too many ctxs on the device";
         default: return "unknown status";
     }
 }
@@ -507,12 +523,14 @@ MOE_API int moe_ctx_create(int device, moe_ctx **out) {
     if (!c) return MOE_ERR_INVALID_ARG;
     c->device = device;
     DeviceGuard g(device);
-    if (!g.ok() || hipMalloc(&c->words, kSyncWords * sizeof(uint32_t)) != hipSuccess ||
-        hipMemset(c->words, 0, kSyncWords * sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-        if (c->words) (void)hipFree(c->words);
+    int khz = 0;
+    const hipError_t e = g.ok() ? moe::ctx_slot_acquire(device, &c->slot, &c->words) : hipErrorInvalidDevice;
+    if (e != hipSuccess) {
         delete c;
-        return MOE_ERR_HIP;
+        return e == hipErrorOutOfMemory ? MOE_ERR_TOO_MANY_CTX : MOE_ERR_HIP;
     }
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
+        c->clock_khz = khz;
     if (const char *v = getenv("MOE_FAULT_AT")) c->fault_countdown = std::max<long long>(0, atoll(v));
     if (const char *v = getenv("MOE_MFMA_MIN_ROWS")) c->mfma_min_rows = std::max(0, atoi(v));
     if (const char *v = getenv("MOE_FEW_ROWS")) c->few_rows = std::max(kFewRowsAuto, atoi(v));
@@ -533,7 +551,9 @@ MOE_API int moe_ctx_destroy(moe_ctx *c) {
         (void)hipEventDestroy(r.b);
     }
     for (auto e : c->spare) (void)hipEventDestroy(e);
-    if (c->words) (void)hipFree(c->words);
+    // the slot may be reused by the next ctx: let this ctx's work finish first
+    (void)hipDeviceSynchronize();
+    if (c->slot >= 0) moe::ctx_slot_release(c->device, c->slot);
     delete c;
     return MOE_OK;
 }
@@ -577,8 +597,21 @@ MOE_API int moe_ctx_device_errors(moe_ctx *c, uint32_t *flags, int clear) {
     if (hipDeviceSynchronize() != hipSuccess) return fail(c, MOE_ERR_HIP);
     if (hipMemcpy(flags, c->words + kWordError, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
         return fail(c, MOE_ERR_HIP);
-    if (clear && hipMemset(c->words + kWordError, 0, sizeof(uint32_t)) != hipSuccess) return fail(c, MOE_ERR_HIP);
-    if (clear && hipDeviceSynchronize() != hipSuccess) return fail(c, MOE_ERR_HIP);
+    if (clear) {
+        if (hipMemset(c->words + kWordError, 0, sizeof(uint32_t)) != hipSuccess) return fail(c, MOE_ERR_HIP);
+        // a wait that gave up may have left the one-launch layer's
+        // synchronisation words inconsistent: nothing runs now, so zero them
+        if ((*flags & moe::kErrWaitTimeout) &&
+            hipMemset(c->words + kWordLayerSync, 0, sizeof(uint32_t) * kLayerSyncWords) != hipSuccess)
+            return fail(c, MOE_ERR_HIP);
+        if (hipDeviceSynchronize() != hipSuccess) return fail(c, MOE_ERR_HIP);
+    }
+    return MOE_OK;
+}
+
+MOE_API int moe_ctx_set_wait_limit(moe_ctx *c, int64_t us) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    c->wait_us = us < 0 ? kDefaultWaitUs : std::min<int64_t>(us, 60 * 1000 * 1000);
     return MOE_OK;
 }
 

@@ -359,9 +359,6 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + expf(-g)) * u;
 }
 
-// Device-side error word bits.
-enum : uint32_t { kErrBadExpertId = 1u, kErrWaitTimeout = 2u };
-
 __device__ __forceinline__ void flag_error(uint32_t *err, uint32_t bit) {
     if (err) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -11,7 +11,6 @@
 namespace moe {
 
 
-constexpr int kMaxSlots = 17;          // top_k <= 16, plus the shared expert
 constexpr int kPairsPerWave = 2;       // gate/up (i, I+i) row pairs per wave
 
 __device__ __forceinline__ float sigmoid(float t) { return 1.0f / (1.0f + expf(-t)); }

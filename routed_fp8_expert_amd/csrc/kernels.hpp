@@ -17,6 +17,28 @@ struct ExpertSet {
 // Per-step bookkeeping written by the grouping kernel, read by the expert
 // kernels (int32 words in the workspace).
 constexpr int kReplicas = 8;   // one copy per XCD (workgroups map to XCDs by index)
+constexpr int kMaxTopK = 16;
+constexpr int kMaxSlots = kMaxTopK + 1;   // routed slots plus the shared expert
+
+// A ctx's synchronisation words (uint32, device memory of the ctx pool), in
+// groups that each start a 256-byte line: the router ticket of the one-row
+// lead kernel, the device error word, the cache-warming sink, the ticket of
+// the fused top-k + grouping launch, then the one-launch layer's lines
+// (layer.hip): a ticket, kReplicas ready-flag copies, a down-done counter,
+// one counter per slot, a slots-done counter and kReplicas h-ready copies.
+constexpr int kSyncLine = 64;   // words per 256-byte line
+constexpr int kLayerSyncWords = (3 + 2 * kReplicas + kMaxSlots) * kSyncLine;
+enum CtxWord : int {
+    kWordRouterTicket = 0,
+    kWordError = 1 * kSyncLine,
+    kWordSink = 2 * kSyncLine,
+    kWordGroupTicket = 3 * kSyncLine,
+    kWordLayerSync = 4 * kSyncLine,
+    kCtxWords = kWordLayerSync + kLayerSyncWords
+};
+// Bits of the ctx's device error word.
+enum : uint32_t { kErrBadExpertId = 1u, kErrWaitTimeout = 2u };
+
 constexpr int kMfmaTileRows = 16;   // rows of an expert per matrix-core tile (down)
 constexpr int kMfmaGuTileRows = 64; // rows of an expert per gate/up matrix-core tile
 
@@ -102,14 +124,26 @@ hipError_t launch_gate_up(const FfnArgs &a, hipStream_t st);
 // One-row layer: router rows + shared expert, then top-k + routed gate/up.
 hipError_t launch_lead_r1(const RouteArgs &r, const FfnArgs &a, hipStream_t st);
 hipError_t launch_gate_up_r1(const FfnArgs &a, hipStream_t st);
-// One-row layer in a single launch (layer.hip); `sync` = 27 lines of 64 ctx words.
+// One-row layer in a single launch (layer.hip); `sync` = the ctx's
+// kLayerSyncWords layer words, all zero between launches; a wait for another
+// workgroup gives up after `wait_ticks` ticks of the device's constant clock
+// (s_memrealtime).
 bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a);
-hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync, hipStream_t st);
+hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync, uint64_t wait_ticks,
+                           hipStream_t st);
 hipError_t launch_down_blend_r1(const FfnArgs &a, hipStream_t st);
 hipError_t launch_down_grouped(const FfnArgs &a, hipStream_t st);
 hipError_t launch_blend(const FfnArgs &a, hipStream_t st);
 hipError_t launch_rmsnorm(const FfnArgs &a, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, hipStream_t st);
+
+// The ctx pool (ctx_pool.hip): kMaxCtxPerDevice slots of kCtxWords words per
+// device in static device memory.  ctx_slot_acquire makes `device` current's
+// pool address known (hipGetSymbolAddress, once per device), takes a free
+// slot, zeroes it (synchronously) and returns its words; release frees it.
+constexpr int kMaxCtxPerDevice = 64;
+hipError_t ctx_slot_acquire(int device, int *slot, uint32_t **words);
+void ctx_slot_release(int device, int slot);
 
 // Diagnostics: decode n codes with the kernels' own converters.
 hipError_t launch_decode_probe(int fmt, const uint8_t *codes, float *out, int n, hipStream_t st);

@@ -19,13 +19,30 @@
 //                   every slot's down matrix at once, wait for the slot
 //                   counters, then blend (the first one publishes the routing)
 //
-// A workgroup only ever waits on lower-indexed workgroups, and workgroups are
-// dispatched in index order, so every wait ends without needing all
-// workgroups resident.  Every wait is also bounded: past the spin limit the
-// workgroup sets the ctx error word and goes on.  Values crossing workgroups
-// are written and read at agent scope (write-through stores, coherent loads);
-// counters are agent-scope atomics; no cache writeback or invalidate is used.
-// The last down workgroup resets the synchronisation words for the next call.
+// Forward progress: the launcher takes this kernel only when every workgroup
+// of the grid can be resident at once (an occupancy query), so all of them
+// run concurrently and every wait is on a running workgroup.  Independently
+// of that, a workgroup only ever waits on lower-indexed workgroups, so with
+// workgroups dispatched in index order (on each XCD) every wait would end
+// even without co-residency.  Every wait is also bounded in time: past the
+// deadline (the ctx's wait limit, 10 ms by default, measured on the device's
+// constant clock) the workgroup sets the ctx error word and goes on, so a
+// starved launch costs at most about two deadlines (the down workgroups' two
+// waits), never a hang.
+//
+// Ordering: values crossing workgroups are written and read only with
+// agent-scope atomic operations (relaxed; on gfx950 these are the
+// device-coherent stores and loads, which bypass the non-coherent caches), so
+// no cache writeback or invalidate is needed.  A producer waits for its own
+// stores to complete (s_waitcnt 0, every wave, then a barrier) before its
+// arrival atomic, so the stores are visible device-wide before the count
+// that announces them; a consumer issues its data loads only after its poll
+// load has returned the flag (in-order issue within a wave, a barrier for
+// the other waves).  This is the release/acquire pattern restricted to data
+// that is itself accessed atomically.
+// The last down workgroup resets the synchronisation words for the next call;
+// after a timed-out wait they may be left inconsistent, and the host clears
+// them with the error word.
 #include "gemv.hpp"
 
 #include <mutex>
@@ -34,12 +51,11 @@
 namespace moe {
 
 constexpr int P1 = kPairsPerWave;
-constexpr int kSpinLimit = 1 << 16;
 
 // Synchronisation words, each on its own 256-byte line so pollers and
 // arrivals on different words do not share a memory channel; the ready flag
 // has kReadyCopies copies, polled by block index.
-constexpr int kLine = 64;            // words per line
+constexpr int kLine = kSyncLine;
 constexpr int kReadyCopies = kReplicas;
 enum : int {
     kSyncTicket = 0,
@@ -50,20 +66,23 @@ enum : int {
     kSyncHReady = (3 + kReadyCopies + kMaxSlots) * kLine,  // kReadyCopies lines
     kSyncWordsTotal = (3 + 2 * kReadyCopies + kMaxSlots) * kLine
 };
+static_assert(kSyncWordsTotal == kLayerSyncWords, "layer synchronisation words and the ctx layout disagree");
 
-// True once *p >= target; false after the spin limit.
-__device__ __forceinline__ bool poll_geq(const unsigned *p, unsigned target) {
-    for (int i = 0; i < kSpinLimit; ++i) {
+// True once *p >= target; false once `ticks` ticks of the constant clock
+// have passed since the first poll (at least one poll is made).
+__device__ __forceinline__ bool poll_geq(const unsigned *p, unsigned target, uint64_t ticks) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
         if (ld_agent(p) >= target) return true;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) return false;
         __builtin_amdgcn_s_sleep(4);
     }
-    return false;
 }
 
 // Every thread of the block calls this; thread 0 polls, the block waits at
 // the barrier.  A timeout sets the error word.
-__device__ __forceinline__ void block_wait(const unsigned *p, unsigned target, uint32_t *err) {
-    if (threadIdx.x == 0 && !poll_geq(p, target)) flag_error(err, kErrWaitTimeout);
+__device__ __forceinline__ void block_wait(const unsigned *p, unsigned target, uint32_t *err, uint64_t ticks) {
+    if (threadIdx.x == 0 && !poll_geq(p, target, ticks)) flag_error(err, kErrWaitTimeout);
     __syncthreads();
 }
 
@@ -93,6 +112,7 @@ __device__ __forceinline__ void slot_done(unsigned *sync, int slot, int blocks_p
 struct LayerGrid {
     int nrb, nsb, ngb, ndb;   // router, shared gate/up, routed gate/up per slot, down blocks
     unsigned *sync;           // kSyncWordsTotal words
+    uint64_t wait_ticks;      // a wait's deadline, in ticks of the constant clock
 };
 
 // h of every slot into LDS, read coherently (8-byte agent-scope loads, all
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     // ---------------------------------------------------------------- routed gate/up
     if (b < k * g.ngb) {
         const int slot = b % k, slice = b / k;
-        block_wait(ready, 1u, a.err);
+        block_wait(ready, 1u, a.err, g.wait_ticks);
         block_topk<NV>(r, lrep, ids_s, w_s);
         const int e = ids_s[slot];
         const ExpertSet &X = a.routed;
@@ -229,7 +249,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     const int o = (b * 4 + wid) * RPW + lane / LPR;
     const bool live = o < a.H;
     const int nslots = k + (has_shared ? 1 : 0);
-    block_wait(ready, 1u, a.err);
+    block_wait(ready, 1u, a.err, g.wait_ticks);
     block_topk<NV>(r, lrep, ids_s, w_s);
     if (b == 0 && wid == 0 && lane < k) {
         r.ids[lane] = ids_s[lane];
@@ -246,7 +266,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     const float s_gate = has_shared ? ld_agent(a.s) : 0.0f;
     const float res_in = a.res ? bf16_to_f32(a.res[live ? o : 0]) : 0.0f;   // unconditional load (clamped)
     // every slot's h is complete once the h-ready flag is up
-    block_wait(sync + kSyncHReady + rep_id * kLine, 1u, a.err);
+    block_wait(sync + kSyncHReady + rep_id * kLine, 1u, a.err, g.wait_ticks);
     stage_h<cols_per_chunk<FMT>(), HS, KS>(a.h_rep + (size_t)rep_id * hrep_stride, nslots,
                                            reinterpret_cast<float *>(hlds4));
     __syncthreads();
@@ -329,7 +349,7 @@ static LayerShape layer_shape(const RouteArgs &r, const FfnArgs &a) {
     return s;
 }
 
-static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, unsigned *sync) {
+static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, unsigned *sync, uint64_t wait_ticks = 0) {
     LayerGrid g;
     const int n_rows = (r.logits_in ? 0 : r.E) + (r.wsg ? 1 : 0);
     g.nrb = n_rows > 0 ? (n_rows + 3) / 4 : 1;
@@ -338,6 +358,7 @@ static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, unsig
     const int rows_per_block = 4 * (kWave / lpr);
     g.ndb = (a.H + rows_per_block - 1) / rows_per_block;
     g.sync = sync;
+    g.wait_ticks = wait_ticks;
     return g;
 }
 static int layer_blocks(const LayerGrid &g, const FfnArgs &a) { return g.nrb + g.nsb + a.k * g.ngb + g.ndb; }
@@ -348,8 +369,9 @@ static size_t layer_lds(const FfnArgs &a) {
 }
 
 template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
-static hipError_t layer_launch(const RouteArgs &r, const FfnArgs &a, unsigned *sync, hipStream_t st) {
-    const LayerGrid g = layer_grid(r, a, LPR, sync);
+static hipError_t layer_launch(const RouteArgs &r, const FfnArgs &a, unsigned *sync, uint64_t wait_ticks,
+                               hipStream_t st) {
+    const LayerGrid g = layer_grid(r, a, LPR, sync, wait_ticks);
     hipLaunchKernelGGL((k_layer_r1<FMT, NCH, NV, LPR, DCH, KS, HS>), dim3(layer_blocks(g, a)), dim3(256),
                        layer_lds(a), st, r, a, g);
     return hipGetLastError();
@@ -415,13 +437,14 @@ bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
     return false;
 }
 
-hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync, hipStream_t st) {
+hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync, uint64_t wait_ticks,
+                           hipStream_t st) {
     const LayerShape s = layer_shape(r, a);
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
 #define MOE_GO(F, N, V, L, D, K, HSV)                                                                  \
     if (s.fmt == F && s.nch == N && s.nv == V && s.lpr == L && s.dch == D && nslots <= K &&              \
         a.routed.inter == HSV && (a.shared.inter == 0 || a.shared.inter == HSV))                          \
-        return layer_launch<F, N, V, L, D, K, HSV>(r, a, sync, st);
+        return layer_launch<F, N, V, L, D, K, HSV>(r, a, sync, wait_ticks, st);
     MOE_LAYER_SHAPES(MOE_GO)
 #undef MOE_GO
     return hipErrorInvalidValue;

@@ -25,7 +25,7 @@ class Resident:
 
     def __init__(self, wl: syn.Workload, rows: int, layers: Optional[int] = None, device="cuda",
                  x_attempts: Optional[Sequence[int]] = None, layer_ids: Optional[Sequence[int]] = None,
-                 keep_y: bool = True, with_routing: bool = True, norm: bool = False):
+                 keep_y: bool = True, with_routing: bool = True, norm: bool = False, progress=None):
         self.wl, self.rows, self.device = wl, rows, torch.device(device)
         ids = list(layer_ids) if layer_ids is not None else list(range(layers or wl.layers))
         self.layer_ids = ids
@@ -33,6 +33,8 @@ class Resident:
         self.lw: List[B.LayerWeights] = []
         self.x, self.logits_in, self.residual0, self.y, self.routing = [], [], [], [], []
         for n, l in enumerate(ids):
+            if progress is not None and n % 8 == 0:
+                progress(f"building layer {n + 1} of {len(ids)}")
             W = syn.make_layer_weights(wl, l, self.device)
             self.W.append(W)
             self.lw.append(layer_weights(wl, W))

@@ -43,9 +43,10 @@ def test_exports_match_headers(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     for status, text in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported shape"),
-                         (-4, "workspace too small"), (-6, "device lost (sticky)")]:
+                         (-4, "workspace too small"), (-6, "device lost (sticky)"),
+                         (-7, "too many ctxs on the device")]:
         assert lib.strerror(status) == text
     assert lib.strerror(-99) == "unknown status"
 

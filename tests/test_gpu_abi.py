@@ -222,3 +222,60 @@ def test_fault_injection_on_single_launch_layer(moe, tiny):
         moe.moe_layer_forward(ctx, lw, x, y, None, ws, routing=rt)  # launch 2 refused
     assert moe.moe_ctx_status(ctx) == moe.binding.MOE_ERR_DEVICE_LOST
     ctx.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "a3b"])
+def test_wait_limit_zero_times_out_and_recovers(moe, orc, name):
+    """A wait limit of zero makes every waiting workgroup of the one-launch
+    layer give up after a single poll (forced from the host: every kernel
+    still exits).  At the 35B-A3B shape the down workgroups' wait for the
+    experts' h cannot have been met by then, so bit 1 of the device error
+    word is set.  Clearing the word also resets the ctx's synchronisation
+    words, and the next call, at the default limit, matches the oracle."""
+    from gpu_helpers import check_layer, oracle_threads
+    from helpers import tie_free_x
+    wl = syn.WORKLOADS[name]
+    W = syn.make_layer_weights(wl, 0, "cuda")
+    ctx = moe.Ctx(0)
+    lw, _, y, rt, ws = _setup(moe, wl, W, rows=1)
+    x, _ = tie_free_x(orc, wl, W, 0, 1, device="cuda")
+    res0 = syn.make_residual(wl, 0, 1, "cuda")
+    moe.moe_ctx_set_timing(ctx, True)
+    moe.moe_ctx_set_wait_limit(ctx, 0)
+    print(f"wait limit 0: {name}", flush=True)
+    for _ in range(3):
+        moe.moe_layer_forward(ctx, lw, x, y, res0.clone(), ws, routing=rt)
+    torch.cuda.synchronize()
+    assert moe.moe_ctx_kernel_stats(ctx, moe.KERNELS.index("layer"))[1] == 3
+    flags = moe.moe_ctx_device_errors(ctx, clear=True)
+    if name == "a3b":
+        assert flags & 2, f"no wait timed out at limit 0 (flags {flags})"
+    assert flags & ~3 == 0
+    moe.moe_ctx_set_wait_limit(ctx, -1)
+    res = res0.clone()
+    print(f"default wait limit after clearing: {name}", flush=True)
+    moe.moe_layer_forward(ctx, lw, x, y, res, ws, routing=rt)
+    torch.cuda.synchronize()
+    assert moe.moe_ctx_device_errors(ctx, clear=False) == 0
+    orc.set_threads(oracle_threads())
+    check_layer(orc, wl, W, x, None, res0, y, res, rt, what=f"{name} after a forced timeout")
+    ctx.close()
+
+
+def test_ctx_pool_slots_are_reused(moe):
+    """Ctxs take their synchronisation words from a fixed pool (64 per
+    device): ctxs are created until the pool is full (at most 64, fewer if
+    other ctxs are alive), the next one is refused with
+    MOE_ERR_TOO_MANY_CTX, and destroying one frees its slot."""
+    import gc
+    gc.collect()
+    live = []
+    with pytest.raises(moe.MoeError) as ei:
+        for _ in range(65):
+            live.append(moe.Ctx(0))
+    assert ei.value.status == moe.binding.MOE_ERR_TOO_MANY_CTX
+    assert 1 <= len(live) <= 64
+    live.pop().close()
+    extra = moe.Ctx(0)
+    for c in live + [extra]:
+        c.close()
