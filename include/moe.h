@@ -262,6 +262,24 @@ MOE_API int moe_layer_forward(moe_ctx *ctx, const moe_layer_weights *w, const vo
                               void *y, void *residual, int64_t ldy, void *ws, size_t ws_bytes,
                               void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_layer_forward with its workspace taken from the library's static
+ * device scratch instead of a caller's buffer.  The scratch is a fixed
+ * 16 MiB array per device (MOE_STATIC_SCRATCH_BYTES), held until the process
+ * ends and shared by every call on that device: calls that overlap on one
+ * GPU (other streams, other ctxs, other threads) race on it and must be
+ * serialised by the caller.  It keeps the last call's contents; no kernel
+ * relies on it starting at zero.  Allocates nothing (no hipMalloc, hipFree
+ * or allocating library call).  Arguments and errors as moe_layer_forward,
+ * plus MOE_ERR_WORKSPACE_TOO_SMALL when the call's workspace
+ * (moe_workspace_bytes) exceeds the scratch: at the 35B-A3B shape up to about
+ * 170 rows. */
+#define MOE_STATIC_SCRATCH_BYTES (16u << 20)
+MOE_API int moe_layer_forward_static(moe_ctx *ctx, const moe_layer_weights *w, const void *x, int rows,
+                                     int64_t ldx, const float *logits_in, const moe_routing *routing,
+                                     void *y, void *residual, int64_t ldy, void *stream);
+
 /* Epilogue of moe_layer_forward_norm: RMSNorm of every output row for the
  * next layer (GB10 blueprint, "Kernels": residual_add_rms_norm, the norm that
  * follows the MoE output joining the residual; Qwen3-8B card, "Structure":

@@ -108,6 +108,8 @@ def lib():
                                 vp, vp, i64, vp, sz, vp], i32),
             "moe_layer_forward": ([vp, C.POINTER(LayerWeightsC), vp, i32, i64, vp,
                                    C.POINTER(RoutingC), vp, vp, i64, vp, sz, vp], i32),
+            "moe_layer_forward_static": ([vp, C.POINTER(LayerWeightsC), vp, i32, i64, vp,
+                                          C.POINTER(RoutingC), vp, vp, i64, vp], i32),
             "moe_layer_forward_norm": ([vp, C.POINTER(LayerWeightsC), vp, i32, i64, vp,
                                         C.POINTER(RoutingC), vp, vp, i64, C.POINTER(NormC), vp, sz, vp], i32),
             "moe_dense_fp8": ([vp, C.POINTER(DenseWeightsC), vp, i32, i64, vp, i64, vp], i32),
@@ -342,6 +344,18 @@ def moe_layer_forward(ctx: Ctx, w: LayerWeights, x: torch.Tensor, y: Optional[to
                                    _p(logits_in), routing.ref if routing is not None else None,
                                    _p(y), _p(residual), ldy, _p(ws), ws.numel(), _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_static(ctx: Ctx, w: LayerWeights, x: torch.Tensor, y: Optional[torch.Tensor],
+                             residual: Optional[torch.Tensor], logits_in: Optional[torch.Tensor] = None,
+                             routing: Optional[Routing] = None, stream=None) -> None:
+    """moe_layer_forward on the library's static device scratch (no workspace argument)."""
+    rows = x.shape[0]
+    ldy = _ld(y if y is not None else residual, w.hidden)
+    _check(lib().moe_layer_forward_static(ctx.handle, w.ref, _p(x), rows, _ld(x, w.hidden), _p(logits_in),
+                                          routing.ref if routing is not None else None, _p(y), _p(residual),
+                                          ldy, _stream(stream)),
+           "moe_layer_forward_static")
 
 
 def moe_layer_forward_norm(ctx: Ctx, w: LayerWeights, x: torch.Tensor, y: Optional[torch.Tensor],

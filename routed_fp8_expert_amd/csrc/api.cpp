@@ -529,6 +529,12 @@ MOE_API int moe_ctx_create(int device, moe_ctx **out) {
         delete c;
         return e == hipErrorOutOfMemory ? MOE_ERR_TOO_MANY_CTX : MOE_ERR_HIP;
     }
+    // the static workspace's address on this device, for moe_layer_forward_static
+    if (moe::static_scratch_init(device) != hipSuccess) {
+        moe::ctx_slot_release(device, c->slot);
+        delete c;
+        return MOE_ERR_HIP;
+    }
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
         c->clock_khz = khz;
     if (const char *v = getenv("MOE_FAULT_AT")) c->fault_countdown = std::max<long long>(0, atoll(v));
@@ -757,6 +763,20 @@ MOE_API int moe_layer_forward(moe_ctx *c, const moe_layer_weights *w, const void
                               const float *logits_in, const moe_routing *routing, void *y, void *res, int64_t ldy,
                               void *ws, size_t ws_bytes, void *stream) {
     return moe_layer_forward_norm(c, w, x, R, ldx, logits_in, routing, y, res, ldy, nullptr, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_layer_forward_static(moe_ctx *c, const moe_layer_weights *w, const void *x, int R, int64_t ldx,
+                                     const float *logits_in, const moe_routing *routing, void *y, void *res,
+                                     int64_t ldy, void *stream) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->status) return MOE_ERR_DEVICE_LOST;
+    int rc;
+    if ((rc = validate_weights(w)) || (rc = validate_rows(w, R))) return rc;
+    if (make_layout(w, R).total > moe::kStaticScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = moe::static_scratch_ptr(c->device);
+    if (!ws) return MOE_ERR_HIP;
+    return moe_layer_forward_norm(c, w, x, R, ldx, logits_in, routing, y, res, ldy, nullptr, ws,
+                                  moe::kStaticScratchBytes, stream);
 }
 
 MOE_API int moe_dense_fp8(moe_ctx *c, const moe_dense_weights *w, const void *x, int R, int64_t ldx, void *y,

@@ -145,6 +145,14 @@ constexpr int kMaxCtxPerDevice = 64;
 hipError_t ctx_slot_acquire(int device, int *slot, uint32_t **words);
 void ctx_slot_release(int device, int slot);
 
+// The static workspace of moe_layer_forward_static (static_scratch.hip):
+// kStaticScratchBytes per device.  static_scratch_init resolves its address
+// on `device`, which must be current (once per device; at ctx creation);
+// static_scratch_ptr returns it (null before init).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch_init(int device);
+void *static_scratch_ptr(int device);
+
 // Diagnostics: decode n codes with the kernels' own converters.
 hipError_t launch_decode_probe(int fmt, const uint8_t *codes, float *out, int n, hipStream_t st);
 
