@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--profile-steps", type=int, default=None,
                    help="run exactly this many steps (no warmup, no report) for profilers")
+    p.add_argument("--phases", type=int, default=None, metavar="N",
+                   help="phase stamps of N one-launch layers (cycling the resident layers, a sync between "
+                        "calls) instead of the timing: when each workgroup role reaches each phase")
     p.add_argument("--copy-calibration", type=int, default=None, metavar="MIB",
                    help="run 10 device-to-device copies of MIB MiB (the counter calibration kernel)")
     return p.parse_args()
@@ -236,6 +239,89 @@ def cpu_baseline(wl, res, budget_s: float, moe, ctx, stream):
     return cpu, parity
 
 
+PHASES = {
+    0: ["start", "row dot done", "arrival counted", "done word published (last of its sub-counter)"],
+    1: ["start", "-", "-", "h stored", "arrival counted"],
+    2: ["start", "routing done words seen", "top-k done", "h stored", "arrival counted", "-", "-", "-", "-",
+        "logits arrived"],
+    3: ["start", "routing done words seen", "top-k done", "down-row loads issued", "gate/up done words seen",
+        "h staged", "blend stored", "group arrival returned", "group line cleared (last of its group)",
+        "logits arrived"],
+}
+# table order of the phases per role (stamp word numbers)
+PHASE_ORDER = {0: [1, 2, 3, 4], 1: [1, 4, 5], 2: [1, 2, 10, 3, 4, 5], 3: [1, 2, 10, 3, 4, 5, 6, 7, 8, 9]}
+ROLES = {0: "router", 1: "shared gate/up", 2: "routed gate/up", 3: "down"}
+
+
+def run_phases(args, wl, res, moe, ctx, stream, layers):
+    """Phase stamps of the one-launch layer: per call, each workgroup's
+    constant-clock stamps relative to the earliest workgroup start of that
+    call; per role and phase the median and the latest workgroup, averaged
+    over the calls.  Also the back-to-back time per layer of the same
+    workload (no stamps) for the launch boundary."""
+    import numpy as np
+    import torch
+
+    def step():
+        res.run(ctx, stream=stream, write_y=False)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    with torch.cuda.stream(stream):
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            step()
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    us_layer = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps / layers
+    buf = torch.full((8192 * 16,), -1, dtype=torch.int64, device=res.device)
+    khz = moe.moe_debug_set_phase_stamps(ctx, buf)
+    per_us = khz / 1000.0
+    med = {}
+    mx = {}
+    spans = []
+    for i in range(args.phases):
+        n = i % layers
+        buf.fill_(-1)
+        torch.cuda.synchronize()
+        moe.moe_layer_forward(ctx, res.lw[n], res.x[n], None, res.residual[n], res.ws,
+                              logits_in=res.logits_in[n], routing=res.routing[n], stream=stream)
+        torch.cuda.synchronize()
+        w = buf.view(-1, 16).cpu().numpy()
+        w = w[w[:, 1] >= 0]
+        t0 = w[:, 1].min()
+        role = w[:, 0] & 0xFF
+        spans.append((w[:, 1:][w[:, 1:] >= 0].max() - t0) / per_us)
+        for r in PHASES:
+            sel = w[role == r]
+            for j in range(1, len(PHASES[r]) + 1):
+                v = sel[:, j]
+                v = v[v >= 0]
+                if v.size == 0:
+                    continue
+                t = (v - t0) / per_us
+                med.setdefault((r, j), []).append(float(np.median(t)))
+                mx.setdefault((r, j), []).append(float(t.max()))
+    moe.moe_debug_set_phase_stamps(ctx, None)
+    assert moe.moe_ctx_device_errors(ctx, clear=False) == 0
+    print(f"| role | phase | median workgroup (us) | latest workgroup (us) |")
+    print("|---|---|---|---|")
+    for r in PHASES:
+        for j in PHASE_ORDER[r]:
+            if (r, j) in med:
+                print(f"| {ROLES[r]} | {PHASES[r][j - 1]} | {np.mean(med[(r, j)]):.2f} | {np.mean(mx[(r, j)]):.2f} |")
+    span = float(np.mean(spans))
+    print()
+    print(f"calls: {args.phases} (layers cycled, a synchronisation between calls); constant clock {khz} kHz")
+    print(f"first workgroup start to last stamp: {span:.2f} us (mean over calls)")
+    print(f"back to back without stamps ({args.steps} steps x {layers} layers): {us_layer:.2f} us per layer; "
+          f"the difference, {us_layer - span:.2f} us, is the launch boundary, the dispatch ramp before the "
+          f"first start and the tail after the last stamp")
+
+
 def run_dense(args):
     """The dense fp8 block-128 projection: `copies` resident matrices of one
     shape (together beyond the on-package cache) applied in turn to the same
@@ -379,6 +465,10 @@ def main():
     ctx = moe.Ctx(0)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
+    if args.phases is not None:
+        run_phases(args, wl, res, moe, ctx, stream, layers)
+        ctx.close()
+        return
 
     def step():
         res.run(ctx, stream=stream, write_y=False)

@@ -24,6 +24,23 @@ extern "C" {
  * arguments (nothing enqueued). */
 MOE_API int moe_debug_decode(moe_ctx *ctx, int fmt, const void *codes, float *out, int n, void *stream);
 
+/* Phase stamps of the one-launch layer (diagnostics): while `stamps` is set
+ * (device, n_words 64-bit words; NULL or n_words 0 turns it off), every
+ * one-launch layer on this ctx writes, per workgroup b, 16 words at
+ * stamps[16 b]: word 0 the workgroup's role (0 router, 1 shared gate/up,
+ * 2 routed gate/up, 3 down) | slot << 8 | (a last arrival) << 16, and words
+ * 1..10 the device's constant clock (s_memrealtime) at its phase boundaries:
+ * 1 start; router: 2 row dot done, 3 arrival counted, 4 done word published
+ * (last of its sub-counter); gate/up: 2 routing ready seen, 3 top-k done,
+ * 4 h stored, 5 arrival counted; down: 2 routing ready seen, 3 top-k done,
+ * 4 down-row loads issued, 5 gate/up done words seen, 6 h staged, 7 blend
+ * stored, 8 group arrival returned, 9 group line cleared (last of its
+ * group); waiters: 10 the logits they select from arrived.  Words a role
+ * does not reach are left as they were.  A launch whose grid needs more than
+ * n_words fails (MOE_ERR_HIP, ctx lost).  *clock_khz (host, may be NULL)
+ * receives the constant clock's rate in kHz. */
+MOE_API int moe_debug_set_phase_stamps(moe_ctx *ctx, uint64_t *stamps, int64_t n_words, int64_t *clock_khz);
+
 #ifdef __cplusplus
 }
 #endif

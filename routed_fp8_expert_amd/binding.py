@@ -114,6 +114,7 @@ def lib():
                                         C.POINTER(RoutingC), vp, vp, i64, C.POINTER(NormC), vp, sz, vp], i32),
             "moe_dense_fp8": ([vp, C.POINTER(DenseWeightsC), vp, i32, i64, vp, i64, vp], i32),
             "moe_debug_decode": ([vp, i32, vp, vp, i32, vp], i32),
+            "moe_debug_set_phase_stamps": ([vp, vp, i64, C.POINTER(i64)], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -395,3 +396,12 @@ def moe_debug_decode(ctx: Ctx, fmt: int, codes: torch.Tensor, out: torch.Tensor,
                      stream=None) -> None:
     _check(lib().moe_debug_decode(ctx.handle, int(fmt), _p(codes), _p(out), codes.numel(),
                                   _stream(stream)), "moe_debug_decode")
+
+
+def moe_debug_set_phase_stamps(ctx: Ctx, stamps: Optional[torch.Tensor]) -> int:
+    """Phase stamps of the one-launch layer into an int64 device tensor (None:
+    off); returns the constant clock's rate in kHz."""
+    n = 0 if stamps is None else stamps.numel()
+    khz = C.c_int64(0)
+    _check(lib().moe_debug_set_phase_stamps(ctx.handle, _p(stamps), n, C.byref(khz)), "moe_debug_set_phase_stamps")
+    return int(khz.value)

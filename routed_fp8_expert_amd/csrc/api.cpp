@@ -71,6 +71,8 @@ struct moe_ctx {
     int slot = -1;               // the pool slot holding them
     int64_t clock_khz = 100000;  // the device's constant clock (s_memrealtime)
     int64_t wait_us = kDefaultWaitUs;
+    uint64_t *stamps = nullptr;  // diagnostics: phase stamps of the one-launch layer
+    int64_t stamp_words = 0;
     bool timing = false;
     std::vector<TimingRecord> recs;
     std::vector<hipEvent_t> spare;
@@ -464,7 +466,7 @@ uint64_t wait_ticks(const moe_ctx *c) { return (uint64_t)c->wait_us * (uint64_t)
 int do_layer_r1(moe_ctx *c, const moe::RouteArgs &r, moe::FfnArgs a, hipStream_t st) {
     if (c->one_row_path == 0 && moe::layer_r1_supported(r, a))
         return launch(c, MOE_K_LAYER, st, [&] {
-            return moe::launch_layer_r1(r, a, c->words + kWordLayerSync, wait_ticks(c), st);
+            return moe::launch_layer_r1(r, a, c->words + kWordLayerSync, wait_ticks(c), c->stamps, c->stamp_words, st);
         });
     int rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_lead_r1(r, a, st); });
     if (rc) return rc;
@@ -607,8 +609,7 @@ MOE_API int moe_ctx_device_errors(moe_ctx *c, uint32_t *flags, int clear) {
         if (hipMemset(c->words + kWordError, 0, sizeof(uint32_t)) != hipSuccess) return fail(c, MOE_ERR_HIP);
         // a wait that gave up may have left the one-launch layer's
         // synchronisation words inconsistent: nothing runs now, so zero them
-        if ((*flags & moe::kErrWaitTimeout) &&
-            hipMemset(c->words + kWordLayerSync, 0, sizeof(uint32_t) * kLayerSyncWords) != hipSuccess)
+        if ((*flags & moe::kErrWaitTimeout) && moe::ctx_layer_words_reset(c->words) != hipSuccess)
             return fail(c, MOE_ERR_HIP);
         if (hipDeviceSynchronize() != hipSuccess) return fail(c, MOE_ERR_HIP);
     }
@@ -806,6 +807,14 @@ MOE_API int moe_dense_fp8(moe_ctx *c, const moe_dense_weights *w, const void *x,
     a.R = R;
     const hipStream_t st = (hipStream_t)stream;
     return launch(c, MOE_K_DENSE, st, [&] { return moe::launch_dense(a, st); });
+}
+
+MOE_API int moe_debug_set_phase_stamps(moe_ctx *c, uint64_t *stamps, int64_t n_words, int64_t *clock_khz) {
+    if (!c || n_words < 0 || (stamps && !aligned(stamps, 8))) return MOE_ERR_INVALID_ARG;
+    c->stamps = n_words > 0 ? stamps : nullptr;
+    c->stamp_words = c->stamps ? n_words : 0;
+    if (clock_khz) *clock_khz = c->clock_khz;
+    return MOE_OK;
 }
 
 MOE_API int moe_debug_decode(moe_ctx *c, int fmt, const void *codes, float *out, int n, void *stream) {

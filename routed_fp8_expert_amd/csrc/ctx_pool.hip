@@ -53,6 +53,12 @@ hipError_t ctx_slot_acquire(int device, int *slot, uint32_t **words) {
     return hipSuccess;
 }
 
+hipError_t ctx_layer_words_reset(uint32_t *words) {
+    hipError_t e = hipMemset(words + kWordLayerSync, 0, sizeof(uint32_t) * kLayerSyncWords);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    return e;
+}
+
 void ctx_slot_release(int device, int slot) {
     std::lock_guard<std::mutex> lock(g_mu);
     if (device >= 0 && device < (int)g_pools.size() && slot >= 0 && slot < kMaxCtxPerDevice)

@@ -23,11 +23,10 @@ constexpr int kMaxSlots = kMaxTopK + 1;   // routed slots plus the shared expert
 // A ctx's synchronisation words (uint32, device memory of the ctx pool), in
 // groups that each start a 256-byte line: the router ticket of the one-row
 // lead kernel, the device error word, the cache-warming sink, the ticket of
-// the fused top-k + grouping launch, then the one-launch layer's lines
-// (layer.hip): a ticket, kReplicas ready-flag copies, a down-done counter,
-// one counter per slot, a slots-done counter and kReplicas h-ready copies.
+// the fused top-k + grouping launch, then the one-launch layer's words
+// (layer.hip: per-replica done-word lines and the arrival sub-counters).
 constexpr int kSyncLine = 64;   // words per 256-byte line
-constexpr int kLayerSyncWords = (3 + 2 * kReplicas + kMaxSlots) * kSyncLine;
+constexpr int kLayerSyncWords = 71 * kSyncLine;
 enum CtxWord : int {
     kWordRouterTicket = 0,
     kWordError = 1 * kSyncLine,
@@ -128,9 +127,12 @@ hipError_t launch_gate_up_r1(const FfnArgs &a, hipStream_t st);
 // kLayerSyncWords layer words, all zero between launches; a wait for another
 // workgroup gives up after `wait_ticks` ticks of the device's constant clock
 // (s_memrealtime).
+// `stamps` (diagnostics, or null): kStampWords words per workgroup of phase
+// timestamps; a launch needing more than `stamp_words` fails.
+constexpr int kStampWords = 16;
 bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a);
 hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync, uint64_t wait_ticks,
-                           hipStream_t st);
+                           uint64_t *stamps, int64_t stamp_words, hipStream_t st);
 hipError_t launch_down_blend_r1(const FfnArgs &a, hipStream_t st);
 hipError_t launch_down_grouped(const FfnArgs &a, hipStream_t st);
 hipError_t launch_blend(const FfnArgs &a, hipStream_t st);
@@ -140,10 +142,13 @@ hipError_t launch_dense(const DenseArgs &a, hipStream_t st);
 // The ctx pool (ctx_pool.hip): kMaxCtxPerDevice slots of kCtxWords words per
 // device in static device memory.  ctx_slot_acquire makes `device` current's
 // pool address known (hipGetSymbolAddress, once per device), takes a free
-// slot, zeroes it (synchronously) and returns its words; release frees it.
+// slot, resets it (synchronously) and returns its words; release frees it.
+// ctx_layer_words_reset returns a slot's layer words to their state between
+// launches (zero).
 constexpr int kMaxCtxPerDevice = 64;
 hipError_t ctx_slot_acquire(int device, int *slot, uint32_t **words);
 void ctx_slot_release(int device, int slot);
+hipError_t ctx_layer_words_reset(uint32_t *words);
 
 // The static workspace of moe_layer_forward_static (static_scratch.hip):
 // kStaticScratchBytes per device.  static_scratch_init resolves its address

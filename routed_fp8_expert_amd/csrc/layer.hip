@@ -52,68 +52,129 @@ namespace moe {
 
 constexpr int P1 = kPairsPerWave;
 
-// Synchronisation words, each on its own 256-byte line so pollers and
-// arrivals on different words do not share a memory channel; the ready flag
-// has kReadyCopies copies, polled by block index.
-constexpr int kLine = kSyncLine;
-constexpr int kReadyCopies = kReplicas;
+// Synchronisation words (kLayerSyncWords of the ctx, zero between launches).
+//
+// Every phase counts its workgroups on kGroups sub-counters (a workgroup
+// takes sub-counter slice % kGroups), so no counter sees more than a few
+// arrivals: arrivals at one address are serialised by the memory side
+// (about 14 ns each), which made one counter per phase cost microseconds.
+// The last arrival of a sub-counter resets it and writes its done word into
+// each of the kGroups replica lines; a waiting workgroup polls the line of
+// its replica group (block index % kGroups, its XCD) with one wave-wide load
+// per 64 words and a ballot over the done words it needs.  The down
+// workgroups count on a per-group counter once they have read every done
+// word they read; the last of group c clears replica line c.  (Polling the
+// logits themselves instead of a done word, with an unset pattern restored
+// after each launch, measured slower: 768 waves re-reading 1 KB each load
+// the memory side enough to delay the routing by 1.4 us.)
+//
+//   kSyncDone     kGroups replica lines of kDoneWords words:
+//                   [0, kGroups)                            router sub-counters done
+//                   [kDoneGu, kDoneGu + kMaxSlots*kGroups)  gate/up (slot, sub) done
+//   kSyncRouter   kGroups router sub-counters, kCtrWords apart
+//   kSyncGu       kMaxSlots * kGroups gate/up sub-counters
+//   kSyncDown     kGroups down counters (one per replica group)
+//   kSyncNorm     the norm epilogue's counter of finished groups
+constexpr int kGroups = kReplicas;
+constexpr int kCtrWords = 16;        // 64 bytes between counters
+constexpr int kDoneWords = 256;      // one replica line set (1 KB)
+constexpr int kDoneGu = 64;
 enum : int {
-    kSyncTicket = 0,
-    kSyncReady = 1 * kLine,                                // kReadyCopies lines
-    kSyncDownDone = (1 + kReadyCopies) * kLine,
-    kSyncSlot0 = (2 + kReadyCopies) * kLine,               // kMaxSlots lines
-    kSyncSlotsDone = (2 + kReadyCopies + kMaxSlots) * kLine,
-    kSyncHReady = (3 + kReadyCopies + kMaxSlots) * kLine,  // kReadyCopies lines
-    kSyncWordsTotal = (3 + 2 * kReadyCopies + kMaxSlots) * kLine
+    kSyncDone = 0,
+    kSyncRouter = kSyncDone + kGroups * kDoneWords,
+    kSyncGu = kSyncRouter + kGroups * kCtrWords,
+    kSyncDown = kSyncGu + kMaxSlots * kGroups * kCtrWords,
+    kSyncNorm = kSyncDown + kGroups * kCtrWords,
+    kSyncWordsTotal = kSyncNorm + kCtrWords
 };
-static_assert(kSyncWordsTotal == kLayerSyncWords, "layer synchronisation words and the ctx layout disagree");
+static_assert(kDoneGu + kMaxSlots * kGroups <= kDoneWords, "done words of one replica");
+static_assert(kSyncWordsTotal <= kLayerSyncWords, "layer synchronisation words exceed the ctx layout");
 
-// True once *p >= target; false once `ticks` ticks of the constant clock
-// have passed since the first poll (at least one poll is made).
-__device__ __forceinline__ bool poll_geq(const unsigned *p, unsigned target, uint64_t ticks) {
+// Arrivals of sub-counter `sub` when `total` workgroups count round-robin.
+__host__ __device__ constexpr unsigned group_count(int total, int sub) {
+    return total > sub ? (unsigned)((total - sub + kGroups - 1) / kGroups) : 0u;
+}
+
+// Wave-wide poll of NC lines of 64 done words at p: true once every word
+// c * 64 + lane with need[c] set in that lane is non-zero; false once
+// `ticks` ticks of the constant clock have passed since the first poll (at
+// least one poll is made).  Every lane of the wave calls it.
+template <int NC>
+__device__ __forceinline__ bool poll_words(const unsigned *p, const bool (&need)[NC], uint64_t ticks) {
+    const int lane = threadIdx.x & (kWave - 1);
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     for (;;) {
-        if (ld_agent(p) >= target) return true;
+        unsigned v[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) v[c] = ld_agent(p + c * kWave + lane);
+        bool missing = false;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) missing |= need[c] && v[c] == 0u;
+        if (__builtin_amdgcn_ballot_w64(missing) == 0) return true;
         if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) return false;
-        __builtin_amdgcn_s_sleep(4);
+        __builtin_amdgcn_s_sleep(2);
     }
 }
 
-// Every thread of the block calls this; thread 0 polls, the block waits at
-// the barrier.  A timeout sets the error word.
-__device__ __forceinline__ void block_wait(const unsigned *p, unsigned target, uint32_t *err, uint64_t ticks) {
-    if (threadIdx.x == 0 && !poll_geq(p, target, ticks)) flag_error(err, kErrWaitTimeout);
+// Every thread of the block calls this; wave 0 polls, the block waits at the
+// barrier.  A timeout sets the error word.
+template <int NC>
+__device__ __forceinline__ void block_wait_words(const unsigned *p, const bool (&need)[NC], uint32_t *err,
+                                                 uint64_t ticks) {
+    if ((threadIdx.x >> 6) == 0 && !poll_words<NC>(p, need, ticks) && threadIdx.x == 0)
+        flag_error(err, kErrWaitTimeout);
     __syncthreads();
 }
 
-// Count this block done on `ctr` once all its waves' stores have completed.
-__device__ __forceinline__ unsigned block_arrive(unsigned *ctr, unsigned *ticket_s) {
+// Count this block on `ctr` (of `n` arrivals) once all its waves' stores
+// have completed; the last arrival resets the counter (nobody else touches
+// it in this launch) and returns true in every thread.
+__device__ __forceinline__ bool block_arrive_last(unsigned *ctr, unsigned n, unsigned *ticket_s) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0)
-        *ticket_s = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+        const unsigned t = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == n - 1) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *ticket_s = t;
+    }
     __syncthreads();
-    return *ticket_s;
+    return *ticket_s == n - 1;
 }
 
-// A gate/up block is done with its slot: the last block of the slot counts
-// the slot done, and the last slot raises the h-ready flag (all copies).
-// Nobody polls the counters themselves, only the flag copies.
-__device__ __forceinline__ void slot_done(unsigned *sync, int slot, int blocks_per_slot, int nslots,
-                                          unsigned *ticket_s) {
-    if (block_arrive(sync + kSyncSlot0 + slot * kLine, ticket_s) != (unsigned)(blocks_per_slot - 1)) return;
-    if (threadIdx.x == 0)
-        *ticket_s = __hip_atomic_fetch_add(sync + kSyncSlotsDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (*ticket_s == (unsigned)(nslots - 1) && threadIdx.x < kReadyCopies)
-        __hip_atomic_store(sync + kSyncHReady + threadIdx.x * kLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Done word `word` of every replica line set (threads 0 .. kGroups-1).
+__device__ __forceinline__ void publish_done(unsigned *sync, int word) {
+    if (threadIdx.x < kGroups)
+        __hip_atomic_store(sync + kSyncDone + threadIdx.x * kDoneWords + word, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 struct LayerGrid {
     int nrb, nsb, ngb, ndb;   // router, shared gate/up, routed gate/up per slot, down blocks
     unsigned *sync;           // kSyncWordsTotal words
     uint64_t wait_ticks;      // a wait's deadline, in ticks of the constant clock
+    uint64_t *stamps;         // diagnostics: kStampWords words per workgroup, or null
 };
+
+// Diagnostics (phase stamps): thread 0 of each workgroup records the constant
+// clock at its phase boundaries in stamps[block * kStampWords + i]; word 0
+// holds the role (0 router, 1 shared gate/up, 2 routed gate/up, 3 down), the
+// slot << 8 and, for a last arrival (router sub-counter, down group), 1 << 16.
+//   1 start
+//   2 router: row dot done; waiters: the routing's done words seen
+//   3 router: arrival counted; waiters: top-k done
+//   4 router (last of its sub-counter): done word published; gate/up: h
+//     computed and stored; down: down-row loads issued
+//   5 gate/up: arrival counted; down: the gate/up done words seen
+//   6 down: h staged in LDS     7 down: blend stored
+//   8 down: its group arrival returned
+//   9 down (last of its group): the group's line cleared
+//  10 waiters: the logits they select from have arrived
+__device__ __forceinline__ void stamp(const LayerGrid &g, int i) {
+    if (g.stamps && threadIdx.x == 0) g.stamps[(size_t)blockIdx.x * kStampWords + i] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void stamp_role(const LayerGrid &g, uint64_t tag) {
+    if (g.stamps && threadIdx.x == 0) g.stamps[(size_t)blockIdx.x * kStampWords] = tag;
+}
 
 // h of every slot into LDS, read coherently (8-byte agent-scope loads, all
 // of them issued before any is used) from one replica, and stored in
@@ -147,12 +208,26 @@ __device__ __forceinline__ void stage_h(const float *h, int nslots, float *hl) {
 // LDS.  Every waiting workgroup computes the same result from the same
 // logits, which saves publishing it (a store and a load round trip).
 template <int NV>
-__device__ __forceinline__ void block_topk(const RouteArgs &r, const float *lrep, int *ids_s, float *w_s) {
+__device__ __forceinline__ void block_topk(const RouteArgs &r, const float *lrep, int *ids_s, float *w_s,
+                                           const LayerGrid &g) {
     if ((threadIdx.x >> 6) == 0) {
         const int lane = threadIdx.x & (kWave - 1);
+        const float *l = r.logits_in ? r.logits_in : lrep;
+        const bool coherent = r.logits_in == nullptr;
+        float raw[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + kWave * i;
+            const int ec = e < r.E ? e : r.E - 1;
+            raw[i] = coherent ? ld_agent(l + ec) : l[ec];
+        }
+        if (g.stamps) {
+            __builtin_amdgcn_s_waitcnt(0);
+            stamp(g, 10);
+        }
         int e;
         float w;
-        topk_wave<NV>(r.logits_in ? r.logits_in : lrep, r.E, r.k, r.logits_in == nullptr, e, w);
+        topk_regs<NV>(raw, r.E, r.k, e, w);
         if (lane < r.k) {
             ids_s[lane] = e;
             w_s[lane] = w;
@@ -165,6 +240,7 @@ template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
 __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerGrid g) {
     // gate/up chunks per lane follow from the router's: H/1024 (fp8), H/2048 (nvfp4)
     constexpr int CH = byte_codes(FMT) ? (NCH + 1) / 2 : (NCH + 3) / 4;
+    constexpr int NCG = (KS * kGroups + kWave - 1) / kWave;   // lines of gate/up done words
     extern __shared__ f32x4 hlds4[];
     __shared__ unsigned ticket_s;
     __shared__ int ids_s[kMaxSlots];
@@ -175,12 +251,16 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     const int k = a.k;
     const bool has_shared = a.shared.inter > 0;
     const int rep_id = blockIdx.x % kReplicas;
-    const unsigned *ready = sync + kSyncReady + rep_id * kLine;
+    const unsigned *done = sync + kSyncDone + rep_id * kDoneWords;   // this group's replica line
     const float *lrep = a.logits_rep + (size_t)rep_id * r.E;
     const size_t hrep_stride = (size_t)(k + (has_shared ? 1 : 0)) * a.hstride;
+    // the routing is ready once every router sub-counter that has arrivals is done
+    const bool need_router[1] = {lane < kGroups && lane < g.nrb};
+    stamp(g, 1);
 
     // ---------------------------------------------------------------- router
     if (b < g.nrb) {
+        stamp_role(g, 0);
         const int n_router = r.logits_in ? 0 : r.E;
         const int n_rows = n_router + (r.wsg ? 1 : 0);
         if (!r.wsg && b == 0 && threadIdx.x == 0) st_agent(r.s, 1.0f);
@@ -198,12 +278,15 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
                 if (lane == kReplicas) r.logits[row] = l;
             }
         }
-        // every router block's stores are complete before its ticket, so the
-        // last one can raise the ready flag at once
-        if (block_arrive(sync + kSyncTicket, &ticket_s) == (unsigned)(g.nrb - 1) && wid == 0) {
-            if (lane == 0) __hip_atomic_store(sync + kSyncTicket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (lane < kReadyCopies)
-                __hip_atomic_store(sync + kSyncReady + lane * kLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        stamp(g, 2);
+        // every router block's stores are complete before it counts itself
+        const int sub = b % kGroups;
+        const bool last = block_arrive_last(sync + kSyncRouter + sub * kCtrWords, group_count(g.nrb, sub), &ticket_s);
+        stamp(g, 3);
+        if (last) {
+            publish_done(sync, sub);
+            stamp_role(g, 1u << 16);
+            stamp(g, 4);
         }
         return;
     }
@@ -211,6 +294,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
 
     // ---------------------------------------------------------------- shared gate/up
     if (b < g.nsb) {
+        stamp_role(g, 1 | ((uint64_t)k << 8));
         const ExpertSet &X = a.shared;
         const int i0 = (b * 4 + wid) * P1;
         if (i0 < X.inter) {
@@ -219,7 +303,11 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
             rows.template apply<true>(a.x, a.H, X.inter, i0, a.h_rep + (size_t)k * a.hstride, hrep_stride,
                                       kReplicas);
         }
-        slot_done(sync, k, g.nsb, k + 1, &ticket_s);
+        stamp(g, 4);
+        const int sub = b % kGroups;
+        if (block_arrive_last(sync + kSyncGu + (k * kGroups + sub) * kCtrWords, group_count(g.nsb, sub), &ticket_s))
+            publish_done(sync, kDoneGu + k * kGroups + sub);
+        stamp(g, 5);
         return;
     }
     b -= g.nsb;
@@ -227,8 +315,11 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     // ---------------------------------------------------------------- routed gate/up
     if (b < k * g.ngb) {
         const int slot = b % k, slice = b / k;
-        block_wait(ready, 1u, a.err, g.wait_ticks);
-        block_topk<NV>(r, lrep, ids_s, w_s);
+        stamp_role(g, 2 | ((uint64_t)slot << 8));
+        block_wait_words<1>(done, need_router, a.err, g.wait_ticks);
+        stamp(g, 2);
+        block_topk<NV>(r, lrep, ids_s, w_s, g);
+        stamp(g, 3);
         const int e = ids_s[slot];
         const ExpertSet &X = a.routed;
         const int i0 = (slice * 4 + wid) * P1;
@@ -238,7 +329,12 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
             rows.template apply<true>(a.x, a.H, X.inter, i0, a.h_rep + (size_t)slot * a.hstride, hrep_stride,
                                       kReplicas);
         }
-        slot_done(sync, slot, g.ngb, k + (has_shared ? 1 : 0), &ticket_s);
+        stamp(g, 4);
+        const int sub = slice % kGroups;
+        if (block_arrive_last(sync + kSyncGu + (slot * kGroups + sub) * kCtrWords, group_count(g.ngb, sub),
+                              &ticket_s))
+            publish_done(sync, kDoneGu + slot * kGroups + sub);
+        stamp(g, 5);
         return;
     }
     b -= k * g.ngb;
@@ -249,8 +345,11 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     const int o = (b * 4 + wid) * RPW + lane / LPR;
     const bool live = o < a.H;
     const int nslots = k + (has_shared ? 1 : 0);
-    block_wait(ready, 1u, a.err, g.wait_ticks);
-    block_topk<NV>(r, lrep, ids_s, w_s);
+    stamp_role(g, 3);
+    block_wait_words<1>(done, need_router, a.err, g.wait_ticks);
+    stamp(g, 2);
+    block_topk<NV>(r, lrep, ids_s, w_s, g);
+    stamp(g, 3);
     if (b == 0 && wid == 0 && lane < k) {
         r.ids[lane] = ids_s[lane];
         r.w[lane] = w_s[lane];
@@ -265,11 +364,32 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     }
     const float s_gate = has_shared ? ld_agent(a.s) : 0.0f;
     const float res_in = a.res ? bf16_to_f32(a.res[live ? o : 0]) : 0.0f;   // unconditional load (clamped)
-    // every slot's h is complete once the h-ready flag is up
-    block_wait(sync + kSyncHReady + rep_id * kLine, 1u, a.err, g.wait_ticks);
+    stamp(g, 4);
+    // every slot's h is complete once every (slot, sub-counter) with arrivals is done
+    bool need_gu[NCG];
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) {
+        const int w = c * kWave + lane, slot = w / kGroups, gsub = w % kGroups;
+        need_gu[c] = slot < nslots && gsub < (slot == k ? g.nsb : g.ngb);
+    }
+    block_wait_words<NCG>(done + kDoneGu, need_gu, a.err, g.wait_ticks);
+    stamp(g, 5);
     stage_h<cols_per_chunk<FMT>(), HS, KS>(a.h_rep + (size_t)rep_id * hrep_stride, nslots,
                                            reinterpret_cast<float *>(hlds4));
     __syncthreads();
+    // Without the norm epilogue the block counts itself on its group's
+    // counter now: it has read every done word it reads (and every gate/up
+    // block counted itself before its word was set).  The atomic's latency
+    // hides behind the blend; the last block of the group clears the group's
+    // replica line at the end.  With the epilogue the count comes after the
+    // outputs are stored (below).
+    const int dsub = b % kGroups;
+    const unsigned n_down = group_count(g.ndb, dsub);
+    unsigned *down_ctr = sync + kSyncDown + rep_id * kCtrWords;
+    unsigned early = 0;
+    if (!a.norm_w && threadIdx.x == 0)
+        early = __hip_atomic_fetch_add(down_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stamp(g, 6);
     const float *hbase = reinterpret_cast<const float *>(hlds4);
     float y = 0.0f;
     if (has_shared && k == KS - 1) {
@@ -308,23 +428,34 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
             if (a.res) a.res[o] = rb;
         }
     }
-    const bool last = block_arrive(sync + kSyncDownDone, &ticket_s) == (unsigned)(g.ndb - 1);
-    if (last && a.norm_w) {
+    stamp(g, 7);
+    bool group_last;
+    if (a.norm_w) {
+        group_last = block_arrive_last(down_ctr, n_down, &ticket_s);
+    } else {
+        // wave 0 learns from thread 0 whether this block was its group's last
+        group_last = wid == 0 && (unsigned)__builtin_amdgcn_readfirstlane((int)early) == n_down - 1;
+        if (group_last && lane == 0) __hip_atomic_store(down_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    stamp(g, 8);
+    if (group_last && wid == 0) {
+        // nobody reads this group's replica line any more in this launch
+        unsigned *line = sync + kSyncDone + rep_id * kDoneWords;
+        if (lane < kGroups) __hip_atomic_store(line + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int c = 0; c < NCG; ++c)
+            if (c * kWave + lane < kMaxSlots * kGroups)
+                __hip_atomic_store(line + kDoneGu + c * kWave + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        stamp_role(g, 3 | (1u << 16));
+        stamp(g, 9);
+    }
+    if (a.norm_w && group_last &&
+        block_arrive_last(sync + kSyncNorm, (unsigned)(g.ndb < kGroups ? g.ndb : kGroups), &ticket_s)) {
         // RMSNorm epilogue of the row (the residual after the add, else y):
-        // every down workgroup's stores completed before its arrival
+        // every down workgroup's stores completed before its group counted it
         float *vrow = reinterpret_cast<float *>(hlds4);
         stage_row<true>(a.res ? a.res : a.y, a.H, vrow);
         block_rms_norm(vrow, a.H, a.norm_w, a.norm_eps, a.norm_out);
-    }
-    if (last && threadIdx.x == 0) {
-        for (int c = 0; c < kReadyCopies; ++c) {
-            __hip_atomic_store(sync + kSyncReady + c * kLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(sync + kSyncHReady + c * kLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __hip_atomic_store(sync + kSyncSlotsDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int j = 0; j < kMaxSlots; ++j)
-            __hip_atomic_store(sync + kSyncSlot0 + j * kLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sync + kSyncDownDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -349,7 +480,8 @@ static LayerShape layer_shape(const RouteArgs &r, const FfnArgs &a) {
     return s;
 }
 
-static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, unsigned *sync, uint64_t wait_ticks = 0) {
+static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, unsigned *sync, uint64_t wait_ticks = 0,
+                            uint64_t *stamps = nullptr) {
     LayerGrid g;
     const int n_rows = (r.logits_in ? 0 : r.E) + (r.wsg ? 1 : 0);
     g.nrb = n_rows > 0 ? (n_rows + 3) / 4 : 1;
@@ -359,6 +491,7 @@ static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, unsig
     g.ndb = (a.H + rows_per_block - 1) / rows_per_block;
     g.sync = sync;
     g.wait_ticks = wait_ticks;
+    g.stamps = stamps;
     return g;
 }
 static int layer_blocks(const LayerGrid &g, const FfnArgs &a) { return g.nrb + g.nsb + a.k * g.ngb + g.ndb; }
@@ -370,8 +503,9 @@ static size_t layer_lds(const FfnArgs &a) {
 
 template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
 static hipError_t layer_launch(const RouteArgs &r, const FfnArgs &a, unsigned *sync, uint64_t wait_ticks,
-                               hipStream_t st) {
-    const LayerGrid g = layer_grid(r, a, LPR, sync, wait_ticks);
+                               uint64_t *stamps, int64_t stamp_words, hipStream_t st) {
+    const LayerGrid g = layer_grid(r, a, LPR, sync, wait_ticks, stamps);
+    if (stamps && (int64_t)layer_blocks(g, a) * kStampWords > stamp_words) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_layer_r1<FMT, NCH, NV, LPR, DCH, KS, HS>), dim3(layer_blocks(g, a)), dim3(256),
                        layer_lds(a), st, r, a, g);
     return hipGetLastError();
@@ -428,6 +562,9 @@ bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
     if (layer_lds(a) > kLayerMaxHLds || (a.hstride & 1)) return false;
     const LayerShape s = layer_shape(r, a);
+    // every replica group needs a down workgroup: its last one clears the
+    // group's done words
+    if (layer_grid(r, a, s.lpr, nullptr).ndb < kGroups) return false;
 #define MOE_MATCH(F, N, V, L, D, K, HSV)                                                               \
     if (s.fmt == F && s.nch == N && s.nv == V && s.lpr == L && s.dch == D && nslots <= K &&              \
         a.routed.inter == HSV && (a.shared.inter == 0 || a.shared.inter == HSV))                          \
@@ -438,13 +575,13 @@ bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
 }
 
 hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync, uint64_t wait_ticks,
-                           hipStream_t st) {
+                           uint64_t *stamps, int64_t stamp_words, hipStream_t st) {
     const LayerShape s = layer_shape(r, a);
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
 #define MOE_GO(F, N, V, L, D, K, HSV)                                                                  \
     if (s.fmt == F && s.nch == N && s.nv == V && s.lpr == L && s.dch == D && nslots <= K &&              \
         a.routed.inter == HSV && (a.shared.inter == 0 || a.shared.inter == HSV))                          \
-        return layer_launch<F, N, V, L, D, K, HSV>(r, a, sync, wait_ticks, st);
+        return layer_launch<F, N, V, L, D, K, HSV>(r, a, sync, wait_ticks, stamps, stamp_words, st);
     MOE_LAYER_SHAPES(MOE_GO)
 #undef MOE_GO
     return hipErrorInvalidValue;
