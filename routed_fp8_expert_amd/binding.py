@@ -14,7 +14,8 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ffn.so")
+# The in-tree build; MOE_LIBRARY names another build of the same sources.
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ffn.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
