@@ -36,7 +36,9 @@ MOE_API int moe_debug_decode(moe_ctx *ctx, int fmt, const void *codes, float *ou
  * 4 down-row loads issued, 5 gate/up done words seen, 6 h staged, 7 blend
  * stored, 8 group arrival returned, 9 group line cleared (last of its
  * group); waiters: 10 the logits they select from arrived.  Words a role
- * does not reach are left as they were.  A launch whose grid needs more than
+ * does not reach read all ones (0xffffffffffffffff).  The stamps are kept in
+ * the workgroup's LDS and written out as it ends, so no barrier waits for
+ * them.  A launch whose grid needs more than
  * n_words fails (MOE_ERR_HIP, ctx lost).  *clock_khz (host, may be NULL)
  * receives the constant clock's rate in kHz. */
 MOE_API int moe_debug_set_phase_stamps(moe_ctx *ctx, uint64_t *stamps, int64_t n_words, int64_t *clock_khz);

@@ -8,6 +8,8 @@
 #include "device.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace moe {
 
 
@@ -123,26 +125,40 @@ __device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
-// Softmax over the E logits of one row, the k largest under the top-k order
-// (larger value first, lower index first among equal values) and their
-// renormalised weights, by one wave.  Each lane holds NV logits (experts
-// lane, lane+64, ...) sorted once; every round the wave takes the largest
-// lane head by a 32-bit wave max, the lane holding it (the lowest expert
-// index among equal heads: a second, rarely taken pass) pops its head.
-// w_j = exp(l_j - m) / sum_j exp(l_j - m), m the largest logit: the softmax
-// denominator over all E cancels in the renormalisation.  Lane j < k returns
-// slot j.  raw[i] is the logit of expert lane + 64 i (entries past E unused).
+// Per lane: b where bit `lane` of the wave mask m is set, else a.  (Chains
+// of selects on one lane-index test compile into longer code than these
+// mask tests.)
+__device__ __forceinline__ uint32_t lane_select(uint32_t a, uint32_t b, uint64_t m) {
+    return ((m >> (threadIdx.x & (kWave - 1))) & 1ull) ? b : a;
+}
+
+// Largest unsigned value of the wave, uniform: DPP row stages, the two row
+// broadcasts carry it into lane 63, which is read out.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    v = mx(v, (uint32_t)dpp<kDppXor1>(0, (int)v));
+    v = mx(v, (uint32_t)dpp<kDppXor2>(0, (int)v));
+    v = mx(v, (uint32_t)dpp<kDppHalfMirror>(0, (int)v));
+    v = mx(v, (uint32_t)dpp<kDppMirror>(0, (int)v));
+    v = mx(v, (uint32_t)dpp<kDppBcast15, 0xa>(0, (int)v));
+    v = mx(v, (uint32_t)dpp<kDppBcast31, 0xc>(0, (int)v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+// The k largest of the wave's keys (key[i] of lane l: expert l + 64 i, key
+// 0 for none) under the top-k order, by rounds: each lane's keys sorted
+// once, stable, with their positions packed four bits each into `perm`;
+// every round the wave takes the largest lane head by a 32-bit wave max, the
+// lane holding it (the lowest expert index among equal heads: a second,
+// rarely taken pass) pops its head.  Lane j < k gets round j's key and
+// expert.  The general path of topk_regs (any number of ties).
 template <int NV>
-__device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, int &my_e, float &my_w) {
+__device__ __forceinline__ void topk_rounds(uint32_t (&key)[NV], int k, int &sel_key, int &sel_idx) {
+    using Perm = typename std::conditional<(NV <= 8), uint32_t, uint64_t>::type;
     const int lane = threadIdx.x & (kWave - 1);
-    uint32_t key[NV];
-    int idx[NV];
+    int pos[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = lane + kWave * i;
-        key[i] = e < E ? logit_key(raw[i]) : 0u;
-        idx[i] = e;
-    }
+    for (int i = 0; i < NV; ++i) pos[i] = i;
     // stable sort by key, descending: equal keys keep ascending index
 #pragma unroll
     for (int i = 1; i < NV; ++i) {
@@ -150,35 +166,138 @@ __device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, 
         for (int j = i; j > 0; --j) {
             const bool sw = key[j] > key[j - 1];
             const uint32_t ka = key[j - 1], kb = key[j];
-            const int ia = idx[j - 1], ib = idx[j];
+            const int ia = pos[j - 1], ib = pos[j];
             key[j - 1] = sw ? kb : ka;
             key[j] = sw ? ka : kb;
-            idx[j - 1] = sw ? ib : ia;
-            idx[j] = sw ? ia : ib;
+            pos[j - 1] = sw ? ib : ia;
+            pos[j] = sw ? ia : ib;
         }
     }
-    uint32_t sel_key = 0;
-    int sel_idx = 0;
+    Perm perm = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) perm |= (Perm)pos[i] << (4 * i);
+    sel_key = 0;
+    sel_idx = 0;
     for (int j = 0; j < k; ++j) {
-        const uint32_t best = wave_ext_u32<true>(key[0]);
+        const uint32_t best = wave_max_u32(key[0]);
         uint64_t hit = __builtin_amdgcn_ballot_w64(key[0] == best);
         if (__builtin_popcountll(hit) > 1) {
-            const uint32_t least = wave_ext_u32<false>(key[0] == best ? (uint32_t)idx[0] : 0xffffffffu);
-            hit = __builtin_amdgcn_ballot_w64(key[0] == best && (uint32_t)idx[0] == least);
+            const uint32_t head = (uint32_t)lane + kWave * (uint32_t)(perm & 15);
+            const uint32_t least = wave_ext_u32<false>(key[0] == best ? head : 0xffffffffu);
+            hit = __builtin_amdgcn_ballot_w64(key[0] == best && head == least);
         }
         const int wl = __builtin_ctzll(hit);
-        const int bi = __builtin_amdgcn_readlane(idx[0], wl);
-        const bool pop = lane == wl;
+        const int bi = wl + kWave * (__builtin_amdgcn_readlane((int)(uint32_t)perm, wl) & 15);
+        // lane wl pops its head; lane j takes the round's key and expert
+        const uint64_t pop = 1ull << wl, put = 1ull << j;
+        key[0] = lane == wl ? (NV > 1 ? key[1] : 0u) : key[0];
 #pragma unroll
-        for (int i = 0; i + 1 < NV; ++i) {
-            key[i] = pop ? key[i + 1] : key[i];
-            idx[i] = pop ? idx[i + 1] : idx[i];
+        for (int i = 1; i + 1 < NV; ++i) key[i] = lane_select(key[i], key[i + 1], pop);
+        if constexpr (NV > 1) key[NV - 1] = lane_select(key[NV - 1], 0u, pop);
+        if constexpr (NV > 1) {
+            if constexpr (NV <= 8) {
+                perm = lane_select((uint32_t)perm, (uint32_t)perm >> 4, pop);
+            } else {
+                const Perm sh = perm >> 4;
+                perm = (Perm)lane_select((uint32_t)perm, (uint32_t)sh, pop) |
+                       ((Perm)lane_select((uint32_t)(perm >> 32), (uint32_t)(sh >> 32), pop) << 32);
+            }
         }
-        key[NV - 1] = pop ? 0u : key[NV - 1];
-        sel_key = lane == j ? best : sel_key;
-        sel_idx = lane == j ? bi : sel_idx;
+        sel_key = (int)lane_select((uint32_t)sel_key, best, put);
+        sel_idx = (int)lane_select((uint32_t)sel_idx, (uint32_t)bi, put);
     }
-    const float v = key_logit(sel_key);
+}
+
+// Lanes below bit `lane` set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Softmax over the E logits of one row, the k largest under the top-k order
+// (larger value first, lower index first among equal values) and their
+// renormalised weights, by one wave (all 64 lanes active).
+//
+// Selection: split the lanes into G >= k groups and take T, the smallest of
+// the G group maxima.  Those are G distinct experts with keys >= T, so the
+// k-th largest key is >= T and every expert of the top-k is a candidate
+// (key >= T).  The candidates (usually a few times k) are packed into lanes
+// 0 .. C-1 by lane permutes; each one's rank is the number of candidates that
+// precede it in the top-k order (larger key, or equal key and lower expert),
+// counted against every candidate in turn, and a last permute puts rank j in
+// lane j.  More than 64 candidates (mass ties) take the round-by-round path.
+// w_j = exp(l_j - m) / sum_j exp(l_j - m), m the largest logit: the softmax
+// denominator over all E cancels in the renormalisation.  Lane j < k returns
+// slot j.  raw[i] is the logit of expert lane + 64 i (entries past E unused).
+template <int NV>
+__device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, int &my_e, float &my_w) {
+    static_assert(NV >= 1 && NV <= 16, "logits per lane");
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t key[NV];
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        key[i] = e < E ? logit_key(raw[i]) : 0u;
+        lmax = key[i] > lmax ? key[i] : lmax;
+    }
+    // group maxima (8 lanes a group for k <= 8, else 4), then their minimum
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+    uint32_t g = lmax;
+    g = mx(g, (uint32_t)dpp<kDppXor1>(0, (int)g));
+    g = mx(g, (uint32_t)dpp<kDppXor2>(0, (int)g));
+    if (k <= 8) {
+        g = mx(g, (uint32_t)dpp<kDppHalfMirror>(0, (int)g));
+    } else {
+        g = mn(g, (uint32_t)dpp<kDppHalfMirror>(-1, (int)g));
+    }
+    g = mn(g, (uint32_t)dpp<kDppMirror>(-1, (int)g));
+    g = mn(g, (uint32_t)dpp<kDppBcast15, 0xa>(-1, (int)g));
+    g = mn(g, (uint32_t)dpp<kDppBcast31, 0xc>(-1, (int)g));
+    const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)g, kWave - 1);
+    uint64_t cm[NV];
+    int cn = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        cm[i] = __builtin_amdgcn_ballot_w64(key[i] >= thr && key[i] != 0u);
+        cn += __builtin_popcountll(cm[i]);
+    }
+    int sel_key, sel_idx;
+    if (cn <= kWave) {
+        // pack the candidates into lanes 0 .. cn-1 (each permute a bijection
+        // of the lanes: non-candidates fill the lanes past its range)
+        uint32_t ck = 0, ci = 0;
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int cnt = __builtin_popcountll(cm[i]);
+            const int below = lanes_below(cm[i]);
+            const bool cand = (cm[i] >> lane) & 1ull;
+            const int dest = cand ? base + below : (base + cnt + (lane - below)) & (kWave - 1);
+            const uint32_t pk = (uint32_t)__builtin_amdgcn_ds_permute(dest * 4, (int)key[i]);
+            const uint32_t pi = (uint32_t)__builtin_amdgcn_ds_permute(dest * 4, lane + kWave * i);
+            const bool mine = (unsigned)(lane - base) < (unsigned)cnt;
+            ck = mine ? pk : ck;
+            ci = mine ? pi : ci;
+            base += cnt;
+        }
+        // rank: candidates ahead of this one (64-bit order key: key, then
+        // the complemented expert index)
+        const uint64_t kp = ((uint64_t)ck << 32) | (uint32_t)~ci;
+        int rank = 0;
+#pragma unroll 4
+        for (int q = 0; q < cn; ++q) {
+            const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)ck, q);
+            const uint32_t iq = (uint32_t)__builtin_amdgcn_readlane((int)ci, q);
+            rank += (((uint64_t)kq << 32) | (uint32_t)~iq) > kp ? 1 : 0;
+        }
+        const int dest = lane < cn ? rank : lane;
+        sel_key = __builtin_amdgcn_ds_permute(dest * 4, (int)ck);
+        sel_idx = __builtin_amdgcn_ds_permute(dest * 4, (int)ci);
+    } else {
+        topk_rounds<NV>(key, k, sel_key, sel_idx);
+    }
+    const float v = key_logit((uint32_t)sel_key);
     const float m = readlane(v, 0);
     const float ex = lane < k ? expf(v - m) : 0.0f;
     const float sum = group_sum<kWave>(ex);
@@ -213,35 +332,38 @@ constexpr int kNormBatch = 8;
 
 // out[o] = bf16(v[o] * rsqrt(mean v^2 + eps) * gamma[o]) for one row whose
 // f32 values v (already bf16-rounded) are in LDS, with room for H more
-// floats after them (the weight is staged there); every thread of the
-// 256-thread block calls it.  The sum of squares runs in a fixed order (per
-// thread over its columns, the wave sum, then the four waves in order), so
-// the result does not depend on timing.
+// floats after them (the weight is staged there); every thread of the block
+// (256 to 1024 threads) calls it.  The sum of squares runs in one fixed order
+// whatever the block size: threads 0..255 each over the columns t, t + 256,
+// ..., the wave sum, then the four waves in order (further waves add zero),
+// so the result does not depend on timing or on the calling kernel.
 __device__ __forceinline__ void block_rms_norm(float *v, int H, const uint16_t *gamma, float eps, uint16_t *out) {
-    __shared__ float part[4];
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+    __shared__ float part[16];
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6, nt = blockDim.x;
     float *gs = v + H;
-    for (int o0 = threadIdx.x; o0 < H; o0 += 256 * kNormBatch) {
+    for (int o0 = threadIdx.x; o0 < H; o0 += nt * kNormBatch) {
         uint16_t t[kNormBatch];
 #pragma unroll
         for (int u = 0; u < kNormBatch; ++u) {
-            const int o = o0 + 256 * u;
+            const int o = o0 + nt * u;
             t[u] = gamma[o < H ? o : H - 1];
         }
 #pragma unroll
         for (int u = 0; u < kNormBatch; ++u) {
-            const int o = o0 + 256 * u;
+            const int o = o0 + nt * u;
             if (o < H) gs[o] = bf16_to_f32(t[u]);
         }
     }
     float ss = 0.0f;
-    for (int o = threadIdx.x; o < H; o += 256) ss = fmaf(v[o], v[o], ss);
+    if (threadIdx.x < 256)
+        for (int o = threadIdx.x; o < H; o += 256) ss = fmaf(v[o], v[o], ss);
     ss = group_sum<kWave>(ss);
     if (lane == 0) part[wid] = ss;
     __syncthreads();
-    const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+    float tot = ((part[0] + part[1]) + part[2]) + part[3];
+    for (int w = 4; w < nt / kWave; ++w) tot += part[w];
     const float r = 1.0f / sqrtf(tot / (float)H + eps);
-    for (int o = threadIdx.x; o < H; o += 256) out[o] = f32_to_bf16(v[o] * r * gs[o]);
+    for (int o = threadIdx.x; o < H; o += nt) out[o] = f32_to_bf16(v[o] * r * gs[o]);
     __syncthreads();
 }
 
@@ -249,11 +371,12 @@ __device__ __forceinline__ void block_rms_norm(float *v, int H, const uint16_t *
 // (COHERENT: agent-scope loads of values other workgroups of the launch wrote).
 template <bool COHERENT>
 __device__ __forceinline__ void stage_row(const uint16_t *src, int H, float *v) {
-    for (int o0 = threadIdx.x; o0 < H; o0 += 256 * kNormBatch) {
+    const int nt = blockDim.x;
+    for (int o0 = threadIdx.x; o0 < H; o0 += nt * kNormBatch) {
         uint16_t t[kNormBatch];
 #pragma unroll
         for (int u = 0; u < kNormBatch; ++u) {
-            const int o = o0 + 256 * u;
+            const int o = o0 + nt * u;
             const int oc = o < H ? o : H - 1;
             if constexpr (COHERENT)
                 t[u] = __hip_atomic_load(const_cast<uint16_t *>(src + oc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -262,7 +385,7 @@ __device__ __forceinline__ void stage_row(const uint16_t *src, int H, float *v) 
         }
 #pragma unroll
         for (int u = 0; u < kNormBatch; ++u) {
-            const int o = o0 + 256 * u;
+            const int o = o0 + nt * u;
             if (o < H) v[o] = bf16_to_f32(t[u]);
         }
     }

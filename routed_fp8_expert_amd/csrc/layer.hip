@@ -117,13 +117,18 @@ __device__ __forceinline__ bool poll_words(const unsigned *p, const bool (&need)
 }
 
 // Every thread of the block calls this; wave 0 polls, the block waits at the
-// barrier.  A timeout sets the error word.
+// barrier.  A timeout sets the error word.  The barrier is a bare s_barrier:
+// the other waves only need to issue their loads after wave 0's poll has
+// returned, and __syncthreads would first wait for every load the waves
+// have in flight (the down workgroups' weight rows, issued long before and
+// not needed until the blend).  The memory clobber keeps the compiler from
+// moving loads across it.
 template <int NC>
 __device__ __forceinline__ void block_wait_words(const unsigned *p, const bool (&need)[NC], uint32_t *err,
                                                  uint64_t ticks) {
     if ((threadIdx.x >> 6) == 0 && !poll_words<NC>(p, need, ticks) && threadIdx.x == 0)
         flag_error(err, kErrWaitTimeout);
-    __syncthreads();
+    asm volatile("s_barrier" ::: "memory");
 }
 
 // Count this block on `ctr` (of `n` arrivals) once all its waves' stores
@@ -156,9 +161,12 @@ struct LayerGrid {
 };
 
 // Diagnostics (phase stamps): thread 0 of each workgroup records the constant
-// clock at its phase boundaries in stamps[block * kStampWords + i]; word 0
-// holds the role (0 router, 1 shared gate/up, 2 routed gate/up, 3 down), the
-// slot << 8 and, for a last arrival (router sub-counter, down group), 1 << 16.
+// clock at its phase boundaries in LDS and copies them to
+// stamps[block * kStampWords + i] when the workgroup ends (stores to global
+// memory would be waited for by the next barrier and lengthen the phase they
+// measure); word 0 holds the role (0 router, 1 shared gate/up, 2 routed
+// gate/up, 3 down), the slot << 8 and, for a last arrival (router
+// sub-counter, down group), 1 << 16.  Words never stamped read all ones.
 //   1 start
 //   2 router: row dot done; waiters: the routing's done words seen
 //   3 router: arrival counted; waiters: top-k done
@@ -169,11 +177,23 @@ struct LayerGrid {
 //   8 down: its group arrival returned
 //   9 down (last of its group): the group's line cleared
 //  10 waiters: the logits they select from have arrived
+__device__ __forceinline__ uint64_t *stamp_lds() {
+    __shared__ uint64_t words[kStampWords];
+    return words;
+}
+__device__ __forceinline__ void stamp_begin(const LayerGrid &g) {
+    if (g.stamps && threadIdx.x == 0)
+        for (int i = 0; i < kStampWords; ++i) stamp_lds()[i] = ~0ull;
+}
 __device__ __forceinline__ void stamp(const LayerGrid &g, int i) {
-    if (g.stamps && threadIdx.x == 0) g.stamps[(size_t)blockIdx.x * kStampWords + i] = __builtin_amdgcn_s_memrealtime();
+    if (g.stamps && threadIdx.x == 0) stamp_lds()[i] = __builtin_amdgcn_s_memrealtime();
 }
 __device__ __forceinline__ void stamp_role(const LayerGrid &g, uint64_t tag) {
-    if (g.stamps && threadIdx.x == 0) g.stamps[(size_t)blockIdx.x * kStampWords] = tag;
+    if (g.stamps && threadIdx.x == 0) stamp_lds()[0] = tag;
+}
+__device__ __forceinline__ void stamp_flush(const LayerGrid &g) {
+    if (g.stamps && threadIdx.x == 0)
+        for (int i = 0; i < kStampWords; ++i) g.stamps[(size_t)blockIdx.x * kStampWords + i] = stamp_lds()[i];
 }
 
 // h of every slot into LDS, read coherently (8-byte agent-scope loads, all
@@ -256,6 +276,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     const size_t hrep_stride = (size_t)(k + (has_shared ? 1 : 0)) * a.hstride;
     // the routing is ready once every router sub-counter that has arrivals is done
     const bool need_router[1] = {lane < kGroups && lane < g.nrb};
+    stamp_begin(g);
     stamp(g, 1);
 
     // ---------------------------------------------------------------- router
@@ -288,6 +309,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
             stamp_role(g, 1u << 16);
             stamp(g, 4);
         }
+        stamp_flush(g);
         return;
     }
     b -= g.nrb;
@@ -308,6 +330,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
         if (block_arrive_last(sync + kSyncGu + (k * kGroups + sub) * kCtrWords, group_count(g.nsb, sub), &ticket_s))
             publish_done(sync, kDoneGu + k * kGroups + sub);
         stamp(g, 5);
+        stamp_flush(g);
         return;
     }
     b -= g.nsb;
@@ -335,6 +358,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
                               &ticket_s))
             publish_done(sync, kDoneGu + slot * kGroups + sub);
         stamp(g, 5);
+        stamp_flush(g);
         return;
     }
     b -= k * g.ngb;
@@ -449,6 +473,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
         stamp_role(g, 3 | (1u << 16));
         stamp(g, 9);
     }
+    stamp_flush(g);
     if (a.norm_w && group_last &&
         block_arrive_last(sync + kSyncNorm, (unsigned)(g.ndb < kGroups ? g.ndb : kGroups), &ticket_s)) {
         // RMSNorm epilogue of the row (the residual after the add, else y):
