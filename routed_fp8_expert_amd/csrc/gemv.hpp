@@ -283,14 +283,31 @@ __device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, 
         }
         // rank: candidates ahead of this one (64-bit order key: key, then
         // the complemented expert index)
+        // every candidate is broadcast to all lanes by a lane permute, 8 at a
+        // time (issued back to back), and compared in vector registers (a
+        // lane read into a scalar register and back costs a pipeline round
+        // trip per candidate); lanes past the candidates hold key 0, which
+        // precedes nothing
+        const uint32_t ckz = lane < cn ? ck : 0u;
         const uint64_t kp = ((uint64_t)ck << 32) | (uint32_t)~ci;
-        int rank = 0;
-#pragma unroll 4
-        for (int q = 0; q < cn; ++q) {
-            const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)ck, q);
-            const uint32_t iq = (uint32_t)__builtin_amdgcn_readlane((int)ci, q);
-            rank += (((uint64_t)kq << 32) | (uint32_t)~iq) > kp ? 1 : 0;
+        int r0 = 0, r1 = 0;
+        for (int q0 = 0; q0 < cn; q0 += 8) {
+            uint32_t kq[8], iq[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                kq[u] = (uint32_t)__builtin_amdgcn_ds_bpermute((q0 + u) * 4, (int)ckz);
+                iq[u] = (uint32_t)__builtin_amdgcn_ds_bpermute((q0 + u) * 4, (int)ci);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int beats = (((uint64_t)kq[u] << 32) | (uint32_t)~iq[u]) > kp ? 1 : 0;
+                if (u & 1)
+                    r1 += beats;
+                else
+                    r0 += beats;
+            }
         }
+        const int rank = r0 + r1;
         const int dest = lane < cn ? rank : lane;
         sel_key = __builtin_amdgcn_ds_permute(dest * 4, (int)ck);
         sel_idx = __builtin_amdgcn_ds_permute(dest * 4, (int)ci);
