@@ -329,19 +329,6 @@ __global__ __launch_bounds__(kDownR1Waves * kWave) void k_down_r1(FfnArgs a) {
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
     auto hrow = [&](int j) { return j == a.k ? (size_t)a.R * a.k + r : (size_t)r * a.k + j; };
 
-    DownRow<FMT, LPR, CH> rows[kMaxSlots];
-    int es[kMaxSlots];
-#pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) {
-        if (j < nslots) {
-            const bool sh = j == a.k;
-            const ExpertSet &X = sh ? a.shared : a.routed;
-            const int e = sh ? 0 : a.ids[(size_t)r * a.k + j];
-            const bool ok = sh || (e >= 0 && e < a.E);
-            es[j] = ok ? e : -1;
-            rows[j].load(X, ok ? e : 0, o, sub, live && ok);
-        }
-    }
     // 32-code chunks (e2m1, int4): h staged in chunk-quad order per slot
     // (DownRow::dot_perm), the quad of slot j starting at element c*CPC + f
     // going to quad (f/4)*(I_j/CPC) + c, so the lanes of a row group read
@@ -349,21 +336,65 @@ __global__ __launch_bounds__(kDownR1Waves * kWave) void k_down_r1(FfnArgs a) {
     // measured faster there, slower for 16-code chunks, which keep the plain
     // layout
     constexpr bool PERM = !byte_codes(FMT);
-    if (HLDS) {
-        constexpr int CPC = cols_per_chunk<FMT>();
-        const int n4 = a.hstride / 4;
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.h);
-        for (int i = threadIdx.x; i < nslots * n4; i += kDownR1Waves * kWave) {
+    constexpr int CPC = cols_per_chunk<FMT>();
+    constexpr int NT = kDownR1Waves * kWave;
+    constexpr int SL = byte_codes(FMT) ? 3 : 6;   // h quads a thread loads per staging pass
+    const int n4 = a.hstride / 4, total = nslots * n4;
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(a.h);
+    f32x4 t[SL];
+    // staging pass i0: loads from clamped indices, all issued before any is stored
+    auto stage_load = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < SL; ++u) {
+            const int i = i0 + u * NT, ic = i < total ? i : total - 1;
+            const int j = ic / n4, q4 = ic - j * n4;
+            t[u] = src[hrow(j) * n4 + q4];
+        }
+    };
+    auto stage_store = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < SL; ++u) {
+            const int i = i0 + u * NT;
+            if (i >= total) continue;
             const int j = i / n4, q4 = i - j * n4;
             if (!PERM) {
-                hlds4[i] = src[hrow(j) * n4 + q4];
+                hlds4[i] = t[u];
                 continue;
             }
             const int ij = j == a.k ? a.shared.inter : a.routed.inter;
             if (4 * q4 < ij) {
                 const int c = (4 * q4) / CPC, f = (4 * q4) % CPC;
-                hlds4[j * n4 + (f >> 2) * (ij / CPC) + c] = src[hrow(j) * n4 + q4];
+                hlds4[j * n4 + (f >> 2) * (ij / CPC) + c] = t[u];
             }
+        }
+    };
+    // the row's expert ids in one load (lane j: slot j), read out at once;
+    // then the first h staging pass (cache hits), then the down rows (from
+    // HBM): loads return in order, so the h stores below wait for the h
+    // loads only
+    const int idv = a.ids[(size_t)r * a.k + (lane < a.k ? lane : 0)];
+    int eid[kMaxSlots];
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j) eid[j] = readlane(idv, j);
+    if (HLDS) stage_load(threadIdx.x);
+    DownRow<FMT, LPR, CH> rows[kMaxSlots];
+    int es[kMaxSlots];
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j) {
+        if (j < nslots) {
+            const bool sh = j == a.k;
+            const ExpertSet &X = sh ? a.shared : a.routed;
+            const int e = sh ? 0 : eid[j];
+            const bool ok = sh || (e >= 0 && e < a.E);
+            es[j] = ok ? e : -1;
+            rows[j].load(X, ok ? e : 0, o, sub, live && ok);
+        }
+    }
+    if (HLDS) {
+        stage_store(threadIdx.x);
+        for (int i0 = threadIdx.x + SL * NT; i0 < total; i0 += SL * NT) {
+            stage_load(i0);
+            stage_store(i0);
         }
         __syncthreads();
     }

@@ -418,26 +418,41 @@ template <int FMT> constexpr int cols_per_chunk() { return byte_codes(FMT) ? 16 
 // columns.  fp8: one f32 (or bf16) per 128x128 block; nvfp4: two e4m3 bytes (two
 // 16-column groups); int8/int4 per row: the row's f32; int4-g64: the f32 of
 // the 64-column group holding the chunk's 32 columns.
+// The stored bits of a chunk's scale (a float, a bf16 or two e4m3 bytes),
+// loaded as they are and decoded by scale_of where the chunk is used: a
+// conversion right after the load would wait for it there, and the loads of
+// a unit's rows (or of a row's slots) would then go out one at a time.
 template <int FMT>
-__device__ __forceinline__ f32x2 chunk_scale(const uint8_t *s, int row, int cols, int c) {
-    const float *sf = reinterpret_cast<const float *>(s);
+__device__ __forceinline__ uint32_t chunk_scale_raw(const uint8_t *s, int row, int cols, int c) {
+    const uint32_t *sf = reinterpret_cast<const uint32_t *>(s);
     if constexpr (FMT == kFp8) {
-        const float v = sf[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)];
-        return f32x2{v, v};
+        return sf[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)];
     } else if constexpr (FMT == kFp8Bf16s) {
         const uint16_t *sb = reinterpret_cast<const uint16_t *>(s);
-        const float v = bf16_to_f32(sb[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)]);
+        return sb[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)];
+    } else if constexpr (FMT == kNvfp4) {
+        return *reinterpret_cast<const uint16_t *>(s + (size_t)row * (cols >> 4) + 2 * c);
+    } else if constexpr (FMT == kInt4G64) {
+        return sf[(size_t)row * (cols >> 6) + (c >> 1)];
+    } else {
+        return sf[row];
+    }
+}
+template <int FMT>
+__device__ __forceinline__ f32x2 scale_of(uint32_t raw) {
+    if constexpr (FMT == kFp8Bf16s) {
+        const float v = bf16_to_f32((uint16_t)raw);
         return f32x2{v, v};
     } else if constexpr (FMT == kNvfp4) {
-        const uint16_t b = *reinterpret_cast<const uint16_t *>(s + (size_t)row * (cols >> 4) + 2 * c);
-        return f32x2{e4m3_f32(b, 0), e4m3_f32(b, 1)};
-    } else if constexpr (FMT == kInt4G64) {
-        const float v = sf[(size_t)row * (cols >> 6) + (c >> 1)];
-        return f32x2{v, v};
+        return f32x2{e4m3_f32(raw, 0), e4m3_f32(raw, 1)};
     } else {
-        const float v = sf[row];
+        const float v = __uint_as_float(raw);
         return f32x2{v, v};
     }
+}
+template <int FMT>
+__device__ __forceinline__ f32x2 chunk_scale(const uint8_t *s, int row, int cols, int c) {
+    return scale_of<FMT>(chunk_scale_raw<FMT>(s, row, cols, c));
 }
 
 // 16-byte loads of activation per weight chunk: bf16 (gate/up) and f32 (down).
@@ -525,7 +540,7 @@ struct GateUpRows {
     static constexpr int NS = fp8_block(FMT) ? 2 : 2 * P;
     static_assert(128 % P == 0, "pairs per wave must divide the scale block");
     u32x4 w[2 * P][CH];
-    f32x2 sc[NS][CH];
+    uint32_t sr[NS][CH];   // scale bits (scale_of), loaded from clamped positions
     float g;
 
     __device__ __forceinline__ static constexpr int sidx(int q) { return fp8_block(FMT) ? (q & 1) : q; }
@@ -554,9 +569,9 @@ struct GateUpRows {
             const int row = ((q & 1) ? I : 0) + (live ? i0 + p : i0);
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
+                // unmasked: a chunk past the row or a dead row has zero codes
                 const int ch = lane + kWave * c;
-                const f32x2 v = chunk_scale<FMT>(sbase, row, H, ch < nch ? ch : nch - 1);
-                sc[q][c] = (live && ch < nch) ? v : f32x2{0.0f, 0.0f};
+                sr[q][c] = chunk_scale_raw<FMT>(sbase, row, H, ch < nch ? ch : nch - 1);
             }
         }
         g = global_scale<FMT>(X.gu_g, e);
@@ -572,7 +587,7 @@ struct GateUpRows {
         for (int c = 0; c < CH; ++c) {
             if (lane + kWave * c < nch) {
 #pragma unroll
-                for (int q = 0; q < 2 * P; ++q) acc[q] += chunk_dot_bf16<FMT>(w[q][c], sc[sidx(q)][c], x[c]);
+                for (int q = 0; q < 2 * P; ++q) acc[q] += chunk_dot_bf16<FMT>(w[q][c], scale_of<FMT>(sr[sidx(q)][c]), x[c]);
             }
         }
     }
@@ -630,7 +645,7 @@ struct GateUpRows {
 template <int FMT, int LPR, int CH>
 struct DownRow {
     u32x4 w[CH];
-    f32x2 sc[CH];
+    uint32_t sr[CH];   // scale bits (scale_of), loaded from clamped positions
 
     // CLAMPED: unconditional loads from a clamped row and chunk, zeroed past
     // the matrix (the grouped kernel: its loads then overlap, 176 against
@@ -655,13 +670,9 @@ struct DownRow {
         }
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
+            // unmasked: a chunk past the row or a dead row has zero codes
             const int ch = sub + LPR * c;
-            if constexpr (CLAMPED) {
-                const f32x2 v = chunk_scale<FMT>(sbase, oc, X.inter, ch < nch ? ch : nch - 1);
-                sc[c] = (live && ch < nch) ? v : f32x2{0.0f, 0.0f};
-            } else {
-                sc[c] = (live && ch < nch) ? chunk_scale<FMT>(sbase, o, X.inter, ch) : f32x2{0.0f, 0.0f};
-            }
+            sr[c] = chunk_scale_raw<FMT>(sbase, live ? o : 0, X.inter, ch < nch ? ch : nch - 1);
         }
     }
 
@@ -671,7 +682,7 @@ struct DownRow {
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < CH; ++c)
-            if (sub + LPR * c < nch) acc += chunk_dot_f32<FMT>(w[c], sc[c], hq[c]);
+            if (sub + LPR * c < nch) acc += chunk_dot_f32<FMT>(w[c], scale_of<FMT>(sr[c]), hq[c]);
         return acc;
     }
 
