@@ -359,6 +359,14 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + expf(-g)) * u;
 }
 
+// Workgroup barrier for data exchanged through LDS: waits for the wave's
+// LDS operations, not for its global loads in flight (__syncthreads waits
+// for both).  The memory clobber keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ void flag_error(uint32_t *err, uint32_t bit) {
     if (err) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -317,16 +317,24 @@ __global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
 // the shared expert's row R*k + r.  kDownR1Waves waves a workgroup: the
 // row's h is staged once for that many waves' output elements.
 constexpr int kDownR1Waves = 8;
-template <int FMT, int LPR, int CH, bool HLDS>
+// h quads a thread of the per-row down kernel loads per staging pass
+__host__ __device__ constexpr int down_r1_stage_loads(int fmt) { return byte_codes(fmt) ? 3 : 6; }
+//
+// KS > 0: an instantiation for exactly KS slots (k + 1 with the shared
+// expert); its slot loops carry no per-slot branch, so the compiler counts
+// the loads in flight exactly and each wait below is for the loads it
+// needs (with branches it waits for all of them).  KS = 0: any slot count.
+template <int FMT, int LPR, int CH, bool HLDS, int KS = 0>
 __global__ __launch_bounds__(kDownR1Waves * kWave) void k_down_r1(FfnArgs a) {
     extern __shared__ f32x4 hlds4[];
     constexpr int RPW = kWave / LPR;
+    constexpr int NS = KS > 0 ? KS : kMaxSlots;
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
     const int r = blockIdx.y;
     const int sub = lane % LPR;
     const int o = (blockIdx.x * kDownR1Waves + wid) * RPW + lane / LPR;
     const bool live = o < a.H;
-    const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
+    const int nslots = KS > 0 ? KS : a.k + (a.shared.inter > 0 ? 1 : 0);
     auto hrow = [&](int j) { return j == a.k ? (size_t)a.R * a.k + r : (size_t)r * a.k + j; };
 
     // 32-code chunks (e2m1, int4): h staged in chunk-quad order per slot
@@ -338,7 +346,7 @@ __global__ __launch_bounds__(kDownR1Waves * kWave) void k_down_r1(FfnArgs a) {
     constexpr bool PERM = !byte_codes(FMT);
     constexpr int CPC = cols_per_chunk<FMT>();
     constexpr int NT = kDownR1Waves * kWave;
-    constexpr int SL = byte_codes(FMT) ? 3 : 6;   // h quads a thread loads per staging pass
+    constexpr int SL = down_r1_stage_loads(FMT);
     const int n4 = a.hstride / 4, total = nslots * n4;
     const f32x4 *src = reinterpret_cast<const f32x4 *>(a.h);
     f32x4 t[SL];
@@ -373,50 +381,88 @@ __global__ __launch_bounds__(kDownR1Waves * kWave) void k_down_r1(FfnArgs a) {
     // HBM): loads return in order, so the h stores below wait for the h
     // loads only
     const int idv = a.ids[(size_t)r * a.k + (lane < a.k ? lane : 0)];
-    int eid[kMaxSlots];
+    // the blend weights likewise (lane j < k: w_j, lane k: the shared gate),
+    // loaded before the rows so that no load issued after them is waited for
+    const float cfv = lane < a.k ? a.w[(size_t)r * a.k + lane] : a.s[r];
+    int eid[NS];
 #pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) eid[j] = readlane(idv, j);
+    for (int j = 0; j < NS; ++j) eid[j] = readlane(idv, j);
+    // and the per-expert global scales (NVFP4; lane j: slot j's expert)
+    float gsv = 1.0f;
+    if constexpr (KS > 0 && FMT == kNvfp4) {
+        const bool ok = idv >= 0 && idv < a.E;
+        gsv = lane < a.k ? a.routed.dn_g[ok ? idv : 0] : a.shared.dn_g[0];
+    }
     if (HLDS) stage_load(threadIdx.x);
-    DownRow<FMT, LPR, CH> rows[kMaxSlots];
-    int es[kMaxSlots];
+    DownRow<FMT, LPR, CH, true> rows[NS];
+    int es[NS];
 #pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) {
-        if (j < nslots) {
+    for (int j = 0; j < NS; ++j) {
+        if (KS > 0 || j < nslots) {
             const bool sh = j == a.k;
             const ExpertSet &X = sh ? a.shared : a.routed;
             const int e = sh ? 0 : eid[j];
             const bool ok = sh || (e >= 0 && e < a.E);
             es[j] = ok ? e : -1;
-            rows[j].load(X, ok ? e : 0, o, sub, live && ok);
+            if constexpr (KS > 0)
+                rows[j].template load<true>(X, ok ? e : 0, o, sub, live && ok);
+            else
+                rows[j].load(X, ok ? e : 0, o, sub, live && ok);
         }
     }
     if (HLDS) {
         stage_store(threadIdx.x);
-        for (int i0 = threadIdx.x + SL * NT; i0 < total; i0 += SL * NT) {
-            stage_load(i0);
-            stage_store(i0);
+        // (KS > 0 is launched only when one pass stages all of h: a loop here
+        // made the compiler wait for every load in flight after it)
+        if constexpr (KS == 0) {
+            for (int i0 = threadIdx.x + SL * NT; i0 < total; i0 += SL * NT) {
+                stage_load(i0);
+                stage_store(i0);
+            }
         }
-        __syncthreads();
+        // LDS only: each slot's dot below waits for its own rows, so the
+        // dots run while the later slots' rows still stream in
+        barrier_lds();
     }
     const float *hl = reinterpret_cast<const float *>(hlds4);
     float y = 0.0f;
+    bool bad = false;   // (KS > 0) an invalid id, flagged at the end
+    if constexpr (KS > 0) {
+        // an invalid id's row was loaded as zeros: its slot adds w * 0
 #pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) {
-        if (j < nslots) {
+        for (int j = 0; j < NS; ++j) bad |= es[j] < 0;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
             const bool sh = j == a.k;
             const ExpertSet &X = sh ? a.shared : a.routed;
-            if (es[j] < 0) {
-                if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, kErrBadExpertId);
-                continue;
-            }
             float d = !HLDS ? rows[j].dot(a.h + hrow(j) * a.hstride, X.inter, sub)
                       : PERM ? rows[j].dot_perm(hl + (size_t)j * a.hstride, X.inter, sub)
                              : rows[j].dot(hl + (size_t)j * a.hstride, X.inter, sub);
-            d *= global_scale<FMT>(X.dn_g, es[j]);
-            y = fmaf(sh ? a.s[r] : a.w[(size_t)r * a.k + j], d, y);
+            if constexpr (FMT == kNvfp4) d *= readlane(gsv, j);
+            y = fmaf(readlane(cfv, j), d, y);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            if (j < nslots) {
+                const bool sh = j == a.k;
+                const ExpertSet &X = sh ? a.shared : a.routed;
+                if (es[j] < 0) {
+                    if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, kErrBadExpertId);
+                    continue;
+                }
+                float d = !HLDS ? rows[j].dot(a.h + hrow(j) * a.hstride, X.inter, sub)
+                          : PERM ? rows[j].dot_perm(hl + (size_t)j * a.hstride, X.inter, sub)
+                                 : rows[j].dot(hl + (size_t)j * a.hstride, X.inter, sub);
+                d *= global_scale<FMT>(X.dn_g, es[j]);
+                y = fmaf(sh ? a.s[r] : a.w[(size_t)r * a.k + j], d, y);
+            }
         }
     }
     if (live && sub == 0) store_out(a.y, a.res, a.ldy, r, o, y);
+    // (a branch with an atomic before the dots made the compiler wait there
+    // for every load in flight)
+    if (bad && threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, kErrBadExpertId);
 }
 
 // Down GEMV for one expert of a multi-row step.  A row group of LPR lanes
@@ -608,14 +654,20 @@ template <int FMT>
 hipError_t down_r1_fmt(const FfnArgs &a, hipStream_t st) {
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
     const size_t hbytes = (size_t)nslots * a.hstride * 4;
+    // one staging pass covers h (the slot-count instantiations need it)
+    const bool one_pass = (size_t)nslots * (a.hstride / 4) <= (size_t)down_r1_stage_loads(FMT) * kDownR1Waves * kWave;
     MOE_DOWN_DISPATCH({
         const int rpb = kDownR1Waves * (kWave / LPR);
         dim3 grid((a.H + rpb - 1) / rpb, a.R), block(kDownR1Waves * kWave);
         (void)rows_per_block;
-        if (hbytes <= kMaxHLds)
-            hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, true>), grid, block, hbytes, st, a);
-        else
+        if (hbytes > kMaxHLds)
             hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, false>), grid, block, 0, st, a);
+        else if (CH == 1 && nslots == 9 && one_pass)
+            hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, true, 9>), grid, block, hbytes, st, a);
+        else if (CH == 1 && nslots == 11 && one_pass)
+            hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, true, 11>), grid, block, hbytes, st, a);
+        else
+            hipLaunchKernelGGL((k_down_r1<FMT, LPR, CH, true>), grid, block, hbytes, st, a);
     });
 }
 // Rows per row group of the grouped down kernel: 8 register rows per lane

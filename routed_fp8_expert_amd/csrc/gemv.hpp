@@ -452,7 +452,24 @@ __device__ __forceinline__ f32x2 scale_of(uint32_t raw) {
 }
 template <int FMT>
 __device__ __forceinline__ f32x2 chunk_scale(const uint8_t *s, int row, int cols, int c) {
-    return scale_of<FMT>(chunk_scale_raw<FMT>(s, row, cols, c));
+    const float *sf = reinterpret_cast<const float *>(s);
+    if constexpr (FMT == kFp8) {
+        const float v = sf[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)];
+        return f32x2{v, v};
+    } else if constexpr (FMT == kFp8Bf16s) {
+        const uint16_t *sb = reinterpret_cast<const uint16_t *>(s);
+        const float v = bf16_to_f32(sb[(size_t)(row >> 7) * (cols >> 7) + ((c * 16) >> 7)]);
+        return f32x2{v, v};
+    } else if constexpr (FMT == kNvfp4) {
+        const uint16_t b = *reinterpret_cast<const uint16_t *>(s + (size_t)row * (cols >> 4) + 2 * c);
+        return f32x2{e4m3_f32(b, 0), e4m3_f32(b, 1)};
+    } else if constexpr (FMT == kInt4G64) {
+        const float v = sf[(size_t)row * (cols >> 6) + (c >> 1)];
+        return f32x2{v, v};
+    } else {
+        const float v = sf[row];
+        return f32x2{v, v};
+    }
 }
 
 // 16-byte loads of activation per weight chunk: bf16 (gate/up) and f32 (down).
@@ -540,7 +557,7 @@ struct GateUpRows {
     static constexpr int NS = fp8_block(FMT) ? 2 : 2 * P;
     static_assert(128 % P == 0, "pairs per wave must divide the scale block");
     u32x4 w[2 * P][CH];
-    uint32_t sr[NS][CH];   // scale bits (scale_of), loaded from clamped positions
+    f32x2 sc[NS][CH];
     float g;
 
     __device__ __forceinline__ static constexpr int sidx(int q) { return fp8_block(FMT) ? (q & 1) : q; }
@@ -569,9 +586,9 @@ struct GateUpRows {
             const int row = ((q & 1) ? I : 0) + (live ? i0 + p : i0);
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                // unmasked: a chunk past the row or a dead row has zero codes
                 const int ch = lane + kWave * c;
-                sr[q][c] = chunk_scale_raw<FMT>(sbase, row, H, ch < nch ? ch : nch - 1);
+                const f32x2 v = chunk_scale<FMT>(sbase, row, H, ch < nch ? ch : nch - 1);
+                sc[q][c] = (live && ch < nch) ? v : f32x2{0.0f, 0.0f};
             }
         }
         g = global_scale<FMT>(X.gu_g, e);
@@ -587,7 +604,7 @@ struct GateUpRows {
         for (int c = 0; c < CH; ++c) {
             if (lane + kWave * c < nch) {
 #pragma unroll
-                for (int q = 0; q < 2 * P; ++q) acc[q] += chunk_dot_bf16<FMT>(w[q][c], scale_of<FMT>(sr[sidx(q)][c]), x[c]);
+                for (int q = 0; q < 2 * P; ++q) acc[q] += chunk_dot_bf16<FMT>(w[q][c], sc[sidx(q)][c], x[c]);
             }
         }
     }
@@ -642,10 +659,17 @@ struct GateUpRows {
 
 // Row o of expert e's down matrix as seen by one lane of its LPR-lane row
 // group: CH chunks (lane-strided by LPR) with their scales.
-template <int FMT, int LPR, int CH>
+//
+// RAW: keep each chunk's scale as its stored bits, loaded unconditionally
+// from a clamped position and decoded where used (the per-row down kernel:
+// its NVFP4 rows otherwise load one slot at a time, each scale conversion
+// waiting for its load); otherwise decode at the load, masked (the one-launch
+// layer measured faster so).
+template <int FMT, int LPR, int CH, bool RAW = false>
 struct DownRow {
     u32x4 w[CH];
-    uint32_t sr[CH];   // scale bits (scale_of), loaded from clamped positions
+    uint32_t sr[CH];   // RAW: scale bits (scale_of)
+    f32x2 sc[CH];      // !RAW: decoded scales, zero past the row
 
     // CLAMPED: unconditional loads from a clamped row and chunk, zeroed past
     // the matrix (the grouped kernel: its loads then overlap, 176 against
@@ -670,10 +694,23 @@ struct DownRow {
         }
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            // unmasked: a chunk past the row or a dead row has zero codes
             const int ch = sub + LPR * c;
-            sr[c] = chunk_scale_raw<FMT>(sbase, live ? o : 0, X.inter, ch < nch ? ch : nch - 1);
+            if constexpr (RAW) {
+                // unmasked: a chunk past the row or a dead row has zero codes
+                sr[c] = chunk_scale_raw<FMT>(sbase, live ? o : 0, X.inter, ch < nch ? ch : nch - 1);
+            } else if constexpr (CLAMPED) {
+                const f32x2 v = chunk_scale<FMT>(sbase, oc, X.inter, ch < nch ? ch : nch - 1);
+                sc[c] = (live && ch < nch) ? v : f32x2{0.0f, 0.0f};
+            } else {
+                sc[c] = (live && ch < nch) ? chunk_scale<FMT>(sbase, o, X.inter, ch) : f32x2{0.0f, 0.0f};
+            }
         }
+    }
+    __device__ __forceinline__ f32x2 scale(int c) const {
+        if constexpr (RAW)
+            return scale_of<FMT>(sr[c]);
+        else
+            return sc[c];
     }
 
     // Per-lane partial sum against the lane's h chunks hq[c] (chunk sub + LPR c).
@@ -682,7 +719,7 @@ struct DownRow {
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < CH; ++c)
-            if (sub + LPR * c < nch) acc += chunk_dot_f32<FMT>(w[c], scale_of<FMT>(sr[c]), hq[c]);
+            if (sub + LPR * c < nch) acc += chunk_dot_f32<FMT>(w[c], scale(c), hq[c]);
         return acc;
     }
 

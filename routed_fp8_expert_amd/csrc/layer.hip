@@ -387,11 +387,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
         }
     }
     const float s_gate = has_shared ? ld_agent(a.s) : 0.0f;
-    // the residual's bits, loaded unconditionally (from x when there is no
-    // residual) and widened where used: a branch around the load made the
-    // compiler widen it at once, waiting for it and for every down row
-    // issued above
-    const uint16_t res_bits = (a.res ? a.res : a.x)[live ? o : 0];
+    const float res_in = a.res ? bf16_to_f32(a.res[live ? o : 0]) : 0.0f;   // unconditional load (clamped)
     stamp(g, 4);
     // every slot's h is complete once every (slot, sub-counter) with arrivals is done
     bool need_gu[NCG];
@@ -446,7 +442,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
         }
     }
     if (live && sub == 0) {
-        const uint16_t yb = f32_to_bf16(y), rb = f32_to_bf16(bf16_to_f32(res_bits) + y);
+        const uint16_t yb = f32_to_bf16(y), rb = f32_to_bf16(res_in + y);
         if (a.norm_w) {
             // written through: the last down workgroup reads the whole row back
             if (a.y) __hip_atomic_store(a.y + o, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
