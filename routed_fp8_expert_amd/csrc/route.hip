@@ -87,33 +87,33 @@ __global__ __launch_bounds__(256) void k_topk(RouteArgs a, int s_mode) {
     }
 }
 
-// Exclusive scan of one int per thread over a 1024-thread block.
+// Inclusive prefix sum over the wave: row shifts by 1, 2, 4, 8 within each
+// 16-lane row, then the two row broadcasts carry rows 0 and 1 into the rows
+// above them.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += dpp<0x111>(0, v);           // row_shr:1
+    v += dpp<0x112>(0, v);           // row_shr:2
+    v += dpp<0x114>(0, v);           // row_shr:4
+    v += dpp<0x118>(0, v);           // row_shr:8
+    v += dpp<kDppBcast15, 0xa>(0, v);
+    v += dpp<kDppBcast31, 0xc>(0, v);
+    return v;
+}
+
+// Exclusive prefix sum over the 1024-thread block; every thread calls it.
+// Each wave scans itself, publishes its total, and then scans the 16 totals
+// itself (no second round through LDS).
 __device__ int block_excl_scan(int v, int *wave_tot, int *total) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int t = __shfl_up(inc, o, kWave);
-        if (lane >= o) inc += t;
-    }
+    const int inc = wave_incl_scan(v);
     if (lane == kWave - 1) wave_tot[wid] = inc;
     __syncthreads();
-    if (wid == 0) {
-        int t = lane < 16 ? wave_tot[lane] : 0;
-        int ti = t;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const int u = __shfl_up(ti, o, kWave);
-            if (lane >= o) ti += u;
-        }
-        if (lane < 16) wave_tot[16 + lane] = ti - t;
-        if (lane == 15) wave_tot[32] = ti;
-    }
-    __syncthreads();
-    const int excl = inc - v + wave_tot[16 + wid];
-    *total = wave_tot[32];
-    __syncthreads();
-    return excl;
+    const int t = lane < 16 ? wave_tot[lane] : 0;
+    const int ti = wave_incl_scan(t);
+    const int before = readlane(ti, wid) - readlane(t, wid);
+    *total = readlane(ti, 15);
+    __syncthreads();   // wave_tot is reused by the next scan
+    return inc - v + before;
 }
 
 // Splits the touched experts into the GEMV-arm list and the MFMA-arm list
@@ -173,16 +173,28 @@ __global__ __launch_bounds__(1024) void k_plan(RouteArgs a) {
 // at offset + (rows before it that chose the same expert).  With `do_plan`
 // it also writes the arm lists.  One 1024-thread workgroup; COHERENT reads
 // the ids at agent scope (written by other workgroups of the same launch).
+constexpr int kGroupIds = 16;   // (row, slot) entries a grouping thread holds: R*k <= 16 * 1024
 template <bool COHERENT>
 __device__ void group_rows(const RouteArgs &a, int do_plan, uint32_t *bm, int *wave_tot, int *soff) {
     const int tid = threadIdx.x;
     const int R = a.R, E = a.E, k = a.k, W = (R + 31) >> 5;
     const int n = R * k;
     auto id_at = [&](int i) { return COHERENT ? ld_agent(a.ids + i) : a.ids[i]; };
+    // the step's ids, kGroupIds a thread (entry tid + 1024 u), all loads in
+    // flight at once and kept for both passes
+    int idr[kGroupIds];
+#pragma unroll
+    for (int u = 0; u < kGroupIds; ++u) {
+        const int i = tid + 1024 * u;
+        idr[u] = i < n ? id_at(i) : -1;
+    }
     for (int i = tid; i < E * W; i += 1024) bm[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < n; i += 1024) {
-        const int e = id_at(i);
+#pragma unroll
+    for (int u = 0; u < kGroupIds; ++u) {
+        const int i = tid + 1024 * u;
+        if (i >= n) continue;
+        const int e = idr[u];
         const int r = i / k;
         if (e >= 0 && e < E)
             atomicOr(&bm[e * W + (r >> 5)], 1u << (r & 31));
@@ -204,9 +216,11 @@ __device__ void group_rows(const RouteArgs &a, int do_plan, uint32_t *bm, int *w
     if (e == 0) a.offsets[E] = total;
     if (do_plan) plan_lists(a, e, c, wave_tot);
     __syncthreads();
-    for (int i = tid; i < n; i += 1024) {
-        const int ee = id_at(i);
-        if (ee < 0 || ee >= E) continue;
+#pragma unroll
+    for (int u = 0; u < kGroupIds; ++u) {
+        const int i = tid + 1024 * u;
+        const int ee = idr[u];
+        if (i >= n || ee < 0 || ee >= E) continue;
         const int r = i / k;
         const uint32_t *row = bm + ee * W;
         int rank = __popc(row[r >> 5] & ((1u << (r & 31)) - 1u));
