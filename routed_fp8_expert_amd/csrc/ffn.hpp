@@ -97,23 +97,30 @@ __device__ __forceinline__ int entry_row(const FfnArgs &a, int entry) {
 
 // Warm a (at most 16 KB) slice `part` of `nparts` of a matrix of `bytes`
 // bytes into the memory-side cache; returns the folded word.
-__device__ __forceinline__ uint32_t warm_slice(const uint8_t *base, size_t bytes, int part, int nparts) {
-    size_t chunk = (bytes + nparts - 1) / nparts;
-    chunk = (chunk + 15) & ~(size_t)15;
-    const size_t cap = (size_t)kWarmLoads * 16 * 256;
-    if (chunk > cap) chunk = cap;
-    const size_t begin = (size_t)part * chunk;
-    uint32_t acc = 0;
+// A block's share of a matrix read once to warm it into the memory-side
+// cache: issue() sends the loads, fold() (after the block's real work, so
+// nothing issued later waits behind these loads) folds them into one word.
+struct WarmSlice {
     u32x4 v[kWarmLoads];
+    __device__ __forceinline__ void issue(const uint8_t *base, size_t bytes, int part, int nparts) {
+        size_t chunk = (bytes + nparts - 1) / nparts;
+        chunk = (chunk + 15) & ~(size_t)15;
+        const size_t cap = (size_t)kWarmLoads * 16 * 256;
+        if (chunk > cap) chunk = cap;
+        const size_t begin = (size_t)part * chunk;
 #pragma unroll
-    for (int i = 0; i < kWarmLoads; ++i) {
-        const size_t off = begin + ((size_t)i * 256 + threadIdx.x) * 16;
-        v[i] = (off + 16 <= bytes && off < begin + chunk) ? ld16(base + off) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < kWarmLoads; ++i) {
+            const size_t off = begin + ((size_t)i * 256 + threadIdx.x) * 16;
+            v[i] = (off + 16 <= bytes && off < begin + chunk) ? ld16(base + off) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
+    __device__ __forceinline__ uint32_t fold() const {
+        uint32_t acc = 0;
 #pragma unroll
-    for (int i = 0; i < kWarmLoads; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
-    return acc;
-}
+        for (int i = 0; i < kWarmLoads; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+        return acc;
+    }
+};
 
 __device__ __forceinline__ void sink_word(uint32_t *sink, uint32_t acc) {
     if (acc == 0x9E3779B9u && sink) *sink = acc;
@@ -239,11 +246,20 @@ __global__ __launch_bounds__(256) void k_lead_r1(RouteArgs r, FfnArgs a) {
     if (X.inter <= 0) return;
     const int b = blockIdx.x - nrb, nsb = gridDim.x - nrb;
     const int i0 = (b * 4 + wid) * P;
-    GateUpRows<FMT, CH, P> rows;
-    if (i0 < X.inter) rows.load(X, 0, i0, a.H);
-    const uint32_t warm = warm_slice(X.dn, (size_t)a.H * row_bytes<FMT>(X.inter), b, nsb);
-    if (i0 < X.inter) rows.apply(a.x, a.H, X.inter, i0, a.h + (size_t)a.k * a.hstride);
-    sink_word(a.sink, warm);
+    // activations, then weights, then the warming loads; the dot waits for
+    // the first two only (a wave past the expert's rows loads clamped rows
+    // as zeros and stores nothing)
+    using Rows = GateUpRows<FMT, CH, P>;
+    u32x4 x[CH][x_quads<FMT>()];
+    Rows::load_x(a.x, a.H, x);
+    Rows rows;
+    rows.load(X, 0, i0, a.H);
+    WarmSlice warm;
+    warm.issue(X.dn, (size_t)a.H * row_bytes<FMT>(X.inter), b, nsb);
+    float acc[2 * P];
+    rows.partial(x, a.H, acc);
+    rows.finish(acc, X.inter, i0, a.h + (size_t)a.k * a.hstride);
+    sink_word(a.sink, warm.fold());
 }
 
 // gate/up of the routed experts of a one-row layer, and of a step of a few
@@ -284,13 +300,23 @@ __global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
         }
         __syncthreads();
     }
+    using Rows = GateUpRows<FMT, CH, P>;
+    constexpr int XQ = x_quads<FMT>();
     if (slot == a.k) {
         const ExpertSet &X = a.shared;
         if (r != 0 || i0 >= X.inter) return;
-        GateUpRows<FMT, CH, P> rows;
+        // every row with this wave's shared rows (the first row's
+        // activations issued with the weights)
+        u32x4 x[CH][XQ];
+        Rows::load_x(a.x, a.H, x);
+        Rows rows;
         rows.load(X, 0, i0, a.H);
-        for (int rr = 0; rr < a.R; ++rr)
-            rows.apply(a.x + (size_t)rr * a.ldx, a.H, X.inter, i0, a.h + (size_t)(a.R * a.k + rr) * a.hstride);
+        for (int rr = 0; rr < a.R; ++rr) {
+            if (rr > 0) Rows::load_x(a.x + (size_t)rr * a.ldx, a.H, x);
+            float acc[2 * P];
+            rows.partial(x, a.H, acc);
+            rows.finish(acc, X.inter, i0, a.h + (size_t)(a.R * a.k + rr) * a.hstride);
+        }
         return;
     }
     const int e = a.topk_src ? e_s : a.ids[(size_t)r * a.k + slot];
@@ -299,13 +325,24 @@ __global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
         return;
     }
     const ExpertSet &X = a.routed;
-    GateUpRows<FMT, CH, P> rows;
-    if (i0 < X.inter) rows.load(X, e, i0, a.H);
-    const uint32_t warm = warm_slice(X.dn + (size_t)e * X.dn_stride, (size_t)a.H * row_bytes<FMT>(X.inter),
-                                     blockIdx.x, gridDim.x);
-    if (i0 < X.inter)
-        rows.apply(a.x + (size_t)r * a.ldx, a.H, X.inter, i0, a.h + ((size_t)r * a.k + slot) * a.hstride);
-    sink_word(a.sink, warm);
+    // activations, weights and warming loads all in flight before the first
+    // wait (a wave past the expert's rows loads clamped rows as zeros and
+    // stores nothing).  The warming is folded after the dot for 32-code
+    // chunks (the dot then waits for its own loads only: 397B-A17B one row
+    // 17.6 -> 15.4 us) and before it for byte codes (its registers would
+    // cost the fp8 kernel a wave per SIMD: 2 rows 14.1 -> 15.5 us).
+    constexpr bool FOLD_LATE = !byte_codes(FMT);
+    u32x4 x[CH][XQ];
+    Rows::load_x(a.x + (size_t)r * a.ldx, a.H, x);
+    Rows rows;
+    rows.load(X, e, i0, a.H);
+    WarmSlice warm;
+    warm.issue(X.dn + (size_t)e * X.dn_stride, (size_t)a.H * row_bytes<FMT>(X.inter), blockIdx.x, gridDim.x);
+    if (!FOLD_LATE) sink_word(a.sink, warm.fold());
+    float acc[2 * P];
+    rows.partial(x, a.H, acc);
+    rows.finish(acc, X.inter, i0, a.h + ((size_t)r * a.k + slot) * a.hstride);
+    if (FOLD_LATE) sink_word(a.sink, warm.fold());
 }
 
 // Down GEMV fused with the blend, for one row (blockIdx.y) of a one-row
