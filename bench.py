@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -69,20 +70,42 @@ def distinct_routed(res) -> int:
     return total
 
 
-def source_digest() -> str:
+CSRC = os.path.join(ROOT, "routed_fp8_expert_amd", "csrc")
+# translation unit of each profiled kernel
+KERNEL_TU = {"layer": "layer.hip", "dense": "dense.hip"}
+
+
+def _digest(names) -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "routed_fp8_expert_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in sorted(names):
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
+def source_digest(kernel: str = None) -> str:
+    """Digest of the native sources: all of them, or those a kernel's code
+    depends on (its translation unit, the headers it includes, directly or
+    not, and the C ABI's host code that sizes and launches it)."""
+    if kernel is None:
+        return _digest(os.listdir(CSRC))
+    names, todo = set(), [KERNEL_TU[kernel], "api.cpp", "host_checks.hpp"]
+    while todo:
+        name = todo.pop()
+        if name in names or not os.path.exists(os.path.join(CSRC, name)):
+            continue
+        names.add(name)
+        with open(os.path.join(CSRC, name)) as f:
+            todo += re.findall(r'^\s*#\s*include\s+"([^"]+)"', f.read(), re.M)
+    return _digest(names)
+
+
 def counter_traffic(kernel: str, workload: str, rows: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this kernel and workload (profiles/traffic_<kernel>_<workload>_r<rows>.txt,
-    `key: value` lines), if it was taken on the current sources."""
+    `key: value` lines), if it was taken on the current sources of that
+    kernel."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_r{rows}.txt")
     if not os.path.exists(path):
         return None
@@ -92,7 +115,7 @@ def counter_traffic(kernel: str, workload: str, rows: int):
             if ":" in line and not line.startswith((" ", "#")):
                 key, _, val = line.partition(":")
                 kv[key.strip()] = val.strip()
-    if kv.get("source_digest") != source_digest():
+    if kv.get("source_digest") != source_digest(kernel):
         return None
     return int(kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in kv else None
 

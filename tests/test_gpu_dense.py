@@ -63,9 +63,9 @@ def _check(orc, q, s, x, y, sel):
 
 
 CASES = [
-    # 129 and 300 rows: the matrix-core arm's second and third 128-row chunk,
-    # the last one ragged
-    ("small_384x640", r) for r in (1, 3, 7, 8, 17, 33, 64, 128, 129, 300)
+    # 129 and 300 rows: several row groups, the last one ragged; 400 rows:
+    # 32-column workgroups, groups of two tiles, padding blocks in the grid
+    ("small_384x640", r) for r in (1, 3, 7, 8, 17, 33, 64, 128, 129, 300, 400)
 ] + [
     ("up_4096x2048", r) for r in (1, 5, 7, 8, 31, 64, 128, 200)
 ] + [
@@ -104,6 +104,7 @@ def test_dense_batch_invariance(moe, name):
     y3 = _run(moe, ctx, w, x[2:5])
     y8 = _run(moe, ctx, w, x[:8])
     y130 = _run(moe, ctx, w, x)
+    y64 = _run(moe, ctx, w, x[64:128])
     y45 = _run(moe, ctx, w, x[85:130])
     y17 = _run(moe, ctx, w, x[100:117])
     ctx.close()
@@ -112,6 +113,7 @@ def test_dense_batch_invariance(moe, name):
         assert torch.equal(v(y7[i:i + 1]), v(ones[i])), f"row {i}: seven-row call differs from one-row call"
     assert torch.equal(v(y7[2:5]), v(y3))
     assert torch.equal(v(y130[:8]), v(y8))
+    assert torch.equal(v(y130[64:128]), v(y64))
     assert torch.equal(v(y130[85:130]), v(y45))
     assert torch.equal(v(y130[100:117]), v(y17))
 
