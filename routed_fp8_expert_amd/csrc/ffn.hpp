@@ -181,8 +181,10 @@ __device__ __forceinline__ void gate_up_gemv_unit(const FfnArgs &a, int bx, int 
 // gate/up of a step, both arms in one launch: workgroups [0, nm) are
 // matrix-core units (column group b % nmx of tile b / nmx, fp8 only), the
 // rest GEMV units (slice b % gx of task b / gx).
+// (fp8: two waves a SIMD where the registers allow it; the compiler would
+// otherwise give the matrix-core unit more and run one.)
 template <int FMT, int CH, int PM>
-__global__ __launch_bounds__(256) void k_gate_up(FfnArgs a, int nmx, int nm, int gx) {
+__global__ __launch_bounds__(256, FMT == kFp8 && CH <= 4 ? 2 : 1) void k_gate_up(FfnArgs a, int nmx, int nm, int gx) {
     int b = blockIdx.x;
     if constexpr (FMT == kFp8) {
         if (b < nm) {
@@ -558,18 +560,34 @@ __device__ __forceinline__ void down_gemv_unit(const FfnArgs &a, int bx, int tas
 }
 
 // Down projection of a multi-row step, both arms in one launch (the layout
-// of k_gate_up): matrix-core units first, then GEMV units.
+// of k_gate_up): matrix-core units of the plan's 16-row down tiles first
+// (nm blocks, column group b % nmx of tile b / nmx; nm = 0 when the 64-row
+// launch below takes the matrix-core arm), then GEMV units (slice b % gx of
+// task b / gx).
 template <int FMT, int LPR, int CH, int RPL>
 __global__ __launch_bounds__(256) void k_down_grouped(FfnArgs a, int nmx, int nm, int gx) {
     int b = blockIdx.x;
     if constexpr (FMT == kFp8) {
         if (b < nm) {
-            mfma_down_unit(a, b % nmx, b / nmx);
+            mfma_down_unit<kMfmaTileRows / 16>(a, b % nmx, b / nmx);
             return;
         }
     }
     b -= nm;
     down_gemv_unit<FMT, LPR, CH, RPL>(a, b % gx, b / gx);
+}
+
+// The matrix-core arm of the down projection on the plan's 64-row (gate/up)
+// tiles, for steps of kDownTallRows rows and more: an expert's down matrix is
+// then read once per 64 rows instead of once per 16.  A launch of its own,
+// before the GEMV units': its tiles take more registers and LDS than those
+// units, which would otherwise run at its occupancy.
+constexpr int kDownTallRows = 256;
+
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void k_down_mfma(FfnArgs a, int nmx) {
+    const int b = blockIdx.x;
+    mfma_down_unit<kMfmaGuTileRows / 16>(a, b % nmx, b / nmx);
 }
 
 // Blend for multi-row steps: y[r][o] = sum_j w[r][j] dbuf[r*k+j][o] (slot
@@ -713,12 +731,22 @@ constexpr int down_rpl(int ch) { return ch <= 1 ? 8 : ch <= 2 ? 4 : 2; }
 
 template <int FMT>
 hipError_t down_grouped_fmt(const FfnArgs &a, hipStream_t st) {
+    const int nmx = mfma_down_groups(a.H);
+    int nm = 0;
+    if constexpr (FMT == kFp8) {
+        if (a.mfma_max_tiles > 0 && a.R >= kDownTallRows) {
+            hipLaunchKernelGGL((k_down_mfma<FMT>), dim3((unsigned)(nmx * a.mfma_gu_max_tiles)), dim3(256), 0, st, a,
+                               nmx);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        } else if (a.mfma_max_tiles > 0) {
+            nm = nmx * a.mfma_max_tiles;
+        }
+    }
     MOE_DOWN_DISPATCH({
         constexpr int RPL = down_rpl(CH);
         const int rows = rows_per_block * RPL;
         const int gx = (a.H + rows - 1) / rows;
-        const int nmx = mfma_down_groups(a.H);
-        const int nm = FMT == kFp8 && a.mfma_max_tiles > 0 ? nmx * a.mfma_max_tiles : 0;
         const long long nb = nm + (long long)gx * n_tasks(a);
         if (nb == 0) return hipSuccess;
         hipLaunchKernelGGL((k_down_grouped<FMT, LPR, CH, RPL>), dim3((unsigned)nb), dim3(256), 0, st, a, nmx, nm, gx);

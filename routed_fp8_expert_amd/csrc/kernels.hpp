@@ -38,7 +38,7 @@ enum CtxWord : int {
 // Bits of the ctx's device error word.
 enum : uint32_t { kErrBadExpertId = 1u, kErrWaitTimeout = 2u };
 
-constexpr int kMfmaTileRows = 16;   // rows of an expert per matrix-core tile (down)
+constexpr int kMfmaTileRows = 16;   // rows of an expert per matrix-core tile (down, fewer-row steps)
 constexpr int kMfmaGuTileRows = 64; // rows of an expert per gate/up matrix-core tile
 
 // Weight formats (the values of the C ABI's moe_weight_format).

@@ -31,8 +31,6 @@ namespace moe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTileRows = kMfmaTileRows;
-
 // 8 e4m3 codes (2 dwords) to 8 bf16, exact.
 __device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
     const bf16x2 a = e4m3x2_bf16<false>(w0), b = e4m3x2_bf16<true>(w0);
@@ -117,7 +115,6 @@ constexpr int kMfmaWaves = 4;    // waves per workgroup; each owns its own colum
 // double-buffered LDS tile whose rows are padded so that the fragment reads
 // of 16 lanes hit distinct banks.
 constexpr int kXRow = 128 + 8;   // bf16 per staged activation row (8 of padding)
-constexpr int kHRow = 128 + 4;   // f32 per staged h row (4 of padding)
 
 // The gate and up weight chunks of one 128-wide K block (16 codes each, two
 // 64-wide halves).
@@ -219,33 +216,52 @@ __device__ __forceinline__ void mfma_gate_up_unit(const FfnArgs &a, int bx, int 
     f32x4 accg[kGuSub], accu[kGuSub];
 #pragma unroll
     for (int q = 0; q < kGuSub; ++q) accg[q] = accu[q] = f32x4{0, 0, 0, 0};
+    // Pipeline: the weights two K blocks ahead, the activations one block
+    // ahead in registers (stored into LDS at the start of the step that
+    // precedes their use).  The barriers wait for LDS only, so loads in
+    // flight stay in flight across them (a full barrier would wait for the
+    // next blocks' weights every step); in the steady loop every load is
+    // unconditional (row 0 for rows past the tile), so the compiler's wait
+    // counts stay exact.
     GuStage s0, s1;
-    gu_load(s0, wg, wu, 0, grp);
-    if (nkb > 1) gu_load(s1, wg, wu, 1, grp);
+    auto load_w = [&](GuStage &st, int kb) { gu_load(st, wg, wu, kb, grp); };
+    u32x4 xr[kGuSub];
+    auto load_x = [&](int kb) {
 #pragma unroll
-    for (int q = 0; q < kGuSub; ++q)
-        if (q < nsub) *reinterpret_cast<u32x4 *>(&xs[0][srow + 16 * q][spiece * 8]) = ld16(xrow(q));
-    __syncthreads();
-    // one K block: the next block's activations loaded, this block multiplied
-    // from LDS, the next block stored into the other buffer, a barrier
-    auto step = [&](int kb, const GuStage &s) {
-        const bool more = kb + 1 < nkb;
-        u32x4 xn[kGuSub];
-#pragma unroll
-        for (int q = 0; q < kGuSub; ++q)
-            if (more && q < nsub) xn[q] = ld16(xrow(q) + (kb + 1) * 128);
-        gu_step(s, xs[kb & 1], col, grp, readlane(sgl, kb), readlane(sul, kb), nsub, accg, accu);
-#pragma unroll
-        for (int q = 0; q < kGuSub; ++q)
-            if (more && q < nsub) *reinterpret_cast<u32x4 *>(&xs[(kb + 1) & 1][srow + 16 * q][spiece * 8]) = xn[q];
-        __syncthreads();
+        for (int q = 0; q < kGuSub; ++q) xr[q] = ld16(xrow(q) + kb * 128);
     };
-    for (int kb = 0; kb < nkb; kb += 2) {
-        step(kb, s0);
-        if (kb + 2 < nkb) gu_load(s0, wg, wu, kb + 2, grp);
+    auto store_x = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < kGuSub; ++q)
+            if (q < nsub) *reinterpret_cast<u32x4 *>(&xs[buf][srow + 16 * q][spiece * 8]) = xr[q];
+    };
+    load_w(s0, 0);
+    if (nkb > 1) load_w(s1, 1);
+    load_x(0);
+    store_x(0);
+    if (nkb > 1) load_x(1);
+    barrier_lds();
+    // one K block: the next block's activations (in xr) stored into the other
+    // LDS buffer, the block after that loaded, this block multiplied from LDS
+    auto step = [&](int kb, const GuStage &st, bool tail) {
+        if (!tail || kb + 1 < nkb) store_x((kb + 1) & 1);
+        if (!tail || kb + 2 < nkb) load_x(kb + 2);
+        gu_step(st, xs[kb & 1], col, grp, readlane(sgl, kb), readlane(sul, kb), nsub, accg, accu);
+        barrier_lds();
+    };
+    int kb = 0;
+    for (; kb + 3 < nkb; kb += 2) {   // every load of the two steps is real
+        step(kb, s0, false);
+        load_w(s0, kb + 2);
+        step(kb + 1, s1, false);
+        load_w(s1, kb + 3);
+    }
+    for (; kb < nkb; kb += 2) {       // the last one to three blocks
+        step(kb, s0, true);
+        if (kb + 2 < nkb) load_w(s0, kb + 2);
         if (kb + 1 < nkb) {
-            step(kb + 1, s1);
-            if (kb + 3 < nkb) gu_load(s1, wg, wu, kb + 3, grp);
+            step(kb + 1, s1, true);
+            if (kb + 3 < nkb) load_w(s1, kb + 3);
         }
     }
     // D[i][j]: lane holds column j = col, rows 16q + 4*grp .. +3
@@ -279,70 +295,94 @@ __device__ __forceinline__ void dn_load(DnStage &s, const uint8_t *const (&wd)[2
     }
 }
 
-// acc[nt] += scale[nt] * (h_tile . W^T) over one K block; the lane's h
-// (row col, k = c*64 + grp*16 .. +15) from the LDS tile enters as hi + lo
-// bf16.
-__device__ __forceinline__ void dn_step(const DnStage &s, const float (*hs)[kHRow], int col, int grp,
-                                        const float (&sc)[2], f32x4 (&acc)[2]) {
-    f32x4 td[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+constexpr int kHbRow = 128 + 8;   // bf16 per staged h row (8 of padding)
+
+// One K block of a down tile's h (SUB 16-row subtiles) in LDS, split as hi +
+// lo bf16 (hi = bf16(h), lo = bf16(h - hi)) once, when staged, for all four
+// waves.
+template <int SUB>
+struct DnHs {
+    uint16_t hi[16 * SUB][kHbRow];
+    uint16_t lo[16 * SUB][kHbRow];
+};
+
+// acc[q][nt] += scale[nt] * (h_q . W^T) over one K block for the tile's
+// first nsub 16-row subtiles q (nsub is the same for the whole workgroup):
+// the block's codes are converted once and multiplied into every subtile.
+// The lane's h fragments (row 16q + col, k = c*64 + grp*16 .. +15) are read
+// as hi and lo from LDS.  Per subtile the MFMA chain is the one a lone
+// 16-row tile takes (hi0, lo0, hi1, lo1 for each half), so a row's result
+// does not depend on its subtile.
+template <int SUB>
+__device__ __forceinline__ void dn_step(const DnStage &s, const DnHs<SUB> &hs, int col, int grp, const float (&sc)[2],
+                                        int nsub, f32x4 (&acc)[SUB][2]) {
+    bf16x8 w0[2][2], w1[2][2];   // [c][nt]
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const f32x4 *hp = reinterpret_cast<const f32x4 *>(&hs[col][c * 64 + grp * 16]);
-        f32x4 h[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = hp[q];
-        bf16x8 hi0, lo0, hi1, lo1;
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v0 = h[q][i], v1 = h[q + 2][i];
-                const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1;
-                hi0[q * 4 + i] = b0;
-                lo0[q * 4 + i] = (__bf16)(v0 - (float)b0);
-                hi1[q * 4 + i] = b1;
-                lo1[q * 4 + i] = (__bf16)(v1 - (float)b1);
-            }
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const bf16x8 w0 = e4m3x8_bf16(s.w[nt][c].x, s.w[nt][c].y), w1 = e4m3x8_bf16(s.w[nt][c].z, s.w[nt][c].w);
-            td[nt] = mfma(hi0, w0, td[nt]);
-            td[nt] = mfma(lo0, w0, td[nt]);
-            td[nt] = mfma(hi1, w1, td[nt]);
-            td[nt] = mfma(lo1, w1, td[nt]);
+            w0[c][nt] = e4m3x8_bf16(s.w[nt][c].x, s.w[nt][c].y);
+            w1[c][nt] = e4m3x8_bf16(s.w[nt][c].z, s.w[nt][c].w);
+        }
+#pragma unroll
+    for (int q = 0; q < SUB; ++q) {
+        if (q < nsub) {
+            f32x4 td[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const u32x4 *hp = reinterpret_cast<const u32x4 *>(&hs.hi[q * 16 + col][c * 64 + grp * 16]);
+                const u32x4 *lp = reinterpret_cast<const u32x4 *>(&hs.lo[q * 16 + col][c * 64 + grp * 16]);
+                const bf16x8 hi0 = as_bf16x8(hp[0]), hi1 = as_bf16x8(hp[1]);
+                const bf16x8 lo0 = as_bf16x8(lp[0]), lo1 = as_bf16x8(lp[1]);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    td[nt] = mfma(hi0, w0[c][nt], td[nt]);
+                    td[nt] = mfma(lo0, w0[c][nt], td[nt]);
+                    td[nt] = mfma(hi1, w1[c][nt], td[nt]);
+                    td[nt] = mfma(lo1, w1[c][nt], td[nt]);
+                }
+            }
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[q][nt][i] = fmaf(sc[nt], td[nt][i], acc[q][nt][i]);
         }
     }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[nt][i] = fmaf(sc[nt], td[nt][i], acc[nt][i]);
 }
 
-// D = h_tile . W_dn^T for a 16-row tile and 32 output columns per wave (two
-// 16-column tiles), all of K = I; two K blocks of weight loads in flight, the
-// next K block of h staged in LDS (two 16-byte loads a thread, whole
-// 256-byte row pieces) while one is multiplied.
+// D = h_tile . W_dn^T for a tile of up to 16*SUB rows (SUB 16-row subtiles:
+// 1, the down tiles of the plan, or 4, its 64-row gate/up tiles) and 32
+// output columns per wave (two 16-column tiles), all of K = I.  The expert's
+// down matrix is read once per tile.  Pipeline as in the gate/up unit: the
+// weights two K blocks ahead, h one block ahead in registers (split into
+// hi + lo when stored into the other LDS buffer, at the start of the step
+// before its use), LDS-only barriers, unconditional loads (entry 0's h for
+// rows past the tile) in the steady loop.
+template <int SUB>
 __device__ __forceinline__ void mfma_down_unit(const FfnArgs &a, int bx, int tile) {
-    __shared__ float hs[2][kTileRows][kHRow];
+    static_assert(SUB == kMfmaTileRows / 16 || SUB == kMfmaGuTileRows / 16, "a planned tile height");
+    __shared__ DnHs<SUB> hs[2];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-    const MTile t = resolve_mtile<kMfmaTileRows>(a, tile);
+    const MTile t = resolve_mtile<16 * SUB>(a, tile);
     if (!t.valid) return;
     const ExpertSet &X = t.X;
     const int I = X.inter, H = a.H, nk = a.R * a.k;
     // H is a multiple of 128: a workgroup's 128 columns are all in range or
     // all past it (uniform exit; the waves share the barriers below)
     if (bx * kMfmaWaves * 32 >= H) return;
+    const int nsub = (t.n + 15) >> 4;   // 1 .. SUB
     const int n0 = (bx * kMfmaWaves + wid) * 32;
     const int col = lane & 15, grp = lane >> 4;
     const int nkb = I >> 7;
     // staging: thread t loads values 4*(t%16) .. +3 and 64 + 4*(t%16) .. +3 of
-    // the K block for tile row t/16
+    // the K block for tile rows t/16 + 16q
     const int srow = threadIdx.x >> 4, spiece = threadIdx.x & 15;
-    const int sent = mtile_entry(t, srow, nk);   // rows without an entry stage entry 0's h (results dropped)
-    const float *sh = a.h + (size_t)(sent >= 0 ? sent : 0) * a.hstride + spiece * 4;
-    int oent[4];   // entries of the output rows this lane holds (D layout), loaded early
+    const float *sh[SUB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) oent[i] = mtile_entry(t, 4 * grp + i, nk);
+    for (int q = 0; q < SUB; ++q) {
+        const int sent = mtile_entry(t, srow + 16 * q, nk);   // -1 past the tile: entry 0's h (results dropped)
+        sh[q] = a.h + (size_t)(sent >= 0 ? sent : 0) * a.hstride + spiece * 4;
+    }
     const uint8_t *wd[2];
     float sl[2];
     const float *sbase = reinterpret_cast<const float *>(X.dn_s + (size_t)t.e * X.dn_s_stride);
@@ -351,42 +391,82 @@ __device__ __forceinline__ void mfma_down_unit(const FfnArgs &a, int bx, int til
         wd[nt] = X.dn + (size_t)t.e * X.dn_stride + (size_t)(n0 + nt * 16 + col) * I;
         sl[nt] = lane < nkb ? sbase[(size_t)((n0 + nt * 16) >> 7) * nkb + lane] : 0.0f;
     }
-    f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    f32x4 acc[SUB][2];
+#pragma unroll
+    for (int q = 0; q < SUB; ++q) acc[q][0] = acc[q][1] = f32x4{0, 0, 0, 0};
     DnStage s0, s1;
+    f32x4 hr[SUB][2];
+    auto load_h = [&](int kb) {
+#pragma unroll
+        for (int q = 0; q < SUB; ++q) {
+            hr[q][0] = *reinterpret_cast<const f32x4 *>(sh[q] + kb * 128);
+            hr[q][1] = *reinterpret_cast<const f32x4 *>(sh[q] + kb * 128 + 64);
+        }
+    };
+    auto store_h = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < SUB; ++q) {
+            if (q < nsub) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    uint32_t hi2[2], lo2[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const float v0 = hr[q][half][2 * i], v1 = hr[q][half][2 * i + 1];
+                        const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1;
+                        const __bf16 l0 = (__bf16)(v0 - (float)b0), l1 = (__bf16)(v1 - (float)b1);
+                        hi2[i] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+                        lo2[i] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+                    }
+                    const int k0 = half * 64 + spiece * 4;
+                    *reinterpret_cast<u32x2 *>(&hs[buf].hi[srow + 16 * q][k0]) = u32x2{hi2[0], hi2[1]};
+                    *reinterpret_cast<u32x2 *>(&hs[buf].lo[srow + 16 * q][k0]) = u32x2{lo2[0], lo2[1]};
+                }
+            }
+        }
+    };
     dn_load(s0, wd, 0, grp);
     if (nkb > 1) dn_load(s1, wd, 1, grp);
-    *reinterpret_cast<f32x4 *>(&hs[0][srow][spiece * 4]) = *reinterpret_cast<const f32x4 *>(sh);
-    *reinterpret_cast<f32x4 *>(&hs[0][srow][64 + spiece * 4]) = *reinterpret_cast<const f32x4 *>(sh + 64);
-    __syncthreads();
-    auto step = [&](int kb, const DnStage &s) {
-        f32x4 hn0 = {0, 0, 0, 0}, hn1 = {0, 0, 0, 0};
-        if (kb + 1 < nkb) {
-            hn0 = *reinterpret_cast<const f32x4 *>(sh + (kb + 1) * 128);
-            hn1 = *reinterpret_cast<const f32x4 *>(sh + (kb + 1) * 128 + 64);
-        }
+    load_h(0);
+    store_h(0);
+    if (nkb > 1) load_h(1);
+    barrier_lds();
+    auto step = [&](int kb, const DnStage &st, bool tail) {
+        if (!tail || kb + 1 < nkb) store_h((kb + 1) & 1);
+        if (!tail || kb + 2 < nkb) load_h(kb + 2);
         const float sc[2] = {readlane(sl[0], kb), readlane(sl[1], kb)};
-        dn_step(s, hs[kb & 1], col, grp, sc, acc);
-        if (kb + 1 < nkb) {
-            *reinterpret_cast<f32x4 *>(&hs[(kb + 1) & 1][srow][spiece * 4]) = hn0;
-            *reinterpret_cast<f32x4 *>(&hs[(kb + 1) & 1][srow][64 + spiece * 4]) = hn1;
-        }
-        __syncthreads();
+        dn_step(st, hs[kb & 1], col, grp, sc, nsub, acc);
+        barrier_lds();
     };
-    for (int kb = 0; kb < nkb; kb += 2) {
-        step(kb, s0);
+    int kb = 0;
+    for (; kb + 3 < nkb; kb += 2) {   // every load of the two steps is real
+        step(kb, s0, false);
+        dn_load(s0, wd, kb + 2, grp);
+        step(kb + 1, s1, false);
+        dn_load(s1, wd, kb + 3, grp);
+    }
+    for (; kb < nkb; kb += 2) {       // the last one to three blocks
+        step(kb, s0, true);
         if (kb + 2 < nkb) dn_load(s0, wd, kb + 2, grp);
         if (kb + 1 < nkb) {
-            step(kb + 1, s1);
+            step(kb + 1, s1, true);
             if (kb + 3 < nkb) dn_load(s1, wd, kb + 3, grp);
         }
     }
+    // D[i][j]: lane holds column j = col, rows 16q + 4*grp .. +3
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int o = n0 + nt * 16 + col;
+    for (int q = 0; q < SUB; ++q) {
+        if (q < nsub) {
+            int oent[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = oent[i];
-            if (e >= 0) a.dbuf[(size_t)e * a.H + o] = acc[nt][i];
+            for (int i = 0; i < 4; ++i) oent[i] = mtile_entry(t, 16 * q + 4 * grp + i, nk);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int o = n0 + nt * 16 + col;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (oent[i] >= 0) a.dbuf[(size_t)oent[i] * a.H + o] = acc[q][nt][i];
+            }
         }
     }
 }
