@@ -22,7 +22,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxHidden = 8192;
 constexpr int kMaxInter = 4096;
-constexpr size_t kMaxGroupWords = 8192;   // grouping bitmap: 32 KB of LDS
+constexpr size_t kMaxGroupWords = 8192;   // grouping bitmap and its prefix counts: 64 KB of LDS
 
 inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

@@ -169,10 +169,12 @@ __global__ __launch_bounds__(1024) void k_plan(RouteArgs a) {
 }
 
 // Grouping by expert: a bitmap of rows per expert (rows ascending), counts
-// by popcount, an exclusive scan for the offsets, and each (row, slot) placed
-// at offset + (rows before it that chose the same expert).  With `do_plan`
-// it also writes the arm lists.  One 1024-thread workgroup; COHERENT reads
-// the ids at agent scope (written by other workgroups of the same launch).
+// by popcount (with each word's count of the expert's earlier rows kept in
+// pre), an exclusive scan for the offsets, and each (row, slot) placed at
+// offset + (rows before it that chose the same expert).  With `do_plan` it
+// also writes the arm lists.  One 1024-thread workgroup; COHERENT reads the
+// ids at agent scope (written by other workgroups of the same launch).  LDS:
+// bm and pre, E * ceil(R/32) words each.
 constexpr int kGroupIds = 16;   // (row, slot) entries a grouping thread holds: R*k <= 16 * 1024
 template <bool COHERENT>
 __device__ void group_rows(const RouteArgs &a, int do_plan, uint32_t *bm, int *wave_tot, int *soff) {
@@ -202,10 +204,14 @@ __device__ void group_rows(const RouteArgs &a, int do_plan, uint32_t *bm, int *w
             flag_error(a.err, kErrBadExpertId);
     }
     __syncthreads();
+    int *pre = reinterpret_cast<int *>(bm + E * W);
     const int e = tid;
     int c = 0;
     if (e < E)
-        for (int q = 0; q < W; ++q) c += __popc(bm[e * W + q]);
+        for (int q = 0; q < W; ++q) {
+            pre[e * W + q] = c;
+            c += __popc(bm[e * W + q]);
+        }
     int total;
     const int off = block_excl_scan(e < E ? c : 0, wave_tot, &total);
     if (e < E) {
@@ -222,15 +228,13 @@ __device__ void group_rows(const RouteArgs &a, int do_plan, uint32_t *bm, int *w
         const int ee = idr[u];
         if (i >= n || ee < 0 || ee >= E) continue;
         const int r = i / k;
-        const uint32_t *row = bm + ee * W;
-        int rank = __popc(row[r >> 5] & ((1u << (r & 31)) - 1u));
-        for (int q = 0; q < (r >> 5); ++q) rank += __popc(row[q]);
+        const int rank = pre[ee * W + (r >> 5)] + __popc(bm[ee * W + (r >> 5)] & ((1u << (r & 31)) - 1u));
         a.perm[soff[ee] + rank] = i;
     }
 }
 
 __global__ __launch_bounds__(1024) void k_group(RouteArgs a, int do_plan) {
-    extern __shared__ uint32_t bm[];          // [E][W]
+    extern __shared__ uint32_t bm[];          // [E][W], then pre [E][W]
     __shared__ int wave_tot[40];
     __shared__ int soff[1024];
     group_rows<false>(a, do_plan, bm, wave_tot, soff);
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(1024) void k_group(RouteArgs a, int do_plan) {
 // the count for the next call.  No workgroup waits on another.
 template <int NV>
 __global__ __launch_bounds__(1024) void k_topk_group(RouteArgs a, int s_mode, int do_plan) {
-    extern __shared__ uint32_t bm[];          // [E][W], the grouping's
+    extern __shared__ uint32_t bm[];          // [E][W] and pre [E][W], the grouping's
     __shared__ int wave_tot[40];
     __shared__ int soff[1024];
     __shared__ unsigned ticket_s;
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(1024) void k_topk_group(RouteArgs a, int s_mode, in
 
 // ------------------------------------------------------------------ launchers
 
-size_t group_lds_bytes(int E, int R) { return (size_t)E * (size_t)((R + 31) / 32) * 4u; }
+size_t group_lds_bytes(int E, int R) { return (size_t)E * (size_t)((R + 31) / 32) * 8u; }
 
 // Activation rows staged per block: 64 KB of LDS at most.
 static int router_rows_per_block(int H, int R) {
