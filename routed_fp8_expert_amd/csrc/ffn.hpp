@@ -582,7 +582,7 @@ __global__ __launch_bounds__(256) void k_down_grouped(FfnArgs a, int nmx, int nm
 // then read once per 64 rows instead of once per 16.  A launch of its own,
 // before the GEMV units': its tiles take more registers and LDS than those
 // units, which would otherwise run at its occupancy.
-constexpr int kDownTallRows = 256;
+constexpr int kDownTallRows = 512;
 
 template <int FMT>
 __global__ __launch_bounds__(256, 2) void k_down_mfma(FfnArgs a, int nmx) {

@@ -342,26 +342,26 @@ def test_mfma_tile_shapes(moe, ctx, orc, rows, counts):
 
 
 def test_down_tile_heights_agree(moe, ctx):
-    """Steps of 256 rows and more run the matrix-core down projection on
+    """Steps of 512 rows and more run the matrix-core down projection on
     64-row tiles (a launch of its own), smaller steps on 16-row tiles inside
     the grouped launch: with every expert on the matrix-core arm, the first
-    200 rows of a 300-row step give the bits of a 200-row step."""
+    300 rows of a 600-row step give the bits of a 300-row step."""
     wl = syn.WORKLOADS["a3b_zipf"]
     W = syn.make_layer_weights(wl, 7, "cuda")
-    x = syn.make_x(wl, 7, 300, 0, "cuda")
-    li = syn.make_logits_in(wl, 7, 300, "cuda")
-    r0 = syn.make_residual(wl, 7, 300, "cuda")
+    x = syn.make_x(wl, 7, 600, 0, "cuda")
+    li = syn.make_logits_in(wl, 7, 600, "cuda")
+    r0 = syn.make_residual(wl, 7, 600, "cuda")
     moe.moe_ctx_set_force_arm(ctx, 2)
     try:
-        _say("a3b_zipf: 300 rows against their first 200, every expert on the matrix cores")
-        y3, res3, rt3, _ = _run(moe, ctx, wl, W, x, li, r0)
-        y2, res2, rt2, _ = _run(moe, ctx, wl, W, x[:200].contiguous(), li[:200].contiguous(), r0[:200].contiguous())
+        _say("a3b_zipf: 600 rows against their first 300, every expert on the matrix cores")
+        y6, res6, rt6, _ = _run(moe, ctx, wl, W, x, li, r0)
+        y3, res3, rt3, _ = _run(moe, ctx, wl, W, x[:300].contiguous(), li[:300].contiguous(), r0[:300].contiguous())
     finally:
         moe.moe_ctx_set_force_arm(ctx, 0)
     assert moe.moe_ctx_device_errors(ctx) == 0
-    assert torch.equal(rt3.topk_ids[:200], rt2.topk_ids)
-    assert torch.equal(y3[:200].view(torch.int16), y2.view(torch.int16))
-    assert torch.equal(res3[:200].view(torch.int16), res2.view(torch.int16))
+    assert torch.equal(rt6.topk_ids[:300], rt3.topk_ids)
+    assert torch.equal(y6[:300].view(torch.int16), y3.view(torch.int16))
+    assert torch.equal(res6[:300].view(torch.int16), res3.view(torch.int16))
 
 
 def test_gemv_arm_only_at_64_rows(moe, ctx, orc):
