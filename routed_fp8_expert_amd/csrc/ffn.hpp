@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void k_lead_r1(RouteArgs r, FfnArgs a) {
         if (ticket_s != (unsigned)(nrb - 1) || wid != 0) return;
         int e;
         float w;
-        topk_wave<NV>(r.logits_in ? r.logits_in : r.logits, r.E, r.k, r.logits_in == nullptr, e, w);
+        topk_wave<NV>(r.logits_in ? r.logits_in : r.logits, r.E, r.k, r.logits_in == nullptr, topk_lds<1>(0), e, w);
         if (lane < r.k) {
             r.ids[lane] = e;
             r.w[lane] = w;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
         if (wid == 0) {
             int my_e;
             float my_w;
-            topk_wave<NV>(a.topk_src + (size_t)r * a.E, a.E, a.k, false, my_e, my_w);
+            topk_wave<NV>(a.topk_src + (size_t)r * a.E, a.E, a.k, false, topk_lds<1>(0), my_e, my_w);
             const int es = __builtin_amdgcn_readlane(my_e, slot);
             if (lane == 0) e_s = es;
             // the routing arrays are the caller's (writable); the other

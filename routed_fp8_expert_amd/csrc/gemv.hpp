@@ -213,6 +213,20 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// LDS words (64-bit) one selecting wave uses in topk_regs: the packed
+// candidates and their zero padding in [0, kTopkOut), the selected ones in
+// [kTopkOut, kTopkOut + kMaxTopK).
+constexpr int kTopkOut = 80;
+constexpr int kTopkLds = kTopkOut + kMaxTopK;
+
+// Per-wave top-k scratch of a kernel whose waves 0 .. MAXW-1 may select at
+// the same time (16-byte aligned; one array per kernel and MAXW).
+template <int MAXW>
+__device__ __forceinline__ uint64_t *topk_lds(int wave) {
+    __shared__ __attribute__((aligned(16))) uint64_t words[MAXW * kTopkLds];
+    return words + wave * kTopkLds;
+}
+
 // Softmax over the E logits of one row, the k largest under the top-k order
 // (larger value first, lower index first among equal values) and their
 // renormalised weights, by one wave (all 64 lanes active).
@@ -220,16 +234,23 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // Selection: split the lanes into G >= k groups and take T, the smallest of
 // the G group maxima.  Those are G distinct experts with keys >= T, so the
 // k-th largest key is >= T and every expert of the top-k is a candidate
-// (key >= T).  The candidates (usually a few times k) are packed into lanes
-// 0 .. C-1 by lane permutes; each one's rank is the number of candidates that
-// precede it in the top-k order (larger key, or equal key and lower expert),
-// counted against every candidate in turn, and a last permute puts rank j in
-// lane j.  More than 64 candidates (mass ties) take the round-by-round path.
+// (key >= T).  The candidates (usually a few times k) are written, as 64-bit
+// order keys (key, then the complemented expert index: distinct, larger
+// first in the top-k order), to consecutive words of the wave's LDS scratch
+// (a ballot prefix gives each its word); each candidate's rank is the number
+// of candidates with a larger order key, counted by every lane against the
+// whole list read back as broadcasts (every lane reads the same words); the
+// candidate of rank j < k is written to output word j, which lane j reads.
+// More than 64 candidates (mass ties) take the round-by-round path.
+// The wave's LDS accesses execute in issue order, so no wait separates the
+// writes from the reads; the compiler barriers keep their program order.
 // w_j = exp(l_j - m) / sum_j exp(l_j - m), m the largest logit: the softmax
 // denominator over all E cancels in the renormalisation.  Lane j < k returns
-// slot j.  raw[i] is the logit of expert lane + 64 i (entries past E unused).
+// slot j.  raw[i] is the logit of expert lane + 64 i (entries past E unused);
+// scr is this wave's kTopkLds words of LDS (16-byte aligned).
 template <int NV>
-__device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, int &my_e, float &my_w) {
+__device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, uint64_t *scr, int &my_e,
+                                          float &my_w) {
     static_assert(NV >= 1 && NV <= 16, "logits per lane");
     const int lane = threadIdx.x & (kWave - 1);
     uint32_t key[NV];
@@ -264,53 +285,37 @@ __device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, 
     }
     int sel_key, sel_idx;
     if (cn <= kWave) {
-        // pack the candidates into lanes 0 .. cn-1 (each permute a bijection
-        // of the lanes: non-candidates fill the lanes past its range)
-        uint32_t ck = 0, ci = 0;
         int base = 0;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int cnt = __builtin_popcountll(cm[i]);
-            const int below = lanes_below(cm[i]);
-            const bool cand = (cm[i] >> lane) & 1ull;
-            const int dest = cand ? base + below : (base + cnt + (lane - below)) & (kWave - 1);
-            const uint32_t pk = (uint32_t)__builtin_amdgcn_ds_permute(dest * 4, (int)key[i]);
-            const uint32_t pi = (uint32_t)__builtin_amdgcn_ds_permute(dest * 4, lane + kWave * i);
-            const bool mine = (unsigned)(lane - base) < (unsigned)cnt;
-            ck = mine ? pk : ck;
-            ci = mine ? pi : ci;
-            base += cnt;
+            if ((cm[i] >> lane) & 1ull)
+                scr[base + lanes_below(cm[i])] = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(lane + kWave * i);
+            base += __builtin_popcountll(cm[i]);
         }
-        // rank: candidates ahead of this one (64-bit order key: key, then
-        // the complemented expert index)
-        // every candidate is broadcast to all lanes by a lane permute, 8 at a
-        // time (issued back to back), and compared in vector registers (a
-        // lane read into a scalar register and back costs a pipeline round
-        // trip per candidate); lanes past the candidates hold key 0, which
-        // precedes nothing
-        const uint32_t ckz = lane < cn ? ck : 0u;
-        const uint64_t kp = ((uint64_t)ck << 32) | (uint32_t)~ci;
+        // zeros after the list up to the next multiple of 8 (precede nothing)
+        if (lane < 8) scr[cn + lane] = 0ull;
+        asm volatile("" ::: "memory");
+        const uint64_t me = scr[lane];
+        typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+        const u64x2 *list = reinterpret_cast<const u64x2 *>(scr);
         int r0 = 0, r1 = 0;
-        for (int q0 = 0; q0 < cn; q0 += 8) {
-            uint32_t kq[8], iq[8];
+        for (int q = 0; q < cn; q += 8) {
+            u64x2 o[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                kq[u] = (uint32_t)__builtin_amdgcn_ds_bpermute((q0 + u) * 4, (int)ckz);
-                iq[u] = (uint32_t)__builtin_amdgcn_ds_bpermute((q0 + u) * 4, (int)ci);
-            }
+            for (int u = 0; u < 4; ++u) o[u] = list[q / 2 + u];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int beats = (((uint64_t)kq[u] << 32) | (uint32_t)~iq[u]) > kp ? 1 : 0;
-                if (u & 1)
-                    r1 += beats;
-                else
-                    r0 += beats;
+            for (int u = 0; u < 4; ++u) {
+                r0 += o[u].x > me ? 1 : 0;
+                r1 += o[u].y > me ? 1 : 0;
             }
         }
         const int rank = r0 + r1;
-        const int dest = lane < cn ? rank : lane;
-        sel_key = __builtin_amdgcn_ds_permute(dest * 4, (int)ck);
-        sel_idx = __builtin_amdgcn_ds_permute(dest * 4, (int)ci);
+        asm volatile("" ::: "memory");
+        if (lane < cn && rank < k) scr[kTopkOut + rank] = me;
+        asm volatile("" ::: "memory");
+        const uint64_t sel = scr[kTopkOut + (lane < k ? lane : 0)];
+        sel_key = (int)(uint32_t)(sel >> 32);
+        sel_idx = (int)~(uint32_t)sel;
     } else {
         topk_rounds<NV>(key, k, sel_key, sel_idx);
     }
@@ -325,7 +330,8 @@ __device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, 
 // The same from logits in memory; `coherent` reads them with agent-scope
 // loads (written by other workgroups of the same launch).
 template <int NV>
-__device__ __forceinline__ void topk_wave(const float *l, int E, int k, bool coherent, int &my_e, float &my_w) {
+__device__ __forceinline__ void topk_wave(const float *l, int E, int k, bool coherent, uint64_t *scr, int &my_e,
+                                          float &my_w) {
     const int lane = threadIdx.x & (kWave - 1);
     float raw[NV];
 #pragma unroll
@@ -334,7 +340,7 @@ __device__ __forceinline__ void topk_wave(const float *l, int E, int k, bool coh
         const int ec = e < E ? e : E - 1;
         raw[i] = coherent ? ld_agent(l + ec) : l[ec];
     }
-    topk_regs<NV>(raw, E, k, my_e, my_w);
+    topk_regs<NV>(raw, E, k, scr, my_e, my_w);
 }
 
 // Logits per lane for E experts: 1, 2, 4, 8 or 16.

@@ -247,7 +247,7 @@ __device__ __forceinline__ void block_topk(const RouteArgs &r, const float *lrep
         }
         int e;
         float w;
-        topk_regs<NV>(raw, r.E, r.k, e, w);
+        topk_regs<NV>(raw, r.E, r.k, topk_lds<1>(0), e, w);
         if (lane < r.k) {
             ids_s[lane] = e;
             w_s[lane] = w;

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_topk(RouteArgs a, int s_mode) {
     const float *l = a.logits_in ? a.logits_in + (size_t)r * a.E : a.logits + (size_t)r * a.E;
     int e;
     float w;
-    topk_wave<NV>(l, a.E, a.k, false, e, w);
+    topk_wave<NV>(l, a.E, a.k, false, topk_lds<4>(threadIdx.x >> 6), e, w);
     if (lane < a.k) {
         a.ids[(size_t)r * a.k + lane] = e;
         a.w[(size_t)r * a.k + lane] = w;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(1024) void k_topk_group(RouteArgs a, int s_mode, in
         const float *l = a.logits_in ? a.logits_in + (size_t)r * a.E : a.logits + (size_t)r * a.E;
         int e;
         float w;
-        topk_wave<NV>(l, a.E, a.k, false, e, w);
+        topk_wave<NV>(l, a.E, a.k, false, topk_lds<16>(threadIdx.x >> 6), e, w);
         if (lane < a.k) {
             st_agent(a.ids + (size_t)r * a.k + lane, e);
             st_agent(a.w + (size_t)r * a.k + lane, w);
