@@ -9,6 +9,12 @@
 //
 //   [router | shared gate/up | routed gate/up | down]
 //
+// Every role works a wave at a time on LW-wave workgroups (LW a template
+// parameter: 8 for the 35B-A3B shapes, where halving the workgroup count
+// against 4 waves shortened the layer by 0.6 us: fewer workgroups to
+// dispatch, to poll the routing, to rerun the top-k and to count; 12 and 16
+// waves measured slower, one workgroup a CU leaving the roles on fewer CUs).
+//
 //   router          one wave per router row (and the shared-gate row); the
 //                   last router workgroup to finish raises a ready flag
 //   shared gate/up  the shared expert's h (needs no routing)
@@ -201,22 +207,22 @@ __device__ __forceinline__ void stamp_flush(const LayerGrid &g) {
 // chunk-quad order per slot (see DownRow::dot_perm): element i of slot j
 // goes to float j*HS + ((f/4) * (HS/CPC) + i/CPC) * 4 + f%4, f = i % CPC.
 // HS is the h stride, equal to every slot's intermediate size here.
-template <int CPC, int HS, int KS>
+template <int CPC, int HS, int KS, int NT>
 __device__ __forceinline__ void stage_h(const float *h, int nslots, float *hl) {
-    constexpr int PER = (KS * HS / 2 + 255) / 256;   // 8-byte loads per thread
+    constexpr int PER = (KS * HS / 2 + NT - 1) / NT;   // 8-byte loads per thread
     const uint64_t *src = reinterpret_cast<const uint64_t *>(h);
     const int n2 = nslots * HS / 2;
     uint64_t t[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int i2 = u * 256 + threadIdx.x;
+        const int i2 = u * NT + threadIdx.x;
         t[u] = i2 < n2 ? __hip_atomic_load(const_cast<uint64_t *>(src + i2), __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT)
                        : 0;
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int i2 = u * 256 + threadIdx.x;
+        const int i2 = u * NT + threadIdx.x;
         if (i2 < n2) {
             const int i = 2 * i2, j = i / HS, e = i % HS, c = e / CPC, f = e % CPC;
             *reinterpret_cast<uint64_t *>(hl + j * HS + ((f >> 2) * (HS / CPC) + c) * 4 + (f & 3)) = t[u];
@@ -256,8 +262,8 @@ __device__ __forceinline__ void block_topk(const RouteArgs &r, const float *lrep
     __syncthreads();
 }
 
-template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
-__global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerGrid g) {
+template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS, int LW>
+__global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a, LayerGrid g) {
     // gate/up chunks per lane follow from the router's: H/1024 (fp8), H/2048 (nvfp4)
     constexpr int CH = byte_codes(FMT) ? (NCH + 1) / 2 : (NCH + 3) / 4;
     constexpr int NCG = (KS * kGroups + kWave - 1) / kWave;   // lines of gate/up done words
@@ -285,7 +291,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
         const int n_router = r.logits_in ? 0 : r.E;
         const int n_rows = n_router + (r.wsg ? 1 : 0);
         if (!r.wsg && b == 0 && threadIdx.x == 0) st_agent(r.s, 1.0f);
-        const int row = b * 4 + wid;
+        const int row = b * LW + wid;
         if (row < n_rows) {
             const bool gate_row = row >= n_router;
             u32x4 wv[NCH];
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     if (b < g.nsb) {
         stamp_role(g, 1 | ((uint64_t)k << 8));
         const ExpertSet &X = a.shared;
-        const int i0 = (b * 4 + wid) * P1;
+        const int i0 = (b * LW + wid) * P1;
         if (i0 < X.inter) {
             GateUpRows<FMT, CH, P1> rows;
             rows.load(X, 0, i0, a.H);
@@ -345,7 +351,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
         stamp(g, 3);
         const int e = ids_s[slot];
         const ExpertSet &X = a.routed;
-        const int i0 = (slice * 4 + wid) * P1;
+        const int i0 = (slice * LW + wid) * P1;
         if (i0 < X.inter) {
             GateUpRows<FMT, CH, P1> rows;
             rows.load(X, e, i0, a.H);
@@ -366,7 +372,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     // ---------------------------------------------------------------- down + blend
     constexpr int RPW = kWave / LPR;
     const int sub = lane % LPR;
-    const int o = (b * 4 + wid) * RPW + lane / LPR;
+    const int o = (b * LW + wid) * RPW + lane / LPR;
     const bool live = o < a.H;
     const int nslots = k + (has_shared ? 1 : 0);
     stamp_role(g, 3);
@@ -398,7 +404,7 @@ __global__ __launch_bounds__(256) void k_layer_r1(RouteArgs r, FfnArgs a, LayerG
     }
     block_wait_words<NCG>(done + kDoneGu, need_gu, a.err, g.wait_ticks);
     stamp(g, 5);
-    stage_h<cols_per_chunk<FMT>(), HS, KS>(a.h_rep + (size_t)rep_id * hrep_stride, nslots,
+    stage_h<cols_per_chunk<FMT>(), HS, KS, LW * kWave>(a.h_rep + (size_t)rep_id * hrep_stride, nslots,
                                            reinterpret_cast<float *>(hlds4));
     __syncthreads();
     // Without the norm epilogue the block counts itself on its group's
@@ -505,14 +511,14 @@ static LayerShape layer_shape(const RouteArgs &r, const FfnArgs &a) {
     return s;
 }
 
-static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, unsigned *sync, uint64_t wait_ticks = 0,
-                            uint64_t *stamps = nullptr) {
+static LayerGrid layer_grid(const RouteArgs &r, const FfnArgs &a, int lpr, int lw, unsigned *sync,
+                            uint64_t wait_ticks = 0, uint64_t *stamps = nullptr) {
     LayerGrid g;
     const int n_rows = (r.logits_in ? 0 : r.E) + (r.wsg ? 1 : 0);
-    g.nrb = n_rows > 0 ? (n_rows + 3) / 4 : 1;
-    g.nsb = a.shared.inter > 0 ? (a.shared.inter + 4 * P1 - 1) / (4 * P1) : 0;
-    g.ngb = (a.routed.inter + 4 * P1 - 1) / (4 * P1);
-    const int rows_per_block = 4 * (kWave / lpr);
+    g.nrb = n_rows > 0 ? (n_rows + lw - 1) / lw : 1;
+    g.nsb = a.shared.inter > 0 ? (a.shared.inter + lw * P1 - 1) / (lw * P1) : 0;
+    g.ngb = (a.routed.inter + lw * P1 - 1) / (lw * P1);
+    const int rows_per_block = lw * (kWave / lpr);
     g.ndb = (a.H + rows_per_block - 1) / rows_per_block;
     g.sync = sync;
     g.wait_ticks = wait_ticks;
@@ -526,12 +532,12 @@ static size_t layer_lds(const FfnArgs &a) {
     return h > row ? h : row;
 }
 
-template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
+template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS, int LW>
 static hipError_t layer_launch(const RouteArgs &r, const FfnArgs &a, unsigned *sync, uint64_t wait_ticks,
                                uint64_t *stamps, int64_t stamp_words, hipStream_t st) {
-    const LayerGrid g = layer_grid(r, a, LPR, sync, wait_ticks, stamps);
+    const LayerGrid g = layer_grid(r, a, LPR, LW, sync, wait_ticks, stamps);
     if (stamps && (int64_t)layer_blocks(g, a) * kStampWords > stamp_words) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_layer_r1<FMT, NCH, NV, LPR, DCH, KS, HS>), dim3(layer_blocks(g, a)), dim3(256),
+    hipLaunchKernelGGL((k_layer_r1<FMT, NCH, NV, LPR, DCH, KS, HS, LW>), dim3(layer_blocks(g, a)), dim3(LW * kWave),
                        layer_lds(a), st, r, a, g);
     return hipGetLastError();
 }
@@ -540,7 +546,7 @@ static hipError_t layer_launch(const RouteArgs &r, const FfnArgs &a, unsigned *s
 // current device: the workgroups that wait are then running while the ones
 // they wait on run, and the phases overlap.  (The waits are correct either
 // way: a workgroup only waits on lower-indexed ones.)
-template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS>
+template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS, int LW>
 static bool layer_resident(const RouteArgs &r, const FfnArgs &a) {
     struct Entry { int device; size_t lds; int per_cu; };
     static std::mutex mu;
@@ -557,13 +563,13 @@ static bool layer_resident(const RouteArgs &r, const FfnArgs &a) {
             if (e.device == dev && e.lds == lds) per_cu = e.per_cu;
         if (per_cu < 0) {
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per_cu, reinterpret_cast<const void *>(&k_layer_r1<FMT, NCH, NV, LPR, DCH, KS, HS>), 256,
+                    &per_cu, reinterpret_cast<const void *>(&k_layer_r1<FMT, NCH, NV, LPR, DCH, KS, HS, LW>), LW * kWave,
                     lds) != hipSuccess)
                 return false;
             cache.push_back({dev, lds, per_cu});
         }
     }
-    return layer_blocks(layer_grid(r, a, LPR, nullptr), a) <= per_cu * cus;
+    return layer_blocks(layer_grid(r, a, LPR, LW, nullptr), a) <= per_cu * cus;
 }
 
 // The shapes the single launch is built for: the tiny layer (H 256, E 16,
@@ -575,13 +581,13 @@ static bool layer_resident(const RouteArgs &r, const FfnArgs &a) {
 // whose workgroups do not all fit on the device at once (the 397B-A17B
 // shape, for one: 2049 workgroups against about 768 resident, measured
 // slower than the three launches), take the three-launch path.
-#define MOE_LAYER_SHAPES(X)             \
-    X(kFp8, 1, 1, 8, 1, 17, 128)        \
-    X(kFp8, 4, 4, 32, 1, 9, 512)        \
-    X(kFp8Bf16s, 4, 4, 32, 1, 9, 512)   \
-    X(kInt8Row, 4, 4, 32, 1, 9, 512)    \
-    X(kInt4Row, 4, 4, 16, 1, 9, 512)    \
-    X(kInt4G64, 4, 4, 16, 1, 9, 512)
+#define MOE_LAYER_SHAPES(X)                \
+    X(kFp8, 1, 1, 8, 1, 17, 128, 4)        \
+    X(kFp8, 4, 4, 32, 1, 9, 512, 8)        \
+    X(kFp8Bf16s, 4, 4, 32, 1, 9, 512, 8)   \
+    X(kInt8Row, 4, 4, 32, 1, 9, 512, 8)    \
+    X(kInt4Row, 4, 4, 16, 1, 9, 512, 8)    \
+    X(kInt4G64, 4, 4, 16, 1, 9, 512, 8)
 
 bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
@@ -589,11 +595,10 @@ bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
     const LayerShape s = layer_shape(r, a);
     // every replica group needs a down workgroup: its last one clears the
     // group's done words
-    if (layer_grid(r, a, s.lpr, nullptr).ndb < kGroups) return false;
-#define MOE_MATCH(F, N, V, L, D, K, HSV)                                                               \
+#define MOE_MATCH(F, N, V, L, D, K, HSV, LWV)                                                          \
     if (s.fmt == F && s.nch == N && s.nv == V && s.lpr == L && s.dch == D && nslots <= K &&              \
         a.routed.inter == HSV && (a.shared.inter == 0 || a.shared.inter == HSV))                          \
-        return layer_resident<F, N, V, L, D, K, HSV>(r, a);
+        return layer_grid(r, a, L, LWV, nullptr).ndb >= kGroups && layer_resident<F, N, V, L, D, K, HSV, LWV>(r, a);
     MOE_LAYER_SHAPES(MOE_MATCH)
 #undef MOE_MATCH
     return false;
@@ -603,10 +608,10 @@ hipError_t launch_layer_r1(const RouteArgs &r, const FfnArgs &a, unsigned *sync,
                            uint64_t *stamps, int64_t stamp_words, hipStream_t st) {
     const LayerShape s = layer_shape(r, a);
     const int nslots = a.k + (a.shared.inter > 0 ? 1 : 0);
-#define MOE_GO(F, N, V, L, D, K, HSV)                                                                  \
+#define MOE_GO(F, N, V, L, D, K, HSV, LWV)                                                             \
     if (s.fmt == F && s.nch == N && s.nv == V && s.lpr == L && s.dch == D && nslots <= K &&              \
         a.routed.inter == HSV && (a.shared.inter == 0 || a.shared.inter == HSV))                          \
-        return layer_launch<F, N, V, L, D, K, HSV>(r, a, sync, wait_ticks, stamps, stamp_words, st);
+        return layer_launch<F, N, V, L, D, K, HSV, LWV>(r, a, sync, wait_ticks, stamps, stamp_words, st);
     MOE_LAYER_SHAPES(MOE_GO)
 #undef MOE_GO
     return hipErrorInvalidValue;
