@@ -263,16 +263,16 @@ def cpu_baseline(wl, res, budget_s: float, moe, ctx, stream):
 
 
 PHASES = {
-    0: ["start", "row dot done", "arrival counted", "done word published (last of its sub-counter)"],
-    1: ["start", "-", "-", "h stored", "arrival counted"],
-    2: ["start", "routing done words seen", "top-k done", "h stored", "arrival counted", "-", "-", "-", "-",
+    0: ["start", "row dot done", "done words stored"],
+    1: ["start", "-", "-", "h stored", "done words stored"],
+    2: ["start", "routing done words seen", "top-k done", "h stored", "done words stored", "-", "-", "-", "-",
         "logits arrived"],
     3: ["start", "routing done words seen", "top-k done", "down-row loads issued", "gate/up done words seen",
         "h staged", "blend stored", "group arrival returned", "group line cleared (last of its group)",
         "logits arrived"],
 }
 # table order of the phases per role (stamp word numbers)
-PHASE_ORDER = {0: [1, 2, 3, 4], 1: [1, 4, 5], 2: [1, 2, 10, 3, 4, 5], 3: [1, 2, 10, 3, 4, 5, 6, 7, 8, 9]}
+PHASE_ORDER = {0: [1, 2, 3], 1: [1, 4, 5], 2: [1, 2, 10, 3, 4, 5], 3: [1, 2, 10, 3, 4, 5, 6, 7, 8, 9]}
 ROLES = {0: "router", 1: "shared gate/up", 2: "routed gate/up", 3: "down"}
 
 

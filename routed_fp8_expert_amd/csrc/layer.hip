@@ -15,15 +15,16 @@
 // dispatch, to poll the routing, to rerun the top-k and to count; 12 and 16
 // waves measured slower, one workgroup a CU leaving the roles on fewer CUs).
 //
-//   router          one wave per router row (and the shared-gate row); the
-//                   last router workgroup to finish raises a ready flag
+//   router          one wave per router row (and the shared-gate row); each
+//                   workgroup stores a done word once its logits are stored
 //   shared gate/up  the shared expert's h (needs no routing)
-//   routed gate/up  wait for the ready flag, take the top-k of the logits,
-//                   then a slice of a routed expert's h; count themselves
-//                   done per slot
-//   down            wait for the ready flag, take the top-k, load row o of
-//                   every slot's down matrix at once, wait for the slot
-//                   counters, then blend (the first one publishes the routing)
+//   routed gate/up  wait for every router done word, take the top-k of the
+//                   logits, then a slice of a routed expert's h; store a
+//                   done word
+//   down            wait for the router done words, take the top-k, load row
+//                   o of every slot's down matrix at once, wait for every
+//                   gate/up done word, then blend (the first one publishes
+//                   the routing)
 //
 // Forward progress: the launcher takes this kernel only when every workgroup
 // of the grid can be resident at once (an occupancy query), so all of them
@@ -41,12 +42,13 @@
 // device-coherent stores and loads, which bypass the non-coherent caches), so
 // no cache writeback or invalidate is needed.  A producer waits for its own
 // stores to complete (s_waitcnt 0, every wave, then a barrier) before its
-// arrival atomic, so the stores are visible device-wide before the count
+// done-word stores, so the stores are visible device-wide before the word
 // that announces them; a consumer issues its data loads only after its poll
-// load has returned the flag (in-order issue within a wave, a barrier for
+// load has returned the word (in-order issue within a wave, a barrier for
 // the other waves).  This is the release/acquire pattern restricted to data
 // that is itself accessed atomically.
-// The last down workgroup resets the synchronisation words for the next call;
+// The last down workgroup of each replica group clears that group's done
+// words for the next call;
 // after a timed-out wait they may be left inconsistent, and the host clears
 // them with the error word.
 #include "gemv.hpp"
@@ -60,46 +62,47 @@ constexpr int P1 = kPairsPerWave;
 
 // Synchronisation words (kLayerSyncWords of the ctx, zero between launches).
 //
-// Every phase counts its workgroups on kGroups sub-counters (a workgroup
-// takes sub-counter slice % kGroups), so no counter sees more than a few
-// arrivals: arrivals at one address are serialised by the memory side
-// (about 14 ns each), which made one counter per phase cost microseconds.
-// The last arrival of a sub-counter resets it and writes its done word into
-// each of the kGroups replica lines; a waiting workgroup polls the line of
-// its replica group (block index % kGroups, its XCD) with one wave-wide load
-// per 64 words and a ballot over the done words it needs.  The down
-// workgroups count on a per-group counter once they have read every done
-// word they read; the last of group c clears replica line c.  (Polling the
-// logits themselves instead of a done word, with an unset pattern restored
-// after each launch, measured slower: 768 waves re-reading 1 KB each load
-// the memory side enough to delay the routing by 1.4 us.)
+// Every router and gate/up workgroup announces itself with a done word of
+// its own, stored once its stores have completed, in each of the kGroups
+// replica lines: no arrival counters on the way (an atomic's round trip per
+// hand-off, and arrivals at one address are serialised by the memory side).
+// A waiting workgroup polls the lines of its replica group (block index %
+// kGroups, its XCD) with one wave-wide load per 64 words and a ballot over
+// the words it needs.  The down workgroups count on a per-group counter once
+// they have read every done word they read; the last of group c clears
+// replica line c.  (Polling the logits themselves instead of a done word,
+// with an unset pattern restored after each launch, measured slower: 768
+// waves re-reading 1 KB each load the memory side enough to delay the
+// routing by 1.4 us.)
 //
 //   kSyncDone     kGroups replica lines of kDoneWords words:
-//                   [0, kGroups)                            router sub-counters done
-//                   [kDoneGu, kDoneGu + kMaxSlots*kGroups)  gate/up (slot, sub) done
-//   kSyncRouter   kGroups router sub-counters, kCtrWords apart
-//   kSyncGu       kMaxSlots * kGroups gate/up sub-counters
+//                   [0, kMaxRouterBlocks)        router workgroup b done
+//                   [kDoneGu, kDoneWords)        gate/up workgroup (slot, slice) done:
+//                                                word kDoneGu + slot * ngb + slice
+//                                                (the shared expert is slot k)
 //   kSyncDown     kGroups down counters (one per replica group)
 //   kSyncNorm     the norm epilogue's counter of finished groups
 constexpr int kGroups = kReplicas;
 constexpr int kCtrWords = 16;        // 64 bytes between counters
-constexpr int kDoneWords = 256;      // one replica line set (1 KB)
-constexpr int kDoneGu = 64;
+constexpr int kDoneWords = 512;      // one replica line set (2 KB)
+constexpr int kMaxRouterBlocks = 64;
+constexpr int kDoneGu = kMaxRouterBlocks;
+static_assert(kDoneGu == kWave, "the router done words fill the first 64-word line");
 enum : int {
     kSyncDone = 0,
-    kSyncRouter = kSyncDone + kGroups * kDoneWords,
-    kSyncGu = kSyncRouter + kGroups * kCtrWords,
-    kSyncDown = kSyncGu + kMaxSlots * kGroups * kCtrWords,
+    kSyncDown = kSyncDone + kGroups * kDoneWords,
     kSyncNorm = kSyncDown + kGroups * kCtrWords,
     kSyncWordsTotal = kSyncNorm + kCtrWords
 };
-static_assert(kDoneGu + kMaxSlots * kGroups <= kDoneWords, "done words of one replica");
 static_assert(kSyncWordsTotal <= kLayerSyncWords, "layer synchronisation words exceed the ctx layout");
 
 // Arrivals of sub-counter `sub` when `total` workgroups count round-robin.
 __host__ __device__ constexpr unsigned group_count(int total, int sub) {
     return total > sub ? (unsigned)((total - sub + kGroups - 1) / kGroups) : 0u;
 }
+
+// Gate/up done words of the lines (64 words) a down workgroup polls.
+__host__ __device__ constexpr int gu_lines(int ks, int ngb) { return (ks * ngb + kWave - 1) / kWave; }
 
 // Wave-wide poll of NC lines of 64 done words at p: true once every word
 // c * 64 + lane with need[c] set in that lane is non-zero; false once
@@ -152,8 +155,11 @@ __device__ __forceinline__ bool block_arrive_last(unsigned *ctr, unsigned n, uns
     return *ticket_s == n - 1;
 }
 
-// Done word `word` of every replica line set (threads 0 .. kGroups-1).
-__device__ __forceinline__ void publish_done(unsigned *sync, int word) {
+// Once all this block's waves' stores have completed, done word `word` of
+// every replica line (threads 0 .. kGroups-1).
+__device__ __forceinline__ void block_publish_done(unsigned *sync, int word) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     if (threadIdx.x < kGroups)
         __hip_atomic_store(sync + kSyncDone + threadIdx.x * kDoneWords + word, 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -171,14 +177,14 @@ struct LayerGrid {
 // stamps[block * kStampWords + i] when the workgroup ends (stores to global
 // memory would be waited for by the next barrier and lengthen the phase they
 // measure); word 0 holds the role (0 router, 1 shared gate/up, 2 routed
-// gate/up, 3 down), the slot << 8 and, for a last arrival (router
-// sub-counter, down group), 1 << 16.  Words never stamped read all ones.
+// gate/up, 3 down), the slot << 8 and, for the last arrival of a down
+// group, 1 << 16.  Words never stamped read all ones.
 //   1 start
 //   2 router: row dot done; waiters: the routing's done words seen
-//   3 router: arrival counted; waiters: top-k done
-//   4 router (last of its sub-counter): done word published; gate/up: h
-//     computed and stored; down: down-row loads issued
-//   5 gate/up: arrival counted; down: the gate/up done words seen
+//   3 router: its stores complete and its done words stored; waiters: top-k done
+//   4 gate/up: h computed and stored; down: down-row loads issued
+//   5 gate/up: its stores complete and its done words stored; down: the
+//     gate/up done words seen
 //   6 down: h staged in LDS     7 down: blend stored
 //   8 down: its group arrival returned
 //   9 down (last of its group): the group's line cleared
@@ -266,7 +272,7 @@ template <int FMT, int NCH, int NV, int LPR, int DCH, int KS, int HS, int LW>
 __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a, LayerGrid g) {
     // gate/up chunks per lane follow from the router's: H/1024 (fp8), H/2048 (nvfp4)
     constexpr int CH = byte_codes(FMT) ? (NCH + 1) / 2 : (NCH + 3) / 4;
-    constexpr int NCG = (KS * kGroups + kWave - 1) / kWave;   // lines of gate/up done words
+    constexpr int NCG = gu_lines(KS, HS / (LW * P1));   // lines of gate/up done words
     extern __shared__ f32x4 hlds4[];
     __shared__ unsigned ticket_s;
     __shared__ int ids_s[kMaxSlots];
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
     const float *lrep = a.logits_rep + (size_t)rep_id * r.E;
     const size_t hrep_stride = (size_t)(k + (has_shared ? 1 : 0)) * a.hstride;
     // the routing is ready once every router sub-counter that has arrivals is done
-    const bool need_router[1] = {lane < kGroups && lane < g.nrb};
+    const bool need_router[1] = {lane < g.nrb};
     stamp_begin(g);
     stamp(g, 1);
 
@@ -306,15 +312,9 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
             }
         }
         stamp(g, 2);
-        // every router block's stores are complete before it counts itself
-        const int sub = b % kGroups;
-        const bool last = block_arrive_last(sync + kSyncRouter + sub * kCtrWords, group_count(g.nrb, sub), &ticket_s);
+        // every router block's stores are complete before its done word
+        block_publish_done(sync, b);
         stamp(g, 3);
-        if (last) {
-            publish_done(sync, sub);
-            stamp_role(g, 1u << 16);
-            stamp(g, 4);
-        }
         stamp_flush(g);
         return;
     }
@@ -332,9 +332,7 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
                                       kReplicas);
         }
         stamp(g, 4);
-        const int sub = b % kGroups;
-        if (block_arrive_last(sync + kSyncGu + (k * kGroups + sub) * kCtrWords, group_count(g.nsb, sub), &ticket_s))
-            publish_done(sync, kDoneGu + k * kGroups + sub);
+        block_publish_done(sync, kDoneGu + k * g.ngb + b);
         stamp(g, 5);
         stamp_flush(g);
         return;
@@ -359,10 +357,7 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
                                       kReplicas);
         }
         stamp(g, 4);
-        const int sub = slice % kGroups;
-        if (block_arrive_last(sync + kSyncGu + (slot * kGroups + sub) * kCtrWords, group_count(g.ngb, sub),
-                              &ticket_s))
-            publish_done(sync, kDoneGu + slot * kGroups + sub);
+        block_publish_done(sync, kDoneGu + slot * g.ngb + slice);
         stamp(g, 5);
         stamp_flush(g);
         return;
@@ -398,10 +393,7 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
     // every slot's h is complete once every (slot, sub-counter) with arrivals is done
     bool need_gu[NCG];
 #pragma unroll
-    for (int c = 0; c < NCG; ++c) {
-        const int w = c * kWave + lane, slot = w / kGroups, gsub = w % kGroups;
-        need_gu[c] = slot < nslots && gsub < (slot == k ? g.nsb : g.ngb);
-    }
+    for (int c = 0; c < NCG; ++c) need_gu[c] = c * kWave + lane < nslots * g.ngb;
     block_wait_words<NCG>(done + kDoneGu, need_gu, a.err, g.wait_ticks);
     stamp(g, 5);
     stage_h<cols_per_chunk<FMT>(), HS, KS, LW * kWave>(a.h_rep + (size_t)rep_id * hrep_stride, nslots,
@@ -471,11 +463,9 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
     if (group_last && wid == 0) {
         // nobody reads this group's replica line any more in this launch
         unsigned *line = sync + kSyncDone + rep_id * kDoneWords;
-        if (lane < kGroups) __hip_atomic_store(line + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int c = 0; c < NCG; ++c)
-            if (c * kWave + lane < kMaxSlots * kGroups)
-                __hip_atomic_store(line + kDoneGu + c * kWave + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int c = 0; c <= NCG; ++c)   // the router line, then the gate/up lines
+            __hip_atomic_store(line + c * kWave + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         stamp_role(g, 3 | (1u << 16));
         stamp(g, 9);
     }
@@ -597,8 +587,12 @@ bool layer_r1_supported(const RouteArgs &r, const FfnArgs &a) {
     // group's done words
 #define MOE_MATCH(F, N, V, L, D, K, HSV, LWV)                                                          \
     if (s.fmt == F && s.nch == N && s.nv == V && s.lpr == L && s.dch == D && nslots <= K &&              \
-        a.routed.inter == HSV && (a.shared.inter == 0 || a.shared.inter == HSV))                          \
-        return layer_grid(r, a, L, LWV, nullptr).ndb >= kGroups && layer_resident<F, N, V, L, D, K, HSV, LWV>(r, a);
+        a.routed.inter == HSV && (a.shared.inter == 0 || a.shared.inter == HSV)) {                        \
+        const LayerGrid g = layer_grid(r, a, L, LWV, nullptr);                                           \
+        return g.ndb >= kGroups && g.nrb <= kMaxRouterBlocks &&                                          \
+               kDoneGu + kWave * gu_lines(K, HSV / (LWV * P1)) <= kDoneWords &&                          \
+               layer_resident<F, N, V, L, D, K, HSV, LWV>(r, a);                                          \
+    }
     MOE_LAYER_SHAPES(MOE_MATCH)
 #undef MOE_MATCH
     return false;
