@@ -371,6 +371,12 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
     const bool live = o < a.H;
     const int nslots = k + (has_shared ? 1 : 0);
     stamp_role(g, 3);
+    // the shared expert's down rows need no routing: with every slot present
+    // (the instantiated shape, the shared expert last) they load before the
+    // routing wait, ahead of the routed weight stream
+    DownRow<FMT, LPR, DCH> rows[KS];
+    const bool full = has_shared && k == KS - 1;
+    if (full) rows[KS - 1].load(a.shared, 0, o, sub, live);
     block_wait_words<1>(done, need_router, a.err, g.wait_ticks);
     stamp(g, 2);
     block_topk<NV>(r, lrep, ids_s, w_s, g);
@@ -379,10 +385,9 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
         r.ids[lane] = ids_s[lane];
         r.w[lane] = w_s[lane];
     }
-    DownRow<FMT, LPR, DCH> rows[KS];
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-        if (j < nslots) {
+        if (j < nslots && !(full && j == KS - 1)) {
             const bool sh = j == k;
             rows[j].load(sh ? a.shared : a.routed, sh ? 0 : ids_s[j], o, sub, live);
         }
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
     const float s_gate = has_shared ? ld_agent(a.s) : 0.0f;
     const float res_in = a.res ? bf16_to_f32(a.res[live ? o : 0]) : 0.0f;   // unconditional load (clamped)
     stamp(g, 4);
-    // every slot's h is complete once every (slot, sub-counter) with arrivals is done
+    // every slot's h is complete once every gate/up workgroup's done word is set
     bool need_gu[NCG];
 #pragma unroll
     for (int c = 0; c < NCG; ++c) need_gu[c] = c * kWave + lane < nslots * g.ngb;
