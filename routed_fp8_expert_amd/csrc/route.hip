@@ -33,9 +33,22 @@ __global__ __launch_bounds__(256) void k_router(RouteArgs a) {
     for (int r0 = 0; r0 < a.R; r0 += RB) {
         const int nr = min(RB, a.R - r0);
         __syncthreads();
-        for (int i = threadIdx.x; i < nr * nch; i += 256) {
-            const int rr = i / nch, c = i - rr * nch;
-            xs[rr * nch + c] = ld16(a.x + (size_t)(r0 + rr) * a.ldx + (size_t)c * 8);
+        // every staging load issued before the first store (a load feeding a
+        // store in a loop with a run-time trip count ran one latency per
+        // iteration); loads past the block read chunk 0 of row r0, unused
+        constexpr int PER = (RB * NCH * kWave + 255) / 256;
+        u32x4 t[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int i = u * 256 + (int)threadIdx.x;
+            const int ic = i < nr * nch ? i : 0;
+            const int rr = ic / nch, c = ic - rr * nch;
+            t[u] = ld16(a.x + (size_t)(r0 + rr) * a.ldx + (size_t)c * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int i = u * 256 + (int)threadIdx.x;
+            if (i < nr * nch) xs[i] = t[u];
         }
         __syncthreads();
         if (!live) continue;
