@@ -96,7 +96,8 @@ enum : int {
 };
 static_assert(kSyncWordsTotal <= kLayerSyncWords, "layer synchronisation words exceed the ctx layout");
 
-// Arrivals of sub-counter `sub` when `total` workgroups count round-robin.
+// Arrivals at the down counter of replica group `sub` when `total` down
+// workgroups are spread over the groups round-robin.
 __host__ __device__ constexpr unsigned group_count(int total, int sub) {
     return total > sub ? (unsigned)((total - sub + kGroups - 1) / kGroups) : 0u;
 }
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
     const unsigned *done = sync + kSyncDone + rep_id * kDoneWords;   // this group's replica line
     const float *lrep = a.logits_rep + (size_t)rep_id * r.E;
     const size_t hrep_stride = (size_t)(k + (has_shared ? 1 : 0)) * a.hstride;
-    // the routing is ready once every router sub-counter that has arrivals is done
+    // the routing is ready once every router workgroup's done word is set
     const bool need_router[1] = {lane < g.nrb};
     stamp_begin(g);
     stamp(g, 1);
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(LW * kWave) void k_layer_r1(RouteArgs r, FfnArgs a,
     __syncthreads();
     // Without the norm epilogue the block counts itself on its group's
     // counter now: it has read every done word it reads (and every gate/up
-    // block counted itself before its word was set).  The atomic's latency
+    // block stored its done word after its h stores completed).  The atomic's latency
     // hides behind the blend; the last block of the group clears the group's
     // replica line at the end.  With the epilogue the count comes after the
     // outputs are stored (below).
