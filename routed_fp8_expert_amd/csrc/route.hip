@@ -18,12 +18,19 @@ namespace moe {
 // wave forms its row's RB partial sums and reduces them together (the
 // transposing reduction: the same bits as the one-row wave sum), so lane
 // group i of the wave ends with row r0 + i.
+#ifndef MOE_ROUTER_WAVES
+#define MOE_ROUTER_WAVES 8
+#endif
+// Waves (router rows) per workgroup: every workgroup stages the activation
+// rows, so more rows a workgroup stage less in all.
+constexpr int kRouterWaves = MOE_ROUTER_WAVES;
+
 template <int NCH, int RB>
-__global__ __launch_bounds__(256) void k_router(RouteArgs a) {
+__global__ __launch_bounds__(kRouterWaves * kWave) void k_router(RouteArgs a) {
     extern __shared__ u32x4 xs[];    // [RB][H/8] 16-byte activation chunks
-    constexpr int SPAN = kWave / RB;
+    constexpr int SPAN = kWave / RB, NT = kRouterWaves * kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int row = blockIdx.x * kRouterWaves + (threadIdx.x >> 6);
     const bool live = row < a.E + (a.wsg ? 1 : 0);
     const bool gate_row = row >= a.E;
     const int nch = a.H >> 3;
@@ -36,18 +43,18 @@ __global__ __launch_bounds__(256) void k_router(RouteArgs a) {
         // every staging load issued before the first store (a load feeding a
         // store in a loop with a run-time trip count ran one latency per
         // iteration); loads past the block read chunk 0 of row r0, unused
-        constexpr int PER = (RB * NCH * kWave + 255) / 256;
+        constexpr int PER = (RB * NCH * kWave + NT - 1) / NT;
         u32x4 t[PER];
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int i = u * 256 + (int)threadIdx.x;
+            const int i = u * NT + (int)threadIdx.x;
             const int ic = i < nr * nch ? i : 0;
             const int rr = ic / nch, c = ic - rr * nch;
             t[u] = ld16(a.x + (size_t)(r0 + rr) * a.ldx + (size_t)c * 8);
         }
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int i = u * 256 + (int)threadIdx.x;
+            const int i = u * NT + (int)threadIdx.x;
             if (i < nr * nch) xs[i] = t[u];
         }
         __syncthreads();
@@ -309,7 +316,7 @@ static hipError_t router_nch(const RouteArgs &a, hipStream_t st) {
     const int rows = a.E + (a.wsg ? 1 : 0);
     const int rb = router_rows_per_block(a.H, a.R);
     const size_t lds = (size_t)rb * (size_t)a.H * 2;
-    dim3 grid((rows + 3) / 4), block(256);
+    dim3 grid((rows + kRouterWaves - 1) / kRouterWaves), block(kRouterWaves * kWave);
     switch (rb) {
         case 2: hipLaunchKernelGGL((k_router<NCH, 2>), grid, block, lds, st, a); break;
         case 4: hipLaunchKernelGGL((k_router<NCH, 4>), grid, block, lds, st, a); break;
