@@ -108,7 +108,9 @@ __host__ __device__ constexpr int gu_lines(int ks, int ngb) { return (ks * ngb +
 // Wave-wide poll of NC lines of 64 done words at p: true once every word
 // c * 64 + lane with need[c] set in that lane is non-zero; false once
 // `ticks` ticks of the constant clock have passed since the first poll (at
-// least one poll is made).  Every lane of the wave calls it.
+// least one poll is made).  Every lane of the wave calls it.  The next poll
+// follows the last one's return with no sleep between (one wave per waiting
+// workgroup polls; a sleep of 128 cycles measured 0.07 us a layer slower).
 template <int NC>
 __device__ __forceinline__ bool poll_words(const unsigned *p, const bool (&need)[NC], uint64_t ticks) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -122,7 +124,6 @@ __device__ __forceinline__ bool poll_words(const unsigned *p, const bool (&need)
         for (int c = 0; c < NC; ++c) missing |= need[c] && v[c] == 0u;
         if (__builtin_amdgcn_ballot_w64(missing) == 0) return true;
         if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) return false;
-        __builtin_amdgcn_s_sleep(2);
     }
 }
 
