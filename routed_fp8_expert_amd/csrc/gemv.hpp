@@ -232,9 +232,9 @@ __device__ __forceinline__ uint64_t *topk_lds(int wave) {
 // renormalised weights, by one wave (all 64 lanes active).
 //
 // Selection: split the lanes into G >= k groups and take T, the smallest of
-// the G group maxima.  Those are G distinct experts with keys >= T, so the
-// k-th largest key is >= T and every expert of the top-k is a candidate
-// (key >= T).  The candidates (usually a few times k) are written, as 64-bit
+// the G group maxima (for 8 < k < 16: the k-th largest of the 16 maxima).
+// Those are G (k) distinct experts with keys >= T, so the k-th largest key
+// is >= T and every expert of the top-k is a candidate (key >= T).  The candidates (usually a few times k) are written, as 64-bit
 // order keys (key, then the complemented expert index: distinct, larger
 // first in the top-k order), to consecutive words of the wave's LDS scratch
 // (a ballot prefix gives each its word); each candidate's rank is the number
@@ -267,15 +267,32 @@ __device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, 
     uint32_t g = lmax;
     g = mx(g, (uint32_t)dpp<kDppXor1>(0, (int)g));
     g = mx(g, (uint32_t)dpp<kDppXor2>(0, (int)g));
-    if (k <= 8) {
-        g = mx(g, (uint32_t)dpp<kDppHalfMirror>(0, (int)g));
+    uint32_t thr;
+    if (k > 8 && k < 16) {
+        // T = the k-th largest of the 16 group maxima (lane 4h holds group
+        // h's; ties ranked by group index): k distinct experts are >= T, and
+        // T is much tighter than the smallest maximum (about 15 candidates
+        // against 50 at 512 experts, top-10)
+        const int gi = lane >> 2;
+        int rank = 0;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)g, 4 * h);
+            rank += (o > g || (o == g && h < gi)) ? 1 : 0;
+        }
+        const uint64_t at = __builtin_amdgcn_ballot_w64(rank == k - 1 && (lane & 3) == 0);
+        thr = (uint32_t)__builtin_amdgcn_readlane((int)g, __builtin_ctzll(at));
     } else {
-        g = mn(g, (uint32_t)dpp<kDppHalfMirror>(-1, (int)g));
+        if (k <= 8) {
+            g = mx(g, (uint32_t)dpp<kDppHalfMirror>(0, (int)g));
+        } else {
+            g = mn(g, (uint32_t)dpp<kDppHalfMirror>(-1, (int)g));
+        }
+        g = mn(g, (uint32_t)dpp<kDppMirror>(-1, (int)g));
+        g = mn(g, (uint32_t)dpp<kDppBcast15, 0xa>(-1, (int)g));
+        g = mn(g, (uint32_t)dpp<kDppBcast31, 0xc>(-1, (int)g));
+        thr = (uint32_t)__builtin_amdgcn_readlane((int)g, kWave - 1);
     }
-    g = mn(g, (uint32_t)dpp<kDppMirror>(-1, (int)g));
-    g = mn(g, (uint32_t)dpp<kDppBcast15, 0xa>(-1, (int)g));
-    g = mn(g, (uint32_t)dpp<kDppBcast31, 0xc>(-1, (int)g));
-    const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)g, kWave - 1);
     uint64_t cm[NV];
     int cn = 0;
 #pragma unroll
