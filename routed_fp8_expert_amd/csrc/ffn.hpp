@@ -267,8 +267,7 @@ __global__ __launch_bounds__(256) void k_lead_r1(RouteArgs r, FfnArgs a) {
 // gate/up of the routed experts of a one-row layer, and of a step of a few
 // rows without grouping.  Grid (slices, slots, R): block (b, j, r) takes slot
 // j of row r (its expert from the published ids, h row r*k + j) and its slice
-// b; each such block also warms its share of that expert's down matrix.  With
-// several rows slot k is the shared expert, run by the blocks of row 0 for
+// b.  With several rows slot k is the shared expert, run by the blocks of row 0 for
 // every row (weights loaded once; h rows R*k + r); at one row the lead kernel
 // runs it.
 //
@@ -327,24 +326,19 @@ __global__ __launch_bounds__(256) void k_gate_up_r1(FfnArgs a) {
         return;
     }
     const ExpertSet &X = a.routed;
-    // activations, weights and warming loads all in flight before the first
-    // wait (a wave past the expert's rows loads clamped rows as zeros and
-    // stores nothing).  The warming is folded after the dot for 32-code
-    // chunks (the dot then waits for its own loads only: 397B-A17B one row
-    // 17.6 -> 15.4 us) and before it for byte codes (its registers would
-    // cost the fp8 kernel a wave per SIMD: 2 rows 14.1 -> 15.5 us).
-    constexpr bool FOLD_LATE = !byte_codes(FMT);
+    // activations and weights in flight before the first wait (a wave past
+    // the expert's rows loads clamped rows as zeros and stores nothing).
+    // (Warming the expert's down matrix into the memory-side cache from here
+    // for the down launch measured slower: 35B-A3B 2 / 4 / 8 rows 19.4 /
+    // 31.4 / 54.0 against 16.4 / 26.2 / 45.3 us, 397B-A17B one row 32.1
+    // against 29.6 us.)
     u32x4 x[CH][XQ];
     Rows::load_x(a.x + (size_t)r * a.ldx, a.H, x);
     Rows rows;
     rows.load(X, e, i0, a.H);
-    WarmSlice warm;
-    warm.issue(X.dn + (size_t)e * X.dn_stride, (size_t)a.H * row_bytes<FMT>(X.inter), blockIdx.x, gridDim.x);
-    if (!FOLD_LATE) sink_word(a.sink, warm.fold());
     float acc[2 * P];
     rows.partial(x, a.H, acc);
     rows.finish(acc, X.inter, i0, a.h + ((size_t)r * a.k + slot) * a.hstride);
-    if (FOLD_LATE) sink_word(a.sink, warm.fold());
 }
 
 // Down GEMV fused with the blend, for one row (blockIdx.y) of a one-row
