@@ -35,13 +35,17 @@ using moe::kWordSink;
 constexpr int64_t kDefaultWaitUs = 10000;   // a one-launch layer's wait gives up after 10 ms
 constexpr int kDenseMaxK = 8192;         // a wave's 64 lanes hold one scale per 128-wide block
 constexpr int kDenseMaxRows = 1 << 20;   // matrix-core grid rows stay far below 65535
-constexpr int kDefaultFewRows = 8;       // steps of 2..8 rows: one GEMV per row and slot (measured)
+// steps of 2..16 rows: one GEMV per row and slot (measured against the grouped
+// path at 8 / 10 / 12 / 16 / 24 / 32 rows: 45.2 / 51.9 / 58.7 / 74.8 / 103.0 /
+// 132.7 against 45.1 / 58.0 / 64.0 / 75.6 / 94.7 / 110.3 us)
+constexpr int kDefaultFewRows = 16;
 constexpr int kFewRowsAuto = -1;         // ctx default: kDefaultFewRows where the per-row h fits kFewRowsHBytes
 constexpr size_t kFewRowsHBytes = 32 * 1024;
 constexpr int kFusedTopkRows = 4;        // few-rows steps up to 4 rows select in the gate/up blocks (measured)
 constexpr int kDefaultMfmaMinRows = 4;   // rows per expert from which the MFMA arm pays (measured)
-// Step rows from which the MFMA arm runs: where the few-rows path ends (up to
-// 8 rows by default; the grouped path below keeps GEMV-only bits there).
+// Step rows from which the MFMA arm runs in grouped steps (grouped steps
+// start past the few-rows path, 16 rows by default; with the few-rows path
+// set lower, the grouped path below 9 rows keeps GEMV-only bits).
 // Measured against 32: 12 rows 84.1 -> 67.2 us, 16 rows 102.0 -> 78.5, 24
 // rows 135.7 -> 98.2 (the shared expert's rows leave one long GEMV task); at
 // 4 rows it was slower.

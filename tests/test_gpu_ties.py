@@ -15,8 +15,8 @@ records, that this kernel ran:
   R = 1, single launch     every waiting workgroup of the one-launch layer
   R = 1, three launches    the last router workgroup of the lead kernel
   R <= 4, few rows         the gate/up workgroups of the few-rows path
-  R 5..8, few rows         the top-k launch
-  R >= 9, grouped          the top-k + grouping launch (grouping checked too)
+  R 5..16, few rows        the top-k launch
+  R >= 17, grouped         the top-k + grouping launch (grouping checked too)
   moe_route                the top-k launch (R = 1) and top-k + grouping
 Ids, their order and the grouping must equal the oracle's bit for bit; the
 weights within 1e-5 and the layer output within the layer's tolerance.
@@ -146,10 +146,10 @@ def test_one_row_router_ties(moe, orc, name, path, expect, where):
     c.close()
 
 
-# R >= 2: the few-rows fused top-k (<= 4 rows), the top-k launch (5..8),
-# the top-k + grouping launch (>= 9)
+# R >= 2: the few-rows fused top-k (<= 4 rows), the top-k launch (5..16),
+# the top-k + grouping launch (>= 17)
 MULTI = [(3, {"topk": False, "gate_up": True}), (4, {"topk": False}), (6, {"topk": True}),
-         (8, {"topk": True}), (16, {"topk": True}), (64, {"topk": True})]
+         (8, {"topk": True}), (16, {"topk": True}), (24, {"topk": True}), (64, {"topk": True})]
 
 
 @pytest.mark.parametrize("rows,expect", MULTI)

@@ -1,7 +1,7 @@
 """moe_layer_forward_static (the entry point that allocates nothing: its
 workspace is the library's static device scratch) against
 moe_layer_forward with a caller's workspace, through the C ABI, on calls in a
-row that shrink: 16 rows (grouped, matrix-core arm), 5 rows (few-rows path),
+row that shrink: 32 rows (grouped, matrix-core arm), 5 rows (few-rows path),
 1 row (the one-launch layer), each compared bit for bit (ids, weights, shared
 gate, grouping, y and the blended residual), which is within the layer's
 tolerance a fortiori.  Also: a call whose workspace exceeds the scratch is
@@ -63,7 +63,7 @@ def _case(moe, ctx, wl, W, rows, layer):
     return out
 
 
-@pytest.mark.parametrize("seq", [[("a3b_multi", 16), ("a3b_multi", 5), ("a3b", 1)],
+@pytest.mark.parametrize("seq", [[("a3b_multi", 32), ("a3b_multi", 5), ("a3b", 1)],
                                  [("a3b_multi", 64), ("tiny", 1)]])
 def test_static_scratch_equals_workspace_entry_point(moe, seq):
     ctx = moe.Ctx(0)
