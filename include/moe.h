@@ -199,9 +199,9 @@ MOE_API int moe_ctx_set_one_row_path(moe_ctx *ctx, int path);
  * routing, then one GEMV per (row, slot) with the one-row kernels (the shared
  * expert's gate/up once for all rows), down fused with the blend per row.
  * Each row's result has the bits of a one-row call.  0 turns it off; -1 (the
- * default; env MOE_FEW_ROWS) chooses: 16 rows where a row's k+1 intermediate
- * vectors take at most 32 KB (the 35B-A3B shape), else 0 (the 397B-A17B shape
- * measured faster grouped).  MOE_ERR_INVALID_ARG for rows < -1. */
+ * default; env MOE_FEW_ROWS) chooses E / (2 top_k) rows, at least 8 and at
+ * most 32 (grouping pays once rows share experts: 16 rows on the 35B-A3B
+ * shape, 25 on the 397B-A17B shape).  MOE_ERR_INVALID_ARG for rows < -1. */
 MOE_API int moe_ctx_set_few_rows(moe_ctx *ctx, int rows);
 /* Device-side error word: kernels that meet an expert id outside [0, E)
  * skip it and set bit 0; a wait of the one-launch layer that reached the

@@ -35,17 +35,25 @@ using moe::kWordSink;
 constexpr int64_t kDefaultWaitUs = 10000;   // a one-launch layer's wait gives up after 10 ms
 constexpr int kDenseMaxK = 8192;         // a wave's 64 lanes hold one scale per 128-wide block
 constexpr int kDenseMaxRows = 1 << 20;   // matrix-core grid rows stay far below 65535
-// steps of 2..16 rows: one GEMV per row and slot (measured against the grouped
-// path at 8 / 10 / 12 / 16 / 24 / 32 rows: 45.2 / 51.9 / 58.7 / 74.8 / 103.0 /
-// 132.7 against 45.1 / 58.0 / 64.0 / 75.6 / 94.7 / 110.3 us)
-constexpr int kDefaultFewRows = 16;
-constexpr int kFewRowsAuto = -1;         // ctx default: kDefaultFewRows where the per-row h fits kFewRowsHBytes
-constexpr size_t kFewRowsHBytes = 32 * 1024;
-constexpr int kFusedTopkRows = 4;        // few-rows steps up to 4 rows select in the gate/up blocks (measured)
+// Steps of 2 .. E / (2k) rows (at least 8, at most 32) run as few rows: one
+// GEMV per row and slot, no grouping.  Grouping pays once rows share experts;
+// with R k <= E / 2 they rarely do.  Measured against the grouped path:
+// 35B-A3B (E / 2k = 16) at 10 / 12 / 16 / 24 / 32 rows 51.9 / 58.7 / 74.8 /
+// 103.0 / 132.7 against 58.0 / 64.0 / 75.6 / 94.7 / 110.3 us; 397B-A17B
+// (E / 2k = 25) at 2 / 8 / 12 / 16 / 24 rows 46.9 / 128.1 / 183.8 / 236.3 /
+// 346.0 against 56.6 / 155.5 / 220.0 / 276.8 / 382.3 us.
+constexpr int kFewRowsMin = 8, kFewRowsMax = 32;
+constexpr int kFewRowsAuto = -1;         // ctx default: the rule above
+// Few-rows steps up to this many rows select in the gate/up blocks (every
+// block reruns its row's top-k) instead of in a top-k launch: 8 rows up to
+// 256 experts (35B-A3B 6 / 8 rows 36.7 / 45.2 -> 35.0 / 44.8 us against 4
+// rows; no gain at 12 and 16), 4 above (397B-A17B at 8 rows: 128 against
+// 141 us with the selection of 512 experts in every block).
+inline int fused_topk_rows(int E) { return E <= 256 ? 8 : 4; }
 constexpr int kDefaultMfmaMinRows = 4;   // rows per expert from which the MFMA arm pays (measured)
 // Step rows from which the MFMA arm runs in grouped steps (grouped steps
-// start past the few-rows path, 16 rows by default; with the few-rows path
-// set lower, the grouped path below 9 rows keeps GEMV-only bits).
+// start past the few-rows path by default; with the few-rows path set lower,
+// the grouped path below 9 rows keeps GEMV-only bits).
 // Measured against 32: 12 rows 84.1 -> 67.2 us, 16 rows 102.0 -> 78.5, 24
 // rows 135.7 -> 98.2 (the shared expert's rows leave one long GEMV task); at
 // 4 rows it was slower.
@@ -293,16 +301,13 @@ int do_ffn(moe_ctx *c, const moe::FfnArgs &a, hipStream_t st) {
 // Steps of a few rows (2 .. few_rows, the default arm choice): no grouping;
 // the one-row gate/up and down+blend kernels over every (row, slot), the
 // shared expert's gate/up once for all rows.
-// The automatic choice: the few-rows down kernel stages a row's k+1 h vectors
-// in every workgroup; where they exceed 32 KB (the 397B-A17B shape: 45 KB) the
-// grouped path measured faster at every row count.
+// The automatic choice: E / (2k) rows, at least kFewRowsMin, at most
+// kFewRowsMax (see kFewRowsMin).
 bool few_rows_path(const moe_ctx *c, const moe_layer_weights *w, int R) {
     if (R < 2 || c->force_arm != 0) return false;
     int lim = c->few_rows;
-    if (lim == kFewRowsAuto) {
-        const size_t h = (size_t)(w->top_k + 1) * (size_t)std::max(w->inter, w->shared_inter) * 4;
-        lim = h <= kFewRowsHBytes ? kDefaultFewRows : 0;
-    }
+    if (lim == kFewRowsAuto)
+        lim = std::min(kFewRowsMax, std::max(kFewRowsMin, w->n_experts / (2 * std::max(1, w->top_k))));
     return R <= lim;
 }
 
@@ -585,7 +590,7 @@ MOE_API int moe_layer_forward_norm(moe_ctx *c, const moe_layer_weights *w, const
         // the router GEMV (unless logits are given); the gate/up blocks take
         // their rows' top-k and publish the routing; the grouping arrays are
         // written only when the caller asked for them
-        if (R <= kFusedTopkRows) {
+        if (R <= fused_topk_rows(w->n_experts)) {
             if (!logits_in) {
                 rc = launch(c, MOE_K_ROUTER, st, [&] { return moe::launch_router(ra, st); });
                 if (rc) return rc;

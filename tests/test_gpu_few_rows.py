@@ -1,4 +1,4 @@
-"""GPU tests of the few-rows path (steps of 2 to 16 rows at the default arm
+"""GPU tests of the few-rows path (steps of 2 to E / 2k rows at the default arm
 choice: no grouping, one GEMV per row and slot with the one-row kernels, down
 fused with the blend per row).  Its rows have one-row bits, so it must give
 exactly the grouped path's bits (which also equal one-row calls); parity

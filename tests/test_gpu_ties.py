@@ -14,9 +14,10 @@ Each case names the kernel that selects and asserts, from the ctx's launch
 records, that this kernel ran:
   R = 1, single launch     every waiting workgroup of the one-launch layer
   R = 1, three launches    the last router workgroup of the lead kernel
-  R <= 4, few rows         the gate/up workgroups of the few-rows path
-  R 5..16, few rows        the top-k launch
-  R >= 17, grouped         the top-k + grouping launch (grouping checked too)
+  R <= 8 (4 above 256 experts), few rows
+                           the gate/up workgroups of the few-rows path
+  R up to E/2k, few rows   the top-k launch
+  R > E/2k, grouped        the top-k + grouping launch (grouping checked too)
   moe_route                the top-k launch (R = 1) and top-k + grouping
 Ids, their order and the grouping must equal the oracle's bit for bit; the
 weights within 1e-5 and the layer output within the layer's tolerance.
@@ -146,10 +147,11 @@ def test_one_row_router_ties(moe, orc, name, path, expect, where):
     c.close()
 
 
-# R >= 2: the few-rows fused top-k (<= 4 rows), the top-k launch (5..16),
-# the top-k + grouping launch (>= 17)
-MULTI = [(3, {"topk": False, "gate_up": True}), (4, {"topk": False}), (6, {"topk": True}),
-         (8, {"topk": True}), (16, {"topk": True}), (24, {"topk": True}), (64, {"topk": True})]
+# R >= 2 (E / 2k = 16 here): the few-rows fused top-k (<= 8 rows), the
+# top-k launch (9..16), the top-k + grouping launch (>= 17)
+MULTI = [(3, {"topk": False, "gate_up": True}), (4, {"topk": False}), (6, {"topk": False}),
+         (8, {"topk": False, "gate_up": True}), (12, {"topk": True}), (16, {"topk": True}),
+         (24, {"topk": True}), (64, {"topk": True})]
 
 
 @pytest.mark.parametrize("rows,expect", MULTI)
@@ -163,15 +165,18 @@ def test_multi_row_given_logits(moe, orc, rows, expect):
     c.close()
 
 
-@pytest.mark.parametrize("rows", [5, 16])
-def test_multi_row_given_logits_nvfp4(moe, orc, rows):
-    """512 experts (eight logits a lane), top-10."""
+@pytest.mark.parametrize("rows,expect", [(4, {"topk": False, "gate_up": True}), (8, {"topk": True}),
+                                         (16, {"topk": True}), (32, {"topk": True})])
+def test_multi_row_given_logits_nvfp4(moe, orc, rows, expect):
+    """512 experts (eight logits a lane), top-10 (E / 2k = 25: few rows with
+    the fused top-k up to 4 rows, with the top-k launch at 8 and 16, grouped
+    at 32)."""
     wl = syn.WORKLOADS["a17b"]
     W = syn.make_layer_weights(wl, 0, "cuda")
     x = syn.make_x(wl, 0, rows, 0, "cuda")
     li = torch.from_numpy(tie_rows(wl.n_experts, wl.top_k, rows, 200 + rows)).cuda()
     c = _ctx(moe)
-    _layer_case(moe, orc, wl, W, x, li, c, {"topk": True}, f"a17b {rows} rows")
+    _layer_case(moe, orc, wl, W, x, li, c, expect, f"a17b {rows} rows")
     c.close()
 
 
