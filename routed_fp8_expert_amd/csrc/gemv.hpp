@@ -55,25 +55,42 @@ __device__ __forceinline__ float dot_bf16_row(const u32x4 (&wv)[NCH], const uint
 
 // x_r . w with the bits of load_bf16_row<16> + dot_bf16_row<16> (the same
 // lane-strided chunks in the same order, the same wave sum), four chunks per
-// lane in flight instead of sixteen held in registers.
-__device__ __forceinline__ float dot_bf16_row_stream(const uint16_t *wrow, const uint16_t *xr, int H) {
+// lane in flight instead of sixteen held in registers.  In two parts, so a
+// caller can issue the first four chunks' loads (all of them for H <= 2048)
+// ahead of other work: row_stream_head, then row_stream_dot.
+struct RowStreamHead {
+    u32x4 wv[4], xv[4];
+};
+__device__ __forceinline__ void row_stream_load(const uint16_t *wrow, const uint16_t *xr, int nch, int t0,
+                                                RowStreamHead &q) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int c = lane + kWave * (t0 + t), cc = c < nch ? c : nch - 1;
+        q.wv[t] = ld16_stream(wrow + (size_t)cc * 8);
+        q.xv[t] = ld16(xr + (size_t)cc * 8);
+    }
+}
+__device__ __forceinline__ void row_stream_head(const uint16_t *wrow, const uint16_t *xr, int H, RowStreamHead &q) {
+    row_stream_load(wrow, xr, H >> 3, 0, q);
+}
+__device__ __forceinline__ float row_stream_dot(RowStreamHead &q, const uint16_t *wrow, const uint16_t *xr, int H) {
     const int lane = threadIdx.x & (kWave - 1), nch = H >> 3;
     float acc = 0.0f;
 #pragma unroll
     for (int t0 = 0; t0 < 16; t0 += 4) {
         if (kWave * t0 >= nch) break;
-        u32x4 wv[4], xv[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int c = lane + kWave * (t0 + t), cc = c < nch ? c : nch - 1;
-            wv[t] = ld16_stream(wrow + (size_t)cc * 8);
-            xv[t] = ld16(xr + (size_t)cc * 8);
-        }
+        if (t0 > 0) row_stream_load(wrow, xr, nch, t0, q);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            if (lane + kWave * (t0 + t) < nch) acc = dot8_bf16(wv[t], xv[t], acc);
+            if (lane + kWave * (t0 + t) < nch) acc = dot8_bf16(q.wv[t], q.xv[t], acc);
     }
     return group_sum<kWave>(acc);
+}
+__device__ __forceinline__ float dot_bf16_row_stream(const uint16_t *wrow, const uint16_t *xr, int H) {
+    RowStreamHead q;
+    row_stream_head(wrow, xr, H, q);
+    return row_stream_dot(q, wrow, xr, H);
 }
 
 // ------------------------------------------------------------------ top-k
@@ -347,16 +364,20 @@ __device__ __forceinline__ void topk_regs(const float (&raw)[NV], int E, int k, 
 // The same from logits in memory; `coherent` reads them with agent-scope
 // loads (written by other workgroups of the same launch).
 template <int NV>
-__device__ __forceinline__ void topk_wave(const float *l, int E, int k, bool coherent, uint64_t *scr, int &my_e,
-                                          float &my_w) {
+__device__ __forceinline__ void load_logits(const float *l, int E, bool coherent, float (&raw)[NV]) {
     const int lane = threadIdx.x & (kWave - 1);
-    float raw[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = lane + kWave * i;
         const int ec = e < E ? e : E - 1;
         raw[i] = coherent ? ld_agent(l + ec) : l[ec];
     }
+}
+template <int NV>
+__device__ __forceinline__ void topk_wave(const float *l, int E, int k, bool coherent, uint64_t *scr, int &my_e,
+                                          float &my_w) {
+    float raw[NV];
+    load_logits<NV>(l, E, coherent, raw);
     topk_regs<NV>(raw, E, k, scr, my_e, my_w);
 }
 
